@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Throughput of the LLM.int8() linear layer on one MI355X.
+
+One step = one int8_linear call (outlier scan, row quantization, int8 GEMM,
+outlier fp16 product, dequantize + add) on synthetic seeded inputs already
+resident in HBM; the weight is quantized once, untimed, as the layer does when
+it is placed on the GPU.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload decode]
+
+The default workload is the decode shape X 8x4096 . W 4096x16384 with 4
+outlier columns.  To keep the 256 MB Infinity Cache from serving the weight,
+steps rotate over several copies of (X, Wq, sw, W, Y, workspace) totalling
+more than 512 MB.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks.
+PEAK_HBM_GBS = 8000.0
+PEAK_INT8_TOPS = 5000.0
+
+# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs,
+# scaled by the copy-kernel calibration factor; valid only for the kernel
+# source it was measured on (sha256 of the listed files).
+TRAFFIC = {}
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "mixed_precision_quantized_int8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move once: X, Wq, the outlier weight rows, Y, scales."""
+    return (2 * w.M * w.K + w.N * w.K + 2 * w.n_out * w.N + 2 * w.M * w.N
+            + 4 * w.N + 4 * w.M + 4 * w.n_out)
+
+
+def dominant_kernel(w):
+    if w.M <= 16 and w.K <= 8192 and w.M * ((w.K + 63) // 64 * 64) <= 65536 and (w.M <= 8 or w.K <= 4096):
+        return "decode_kernel", "hbm", ["decode.hip", "common.h"]
+    return "gemm_i8_kernel", "mfma", ["gemm.hip", "common.h"]
+
+
+def cpu_baseline(w, X, W, budget_s=12.0):
+    """Time the CPU oracle (as it stands) on the same workload on the host cores."""
+    import numpy as np
+    from oracle import int8_oracle as O
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max((i.get("num_threads") or 0) for i in info) if info else None
+    except Exception:
+        pass
+    Wq, sw = O.quantize_weight(W)            # untimed, as on the GPU side
+    reps, t_total, out = 0, 0.0, None
+    t0 = time.perf_counter()
+    while reps < 100 and (time.perf_counter() - t0) < budget_s:
+        s = time.perf_counter()
+        out = O.int8_linear(X, Wq, sw, W, w.threshold)
+        t_total += time.perf_counter() - s
+        reps += 1
+    per_call = t_total / reps
+    return {
+        "value": round(w.int_ops / per_call / 1e12, 6),
+        "unit": "TOPS",
+        "cores": threads or os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"full {w.name} call ({w.M}x{w.K}x{w.N}), weight pre-quantized, "
+                  f"{reps} calls, {per_call * 1e3:.1f} ms/call; host has {os.cpu_count()} cpus",
+    }, out, Wq, sw
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: auto, >512 MB)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixed_precision_quantized_int8_amd as pkg
+    from mixed_precision_quantized_int8_amd import _binding, workloads
+
+    if not os.path.exists(_binding.LIB_PATH):
+        from mixed_precision_quantized_int8_amd import build
+        build.build_library()
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    X, W, _ = workloads.make_inputs(w)
+    Xd = torch.from_numpy(X).to(dev)
+    Wd = torch.from_numpy(W).to(dev)
+    Wq, sw = pkg.quantize_weight(Wd)
+    ws_bytes = pkg.workspace_bytes(w.M, w.K, w.N)
+    set_bytes = Xd.numel() * 2 + Wq.numel() + Wd.numel() * 2 + ws_bytes + 2 * w.M * w.N
+    R = args.rotate or max(1, min(16, -(-512 * 2**20 // set_bytes)))
+    sets = []
+    for r in range(R):
+        if r == 0:
+            s = (Xd, Wq, sw, Wd)
+        else:
+            s = (Xd.clone(), Wq.clone(), sw.clone(), Wd.clone())
+        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+        Y = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+        sets.append((*s, ws, Y))
+
+    def step(i):
+        x, q, s, wf, ws, y = sets[i % R]
+        pkg.linear(x, q, s, wf, w.threshold, workspace=ws, out=y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record()
+    for i in range(K):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_begin.elapsed_time(t_end)
+    ms_per_step = ms_total / K
+    per_launch = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    ms_launch = float(per_launch.mean())
+
+    value = w.int_ops / (ms_per_step * 1e-3) / 1e12
+    kname, bound, files = dominant_kernel(w)
+    src_hash = kernel_source_hash(files)
+    if bound == "hbm":
+        alg = algorithmic_bytes(w)
+        achieved = alg / (ms_launch * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = w.int_ops / (ms_launch * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
+                "unit": "TOPS", "frac": round(achieved / PEAK_INT8_TOPS, 4)}
+    tr = TRAFFIC.get((kname, w.name))
+    roof["traffic"] = tr["bytes"] if tr and tr["src"] == src_hash else None
+    roof["kernel"] = kname
+    roof["kernel_ms"] = round(ms_launch, 5)
+    roof["kernel_src"] = src_hash
+
+    result = {
+        "metric": "int8_linear TOPS and % of int8-MFMA / HBM roofline on one MI355X",
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N,
+                   "outlier_columns": w.n_out, "threshold": w.threshold,
+                   "buffer_sets": R, "x_dtype": "fp16", "y_dtype": "fp16"},
+        "roofline": roof,
+    }
+
+    if not args.no_cpu_baseline:
+        cb, ref, Wq_o, sw_o = cpu_baseline(w, X, W)
+        result["cpu_baseline"] = cb
+        y = sets[0][5].cpu().numpy().astype(np.float64)
+        err = np.abs(y - ref["Y64"])
+        tol = np.maximum(2e-3 * np.abs(ref["Y64"]), 1e-2)
+        result["parity"] = {
+            "Y_within_tol": bool(np.all(err <= tol)),
+            "Wq_bitexact": bool(np.array_equal(Wq.cpu().numpy(), Wq_o)),
+            "max_abs_err": float(err.max()),
+        }
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * int8lin.h -- C ABI of the LLM.int8() quantized linear layer for AMD MI355X
+ * (gfx950).  Implemented by libint8lin.so (hand-written HIP kernels).
+ *
+ * The method is the one described in the blog "A Gentle Introduction to 8-bit
+ * Matrix Multiplication for transformers at scale using Hugging Face
+ * Transformers, Accelerate and bitsandbytes" (cited as [blog] below):
+ *   - vector-wise absmax quantization: one scale per row of the fp16 hidden
+ *     states X and one per output column of the weight W
+ *     ([blog, "Introduction to model quantization"]);
+ *   - mixed-precision decomposition: a column of X holding any value of
+ *     magnitude >= threshold (6 in the blog) is an outlier column; outlier
+ *     columns are multiplied in fp16 against the matching fp16 rows of W, the
+ *     rest in int8 x int8 -> int32; the int8 result is dequantized with the
+ *     outer product of the scales over 127^2 and added to the fp16 outlier
+ *     product ([blog, "A gentle summary of LLM.int8()"] and
+ *     [blog, "A closer look at the MatMul"]).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers (HBM of the current HIP device) and
+ *     are row-major.  fp16 tensors are passed as raw IEEE binary16 bits
+ *     (uint16_t).  The caller owns and allocates every buffer; the library
+ *     allocates no device memory and keeps no state besides a thread-local
+ *     error message.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL means the
+ *     default stream) and returns without synchronizing.  Device-side faults
+ *     surface at the caller's next synchronization.
+ *   - All argument checks run on the host before any HIP call; on a non-OK
+ *     status nothing has been enqueued and i8l_last_error() tells why.
+ *   - Shapes: M (rows of X) >= 0, N (output features) >= 0; M == 0 or N == 0
+ *     is a valid no-op.  K (input features) must satisfy 16 <= K <= 133136 and
+ *     K % 16 == 0 (K * 127^2 must fit in int32).
+ *   - Alignment: X, Y, Wq, Xq, acc, X_outliers and workspace pointers must be
+ *     16-byte aligned; sw, sx, outlier_idx and n_outliers 4-byte aligned; W and
+ *     W_outlier_rows 2-byte aligned.
+ *   - Rounding: quantized codes are clamp(round_half_away_from_zero(
+ *     fp32(x) * fl32(127 / absmax)), -127, 127), with 127 / absmax an IEEE fp32
+ *     division; absmax == 0 gives code 0.
+ *   - Functions are reentrant; calls that share a workspace must not overlap.
+ */
+#ifndef INT8LIN_H
+#define INT8LIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  I8L_OK = 0,
+  I8L_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad shape, NaN threshold */
+  I8L_ERR_K_TOO_LARGE = 2, /* K > 133136: int32 accumulators could overflow */
+  I8L_ERR_WORKSPACE = 3,   /* workspace smaller than required */
+  I8L_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} i8l_status;
+
+/* Largest supported K (K * 127 * 127 < 2^31, rounded down to a multiple of 16). */
+#define I8L_MAX_K 133136
+
+/* Byte offsets, inside the int8_linear / int8_quantize_activation workspace, of
+ * the intermediates that the call leaves there.  After an int8_linear call
+ * (once the stream has reached it) the workspace holds, for that call:
+ *   n_outliers   int32 [1]        number of outlier columns n_out
+ *   outlier_idx  int32 [K] cap    ascending outlier column indices, first n_out
+ *   sx           fp32  [M]        row absmax of X over the regular columns
+ *   Xq           int8  [M][K]     row-quantized X, 0 in outlier columns
+ *   X_outliers   fp16  [M][K] cap outlier values, element (i, j) at i*K + j,
+ *                                 j < n_out, j-th outlier column in ascending order
+ *   flags        uint32 [ceil(K/32)] internal: outlier column bitmask
+ * `total` is the size the call requires. */
+typedef struct {
+  size_t total;
+  size_t n_outliers;
+  size_t outlier_idx;
+  size_t sx;
+  size_t Xq;
+  size_t X_outliers;
+  size_t flags;
+} i8l_workspace_layout;
+
+/* Fills *layout for an int8_linear call of this shape (N does not change it).
+ * Returns I8L_ERR_INVALID_ARG / I8L_ERR_K_TOO_LARGE on a bad shape. */
+i8l_status i8l_linear_workspace(int64_t M, int64_t K, int64_t N, i8l_workspace_layout *layout);
+
+/* Workspace bytes int8_linear needs for this shape (0 on a bad shape). */
+size_t i8l_linear_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/* Weight quantization ([blog, "A closer look at the MatMul"]: the weight is
+ * quantized per column; [blog, "Usage"]: it happens once, when the layer is
+ * placed on the GPU, and keeps the int8 weight in nn.Linear's [out][in] layout
+ * next to one absmax per output feature).
+ *   W   fp16 [K][N]  math layout (Y = X @ W), read only
+ *   Wq  int8 [N][K]  out: Wq[n][k] = code(W[k][n], sw[n])
+ *   sw  fp32 [N]     out: sw[n] = max_k |W[k][n]| */
+i8l_status int8_quantize_weight(const uint16_t *W, int64_t K, int64_t N,
+                                int8_t *Wq, float *sw, void *stream);
+
+/* The LLM.int8() linear layer: Y = dequant(int8 part) + fp16 outlier part.
+ *   X               fp16 [M][K]  hidden states, read only
+ *   Wq, sw          from int8_quantize_weight for the same K, N
+ *   W_outlier_rows  fp16 [K][N]  the fp16 weight in math layout; only rows
+ *                   that are outlier columns of X are read.  May be NULL only
+ *                   when the decomposition is disabled (see threshold).
+ *   threshold       finite > 0: columns of X with any |x| >= threshold are
+ *                   outliers; <= 0 or +inf: no decomposition (pure int8);
+ *                   NaN: I8L_ERR_INVALID_ARG.
+ *   Y               fp16 [M][N]  out: fp16(acc*sx[i]*sw[n]/127^2 + outlier
+ *                   product), accumulated in fp32, round-to-nearest-even,
+ *                   overflow to +/-inf.
+ *   workspace       device scratch of i8l_linear_workspace_bytes(M, K, N)
+ *                   bytes; it holds the call's intermediates afterwards (see
+ *                   i8l_workspace_layout). */
+i8l_status int8_linear(const uint16_t *X, int64_t M, int64_t K,
+                       const int8_t *Wq, const float *sw, int64_t N,
+                       const uint16_t *W_outlier_rows, float threshold,
+                       uint16_t *Y, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Activation stage on its own ([blog, "A gentle summary of LLM.int8()"],
+ * step 1, and the row-wise quantization of [blog, "A closer look at the
+ * MatMul"]); the same kernels int8_linear runs for M > 16.
+ *   Xq          int8 [M][K]      out, 0 in outlier columns
+ *   sx          fp32 [M]         out
+ *   outlier_idx int32 [K] cap    out, ascending, first n_out entries valid
+ *   n_outliers  int32 [1]        out
+ *   X_outliers  fp16 [M][K] cap  out, element (i, j) at i*K + j for j < n_out
+ *   workspace   at least i8l_linear_workspace_bytes(M, K, 0) bytes */
+i8l_status int8_quantize_activation(const uint16_t *X, int64_t M, int64_t K, float threshold,
+                                    int8_t *Xq, float *sx, int32_t *outlier_idx,
+                                    int32_t *n_outliers, uint16_t *X_outliers,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Exact int8 GEMM on its own ([blog, "Introduction to model quantization"]:
+ * the normalised int8 matrices are multiplied), the kernel int8_linear uses
+ * for M > 16 with its int32 result written out instead of dequantized.
+ *   Xq   int8 [M][K]
+ *   Wq   int8 [N][K]
+ *   acc  int32 [M][N]  out: acc[i][n] = sum_k Xq[i][k] * Wq[n][k] */
+i8l_status int8_gemm_i32(const int8_t *Xq, const int8_t *Wq, int64_t M, int64_t N, int64_t K,
+                         int32_t *acc, void *stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *i8l_last_error(void);
+
+/* Static build description: target architecture and kernel tile sizes. */
+const char *i8l_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INT8LIN_H */

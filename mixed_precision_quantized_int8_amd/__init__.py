@@ -1,0 +1,162 @@
+"""LLM.int8() quantized linear layer for AMD MI355X (gfx950).
+
+Python face of the C ABI in include/int8lin.h: same operation names, torch
+tensors in and out.  Marshalling only -- every step runs in the HIP kernels of
+libint8lin.so; torch supplies device memory and the current stream.
+
+    Wq, sw = quantize_weight(W)              # W fp16 [K][N] (Y = X @ W)
+    Y = linear(X, Wq, sw, W, threshold=6.0)  # X fp16 [M][K] -> Y fp16 [M][N]
+"""
+from __future__ import annotations
+
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    Int8LinError,
+    MAX_K,
+    build_info,
+    check,
+    last_error,
+    lib,
+    workspace_bytes,
+    workspace_layout,
+)
+
+__all__ = [
+    "quantize_weight",
+    "linear",
+    "quantize_activation",
+    "gemm_i32",
+    "workspace_layout",
+    "workspace_bytes",
+    "workspace_views",
+    "Int8LinError",
+    "build_info",
+]
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize_weight(W, Wq=None, sw=None):
+    """W fp16 [K][N] -> (Wq int8 [N][K], sw fp32 [N]); column-wise absmax codes."""
+    torch = _torch()
+    _require(W, torch.float16, "W")
+    K, N = W.shape
+    if Wq is None:
+        Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    if sw is None:
+        sw = torch.empty((N,), dtype=torch.float32, device=W.device)
+    with torch.cuda.device(W.device):
+        check(lib().int8_quantize_weight(W.data_ptr(), K, N, Wq.data_ptr(), sw.data_ptr(),
+                                         _stream(W)))
+    return Wq, sw
+
+
+def new_workspace(M, K, N, device):
+    torch = _torch()
+    return torch.empty((max(workspace_bytes(M, K, N), 1),), dtype=torch.uint8, device=device)
+
+
+def linear(X, Wq, sw, W=None, threshold=6.0, workspace=None, out=None):
+    """LLM.int8() linear layer: X fp16 [M][K] -> Y fp16 [M][N].
+
+    W (fp16 [K][N]) supplies the weight rows of the outlier columns; it may be
+    None when ``threshold`` disables the decomposition (<= 0 or inf).
+    """
+    torch = _torch()
+    _require(X, torch.float16, "X")
+    _require(Wq, torch.int8, "Wq")
+    _require(sw, torch.float32, "sw")
+    M, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or sw.shape != (N,):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wq {tuple(Wq.shape)}, sw {tuple(sw.shape)}")
+    if W is not None:
+        _require(W, torch.float16, "W")
+        if tuple(W.shape) != (K, N):
+            raise ValueError(f"W must be [K][N] = [{K}][{N}], got {tuple(W.shape)}")
+    if workspace is None:
+        workspace = new_workspace(M, K, N, X.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    with torch.cuda.device(X.device):
+        check(lib().int8_linear(
+            X.data_ptr(), M, K, Wq.data_ptr(), sw.data_ptr(), N,
+            W.data_ptr() if W is not None else None, float(threshold),
+            out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(X)))
+    return out
+
+
+def workspace_views(workspace, M, K):
+    """Typed views of the intermediates an int8_linear call leaves in its workspace."""
+    torch = _torch()
+    L = workspace_layout(M, K, 0)
+    b = workspace
+
+    def view(off, nbytes, dtype, shape):
+        return b[off:off + nbytes].view(dtype).view(shape)
+
+    return {
+        "n_out": view(L["n_outliers"], 4, torch.int32, (1,)),
+        "idx": view(L["outlier_idx"], 4 * K, torch.int32, (K,)),
+        "sx": view(L["sx"], 4 * M, torch.float32, (M,)),
+        "Xq": view(L["Xq"], M * K, torch.int8, (M, K)),
+        "X_O": view(L["X_outliers"], 2 * M * K, torch.float16, (M, K)),
+    }
+
+
+def quantize_activation(X, threshold=6.0, workspace=None):
+    """Activation stage alone: dict of Xq [M][K], sx [M], idx [K] (first n_out
+    valid), n_out [1], X_O [M][K] (first n_out columns valid)."""
+    torch = _torch()
+    _require(X, torch.float16, "X")
+    M, K = X.shape
+    dev = X.device
+    Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sx = torch.empty((M,), dtype=torch.float32, device=dev)
+    idx = torch.empty((K,), dtype=torch.int32, device=dev)
+    n_out = torch.empty((1,), dtype=torch.int32, device=dev)
+    X_O = torch.empty((M, K), dtype=torch.float16, device=dev)
+    if workspace is None:
+        workspace = new_workspace(M, K, 0, dev)
+    with torch.cuda.device(dev):
+        check(lib().int8_quantize_activation(
+            X.data_ptr(), M, K, float(threshold), Xq.data_ptr(), sx.data_ptr(), idx.data_ptr(),
+            n_out.data_ptr(), X_O.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(X)))
+    return {"Xq": Xq, "sx": sx, "idx": idx, "n_out": n_out, "X_O": X_O}
+
+
+def gemm_i32(Xq, Wq):
+    """Exact int8 GEMM: Xq int8 [M][K], Wq int8 [N][K] -> int32 [M][N]."""
+    torch = _torch()
+    _require(Xq, torch.int8, "Xq")
+    _require(Wq, torch.int8, "Wq")
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K:
+        raise ValueError("Xq and Wq must share K")
+    acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    with torch.cuda.device(Xq.device):
+        check(lib().int8_gemm_i32(Xq.data_ptr(), Wq.data_ptr(), M, N, K, acc.data_ptr(),
+                                  _stream(Xq)))
+    return acc

@@ -1,0 +1,261 @@
+// Activation stage of LLM.int8(): outlier column scan, row absmax over the
+// regular columns, row-wise int8 codes and the gather of the outlier values.
+//
+// [blog, "A gentle summary of LLM.int8()"], step 1: outliers are taken out of
+// the hidden states column by column.  [blog, "A closer look at the MatMul"]:
+// an outlier has magnitude 6 or more (the threshold), and the remaining hidden
+// states are quantized row by row.  [blog, "Introduction to model
+// quantization"]: absmax codes are round(x * 127 / absmax) in [-127, 127].
+//
+// Three launches on the caller's stream:
+//   clear     zero the column bitmask (a fill kernel, safe under graph capture)
+//   colflags  one pass over X: per thread 16-byte loads, 8 running column
+//             maxima; a set bit for every column whose absmax reaches the
+//             threshold (atomicOr, issued only for the rare outlier columns)
+//   rowquant  one workgroup per row: the bitmask and its prefix popcounts go
+//             to LDS, the row is held in registers while its absmax over the
+//             regular columns is reduced, then codes are written (8 bytes per
+//             thread, coalesced) and outlier values are scattered to X_O at
+//             their rank; workgroup 0 also writes the ascending index list.
+// The column dependency (every row must be seen before any row scale) is why
+// X is read twice; the second read is one coalesced pass per row.
+#include "common.h"
+#include "launch.h"
+
+namespace i8l {
+
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, int n, uint32_t v) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int n, uint32_t v, hipStream_t stream) {
+  const int blocks = n > 0 ? (n + 255) / 256 : 1;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks < 1024 ? blocks : 1024), dim3(256), 0, stream, p,
+                     n, v);
+  return hipGetLastError();
+}
+
+constexpr int kColThreads = 256;
+constexpr int kColStrip = kWave * 8;   // columns per workgroup: 8 fp16 per lane
+
+// grid = (ceil(K / 512), ceil(M / rows_per_block)); waves of a block stride over rows.
+__global__ __launch_bounds__(kColThreads) void colflags_kernel(const uint16_t* __restrict__ X, int M,
+                                                              int K, int rows_per_block,
+                                                              float threshold,
+                                                              uint32_t* __restrict__ flags) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * kColStrip + lane * 8;
+  if (c >= K) return;   // K % 16 == 0, so c < K means all 8 columns are in range
+  const int r0 = blockIdx.y * rows_per_block;
+  const int r1 = min(M, r0 + rows_per_block);
+  const uint16_t* base = X + c;
+  uint32_t mx[4] = {0, 0, 0, 0};   // packed pairs of |fp16| bit patterns
+  int r = r0 + wave;
+  // four independent 16-byte loads in flight per thread
+  for (; r + 12 < r1; r += 16) {
+    v4i a = *reinterpret_cast<const v4i*>(base + (size_t)r * K);
+    v4i b = *reinterpret_cast<const v4i*>(base + (size_t)(r + 4) * K);
+    v4i d = *reinterpret_cast<const v4i*>(base + (size_t)(r + 8) * K);
+    v4i e = *reinterpret_cast<const v4i*>(base + (size_t)(r + 12) * K);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t x0 = (uint32_t)a[j] & 0x7fff7fffu, x1 = (uint32_t)b[j] & 0x7fff7fffu;
+      uint32_t x2 = (uint32_t)d[j] & 0x7fff7fffu, x3 = (uint32_t)e[j] & 0x7fff7fffu;
+      // per-halfword unsigned max
+      uint32_t lo = max(max(x0 & 0xffffu, x1 & 0xffffu), max(x2 & 0xffffu, x3 & 0xffffu));
+      uint32_t hi = max(max(x0 >> 16, x1 >> 16), max(x2 >> 16, x3 >> 16));
+      lo = max(lo, mx[j] & 0xffffu);
+      hi = max(hi, mx[j] >> 16);
+      mx[j] = lo | (hi << 16);
+    }
+  }
+  for (; r < r1; r += 4) {
+    v4i a = *reinterpret_cast<const v4i*>(base + (size_t)r * K);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t x0 = (uint32_t)a[j] & 0x7fff7fffu;
+      uint32_t lo = max(x0 & 0xffffu, mx[j] & 0xffffu);
+      uint32_t hi = max(x0 >> 16, mx[j] >> 16);
+      mx[j] = lo | (hi << 16);
+    }
+  }
+  uint32_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t h = (mx[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+    if (h2f((uint16_t)h) >= threshold) bits |= 1u << e;
+  }
+  if (bits) atomicOr(flags + (c >> 5), bits << (c & 31));
+}
+
+// Exclusive block-wide prefix sum (blockDim.x threads, multiple of 64).
+template <int BS>
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = wave_incl_scan(v);
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < BS / 64 ? s_tmp[lane] : 0;
+    int wi = wave_incl_scan(w);
+    if (lane < BS / 64) s_tmp[lane] = wi - w;
+    if (lane == 63) s_tmp[BS / 64] = wi;
+  }
+  __syncthreads();
+  int r = s_tmp[wave] + incl - v;
+  *total = s_tmp[BS / 64];
+  __syncthreads();
+  return r;
+}
+
+constexpr int kMaxFlagWords = (I8L_MAX_K_DEV + 31) / 32;
+
+// One workgroup per row of X.  NCH 16-byte chunks per thread: K <= BS * 8 * NCH.
+template <int BS, int NCH>
+__global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict__ X, int M, int K,
+                                                     const uint32_t* __restrict__ flags,
+                                                     int8_t* __restrict__ Xq, float* __restrict__ sx,
+                                                     int32_t* __restrict__ idx,
+                                                     int32_t* __restrict__ n_out,
+                                                     uint16_t* __restrict__ X_O) {
+  __shared__ uint32_t s_flags[kMaxFlagWords];
+  __shared__ int s_rank[kMaxFlagWords];
+  __shared__ int s_tmp[BS / 64 + 1];
+  __shared__ uint32_t s_max[BS / 64];
+
+  const int t = threadIdx.x;
+  const int row = blockIdx.x;
+  const int nw = (K + 31) >> 5;
+
+  // flags -> LDS, exclusive prefix popcount per word
+  const int w0 = t * ((nw + BS - 1) / BS);
+  const int w1 = min(nw, w0 + (nw + BS - 1) / BS);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t f = flags[w];
+    s_flags[w] = f;
+    cnt += __builtin_popcount(f);
+  }
+  int total;
+  int base = block_excl_scan<BS>(cnt, s_tmp, &total);
+  for (int w = w0; w < w1; ++w) {
+    s_rank[w] = base;
+    base += __builtin_popcount(s_flags[w]);
+  }
+  __syncthreads();
+
+  // the row, in registers
+  const uint16_t* xr = X + (size_t)row * K;
+  const int nchunks = K >> 3;
+  v4i raw[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int q = t + j * BS;
+    if (q < nchunks) raw[j] = *reinterpret_cast<const v4i*>(xr + q * 8);
+    else raw[j] = v4i{0, 0, 0, 0};
+  }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int q = t + j * BS;
+    if (q < nchunks) {
+      const uint32_t ob = (s_flags[q >> 2] >> ((q & 3) * 8)) & 0xffu;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t h = ((uint32_t)raw[j][e >> 1] >> ((e & 1) * 16)) & 0x7fffu;
+        if (!((ob >> e) & 1u)) mx = h > mx ? h : mx;
+      }
+    }
+  }
+  mx = wave_max_u32(mx);
+  if ((t & 63) == 0) s_max[t >> 6] = mx;
+  __syncthreads();
+  mx = 0;
+#pragma unroll
+  for (int w = 0; w < BS / 64; ++w) mx = s_max[w] > mx ? s_max[w] : mx;
+  const float amax = h2f((uint16_t)mx);
+  const float inv = quant_scale(amax);
+
+  int8_t* qr = Xq + (size_t)row * K;
+  uint16_t* orow = X_O + (size_t)row * K;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int q = t + j * BS;
+    if (q < nchunks) {
+      const int word = q >> 2;
+      const int sh = (q & 3) * 8;
+      const uint32_t ob = (s_flags[word] >> sh) & 0xffu;
+      int code[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t hb = (uint16_t)(((uint32_t)raw[j][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+        code[e] = ((ob >> e) & 1u) ? 0 : quant_code(h2f(hb), inv);
+      }
+      v2i packed = {(int)pack4_i8(code[0], code[1], code[2], code[3]),
+                    (int)pack4_i8(code[4], code[5], code[6], code[7])};
+      *reinterpret_cast<v2i*>(qr + q * 8) = packed;
+      if (ob) {
+        const uint32_t fw = s_flags[word];
+        const int rb = s_rank[word];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if ((ob >> e) & 1u) {
+            const int bit = sh + e;
+            const int rank = rb + __builtin_popcount(fw & ((1u << bit) - 1u));
+            orow[rank] = (uint16_t)(((uint32_t)raw[j][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+          }
+        }
+      }
+    }
+  }
+  if (t == 0) sx[row] = amax;
+
+  if (row == 0) {
+    for (int w = t; w < nw; w += BS) {
+      uint32_t f = s_flags[w];
+      int r = s_rank[w];
+      while (f) {
+        const int b = __builtin_ctz(f);
+        idx[r++] = w * 32 + b;
+        f &= f - 1u;
+      }
+    }
+    if (t == 0) *n_out = total;
+  }
+}
+
+template <int BS, int NCH>
+static void launch_rowquant(const uint16_t* X, int M, int K, const Workspace& ws,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL((rowquant_kernel<BS, NCH>), dim3(M), dim3(BS), 0, stream, X, M, K,
+                     (const uint32_t*)ws.flags, ws.Xq, ws.sx, ws.idx, ws.n_out, ws.X_O);
+}
+
+hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float threshold,
+                                      bool enabled, const Workspace& ws, hipStream_t stream) {
+  const int nw = (K + 31) / 32;
+  launch_fill_u32(ws.flags, nw, 0u, stream);
+  if (enabled && M > 0) {
+    const int bx = (K + kColStrip - 1) / kColStrip;
+    long long want = ((long long)M * bx + 2047) / 2048;
+    int rows = (int)((want + 15) / 16 * 16);
+    if (rows < 16) rows = 16;
+    const int by = (M + rows - 1) / rows;
+    hipLaunchKernelGGL(colflags_kernel, dim3(bx, by), dim3(kColThreads), 0, stream, X, M, K, rows,
+                       threshold, ws.flags);
+  }
+  if (M > 0) {
+    const int nch256 = (K / 8 + 255) / 256;
+    if (nch256 <= 1) launch_rowquant<256, 1>(X, M, K, ws, stream);
+    else if (nch256 <= 2) launch_rowquant<256, 2>(X, M, K, ws, stream);
+    else if (nch256 <= 4) launch_rowquant<256, 4>(X, M, K, ws, stream);
+    else if (nch256 <= 8) launch_rowquant<256, 8>(X, M, K, ws, stream);
+    else if (nch256 <= 16) launch_rowquant<256, 16>(X, M, K, ws, stream);
+    else if (nch256 <= 32) launch_rowquant<256, 32>(X, M, K, ws, stream);
+    else launch_rowquant<1024, 17>(X, M, K, ws, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace i8l

@@ -1,0 +1,72 @@
+// Shared device helpers of the gfx950 kernels (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8l {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+#define I8L_MAX_K_DEV 133136
+
+__device__ __forceinline__ float h2f(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+__device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even, overflow -> inf
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+// |x| of an fp16 value as an fp16 bit pattern; for finite values the unsigned
+// order of these patterns is the order of the magnitudes.
+__device__ __forceinline__ uint32_t habs_bits(uint32_t b) { return b & 0x7fffu; }
+
+// Absmax code of one value: clamp(round_half_away(fp32(x) * inv), -127, 127),
+// where inv = fl32(127 / absmax) is computed once per vector by the caller
+// (IEEE division).  roundf rounds halfway cases away from zero.
+__device__ __forceinline__ int quant_code(float x, float inv) {
+  float v = x * inv;
+  float r = __builtin_roundf(v);
+  r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+__device__ __forceinline__ float quant_scale(float absmax) {
+  return absmax > 0.0f ? 127.0f / absmax : 0.0f;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+         ((uint32_t)(d & 0xff) << 24);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+}  // namespace i8l

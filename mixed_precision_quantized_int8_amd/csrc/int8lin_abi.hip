@@ -1,0 +1,222 @@
+// C ABI of the LLM.int8() linear layer (declared in include/int8lin.h).
+//
+// Every entry point validates its arguments on the host before making any HIP
+// call, so a bad call returns an error code with nothing enqueued.  Then it
+// carves the caller's workspace and enqueues the kernels on the caller's
+// stream; it never synchronizes and never allocates device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/int8lin.h"
+#include "launch.h"
+
+#define I8L_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+i8l_status fail(i8l_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+i8l_status ok() {
+  g_err[0] = 0;
+  return I8L_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Shape rules shared by all entry points.
+i8l_status check_shape(const char* fn, int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || N < 0) return fail(I8L_ERR_INVALID_ARG, "%s: M=%lld and N=%lld must be >= 0", fn,
+                                  (long long)M, (long long)N);
+  if (K > I8L_MAX_K)
+    return fail(I8L_ERR_K_TOO_LARGE, "%s: K=%lld exceeds %d (K*127^2 must fit in int32)", fn,
+                (long long)K, I8L_MAX_K);
+  if (K < 16 || K % 16 != 0)
+    return fail(I8L_ERR_INVALID_ARG, "%s: K=%lld must be a positive multiple of 16", fn,
+                (long long)K);
+  if (M > INT32_MAX || N > INT32_MAX)
+    return fail(I8L_ERR_INVALID_ARG, "%s: M and N must be < 2^31", fn);
+  if ((M > 0 && (uint64_t)M * (uint64_t)K > (1ull << 40)) ||
+      (N > 0 && (uint64_t)N * (uint64_t)K > (1ull << 40)) ||
+      (uint64_t)M * (uint64_t)N > (1ull << 40))
+    return fail(I8L_ERR_INVALID_ARG, "%s: tensor sizes exceed 2^40 elements", fn);
+  return I8L_OK;
+}
+
+i8l_workspace_layout layout_of(int64_t M, int64_t K) {
+  i8l_workspace_layout L;
+  size_t off = 0;
+  L.n_outliers = off; off += up(sizeof(int32_t));
+  L.outlier_idx = off; off += up((size_t)K * sizeof(int32_t));
+  L.sx = off; off += up((size_t)M * sizeof(float));
+  L.flags = off; off += up((size_t)((K + 31) / 32) * sizeof(uint32_t));
+  L.Xq = off; off += up((size_t)M * (size_t)K);
+  L.X_outliers = off; off += up((size_t)M * (size_t)K * sizeof(uint16_t));
+  L.total = off;
+  return L;
+}
+
+i8l::Workspace carve(void* ws, const i8l_workspace_layout& L) {
+  char* b = static_cast<char*>(ws);
+  i8l::Workspace w;
+  w.n_out = reinterpret_cast<int32_t*>(b + L.n_outliers);
+  w.idx = reinterpret_cast<int32_t*>(b + L.outlier_idx);
+  w.sx = reinterpret_cast<float*>(b + L.sx);
+  w.Xq = reinterpret_cast<int8_t*>(b + L.Xq);
+  w.X_O = reinterpret_cast<uint16_t*>(b + L.X_outliers);
+  w.flags = reinterpret_cast<uint32_t*>(b + L.flags);
+  return w;
+}
+
+#define REQUIRE_PTR(fn, p, al)                                                                   \
+  do {                                                                                           \
+    if (!(p)) return fail(I8L_ERR_INVALID_ARG, "%s: " #p " is NULL", fn);                        \
+    if (!aligned((p), (al)))                                                                     \
+      return fail(I8L_ERR_INVALID_ARG, "%s: " #p " must be %d-byte aligned", fn, (int)(al));    \
+  } while (0)
+
+i8l_status hip_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(I8L_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+I8L_API i8l_status i8l_linear_workspace(int64_t M, int64_t K, int64_t N,
+                                        i8l_workspace_layout* layout) {
+  i8l_status s = check_shape("i8l_linear_workspace", M, K, N);
+  if (s != I8L_OK) return s;
+  if (!layout) return fail(I8L_ERR_INVALID_ARG, "i8l_linear_workspace: layout is NULL");
+  *layout = layout_of(M, K);
+  return ok();
+}
+
+I8L_API size_t i8l_linear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  if (check_shape("i8l_linear_workspace_bytes", M, K, N) != I8L_OK) return 0;
+  return layout_of(M, K).total;
+}
+
+I8L_API i8l_status int8_quantize_weight(const uint16_t* W, int64_t K, int64_t N, int8_t* Wq,
+                                        float* sw, void* stream) {
+  const char* fn = "int8_quantize_weight";
+  i8l_status s = check_shape(fn, 0, K, N);
+  if (s != I8L_OK) return s;
+  if (N == 0) return ok();
+  REQUIRE_PTR(fn, W, 2);
+  REQUIRE_PTR(fn, Wq, 16);
+  REQUIRE_PTR(fn, sw, 4);
+  (void)hipGetLastError();
+  return hip_status(fn, i8l::launch_quantize_weight(W, (int)K, (int)N, Wq, sw,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+I8L_API i8l_status int8_linear(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
+                               const float* sw, int64_t N, const uint16_t* W_outlier_rows,
+                               float threshold, uint16_t* Y, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  const char* fn = "int8_linear";
+  i8l_status s = check_shape(fn, M, K, N);
+  if (s != I8L_OK) return s;
+  if (isnan(threshold)) return fail(I8L_ERR_INVALID_ARG, "%s: threshold is NaN", fn);
+  const bool enabled = threshold > 0.0f && isfinite(threshold);
+  if (M == 0 || N == 0) return ok();   // nothing to read or write
+  REQUIRE_PTR(fn, X, 16);
+  REQUIRE_PTR(fn, Wq, 16);
+  REQUIRE_PTR(fn, sw, 4);
+  REQUIRE_PTR(fn, Y, 16);
+  REQUIRE_PTR(fn, workspace, 16);
+  if (enabled) REQUIRE_PTR(fn, W_outlier_rows, 2);
+  else if (W_outlier_rows && !aligned(W_outlier_rows, 2))
+    return fail(I8L_ERR_INVALID_ARG, "%s: W_outlier_rows must be 2-byte aligned", fn);
+  const i8l_workspace_layout L = layout_of(M, K);
+  if (workspace_bytes < L.total)
+    return fail(I8L_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn,
+                workspace_bytes, L.total);
+  (void)hipGetLastError();
+  const i8l::Workspace w = carve(workspace, L);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int m = (int)M, k = (int)K, n = (int)N;
+  if (m <= 16) {
+    return hip_status(fn, i8l::launch_decode(X, m, k, Wq, sw, n, W_outlier_rows, threshold,
+                                             enabled, Y, w, st));
+  }
+  hipError_t e = i8l::launch_quantize_activation(X, m, k, threshold, enabled, w, st);
+  if (e != hipSuccess) return hip_status(fn, e);
+  i8l::GemmArgs g{w.Xq, Wq, m, n, k, w.sx, sw, w.n_out, w.idx, w.X_O, W_outlier_rows, Y, nullptr};
+  return hip_status(fn, i8l::launch_gemm(g, st));
+}
+
+I8L_API i8l_status int8_quantize_activation(const uint16_t* X, int64_t M, int64_t K,
+                                            float threshold, int8_t* Xq, float* sx,
+                                            int32_t* outlier_idx, int32_t* n_outliers,
+                                            uint16_t* X_outliers, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  const char* fn = "int8_quantize_activation";
+  i8l_status s = check_shape(fn, M, K, 0);
+  if (s != I8L_OK) return s;
+  if (isnan(threshold)) return fail(I8L_ERR_INVALID_ARG, "%s: threshold is NaN", fn);
+  const bool enabled = threshold > 0.0f && isfinite(threshold);
+  if (M == 0) {
+    // no rows: no outliers; only the count (0) is written, so only it is required
+    REQUIRE_PTR(fn, n_outliers, 4);
+    (void)hipGetLastError();
+    return hip_status(fn, i8l::launch_fill_u32(reinterpret_cast<uint32_t*>(n_outliers), 1, 0u,
+                                               static_cast<hipStream_t>(stream)));
+  }
+  REQUIRE_PTR(fn, X, 16);
+  REQUIRE_PTR(fn, Xq, 16);
+  REQUIRE_PTR(fn, sx, 4);
+  REQUIRE_PTR(fn, outlier_idx, 4);
+  REQUIRE_PTR(fn, n_outliers, 4);
+  REQUIRE_PTR(fn, X_outliers, 16);
+  REQUIRE_PTR(fn, workspace, 16);
+  const i8l_workspace_layout L = layout_of(M, K);
+  if (workspace_bytes < L.total)
+    return fail(I8L_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn,
+                workspace_bytes, L.total);
+  (void)hipGetLastError();
+  i8l::Workspace w = carve(workspace, L);
+  w.n_out = n_outliers;
+  w.idx = outlier_idx;
+  w.sx = sx;
+  w.Xq = Xq;
+  w.X_O = X_outliers;
+  return hip_status(fn, i8l::launch_quantize_activation(X, (int)M, (int)K, threshold, enabled, w,
+                                                        static_cast<hipStream_t>(stream)));
+}
+
+I8L_API i8l_status int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N,
+                                 int64_t K, int32_t* acc, void* stream) {
+  const char* fn = "int8_gemm_i32";
+  i8l_status s = check_shape(fn, M, K, N);
+  if (s != I8L_OK) return s;
+  if (M == 0 || N == 0) return ok();
+  REQUIRE_PTR(fn, Xq, 16);
+  REQUIRE_PTR(fn, Wq, 16);
+  REQUIRE_PTR(fn, acc, 16);
+  (void)hipGetLastError();
+  i8l::GemmArgs g{Xq, Wq, (int)M, (int)N, (int)K, nullptr, nullptr, nullptr, nullptr,
+                  nullptr, nullptr, nullptr, acc};
+  return hip_status(fn, i8l::launch_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+I8L_API const char* i8l_last_error(void) { return g_err; }
+
+I8L_API const char* i8l_build_info(void) {
+  static char info[512];
+  snprintf(info, sizeof(info), "int8lin gfx950; %s; decode: fused small-M kernel",
+           i8l::gemm_tile_info());
+  return info;
+}

@@ -1,0 +1,61 @@
+// Internal launchers of the gfx950 kernels; the C ABI (int8lin_abi.hip) calls
+// these after validating its arguments on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace i8l {
+
+// Workspace carving shared by int8_linear and int8_quantize_activation.
+struct Workspace {
+  int32_t* n_out;      // [1]
+  int32_t* idx;        // [K]
+  float* sx;           // [M]
+  int8_t* Xq;          // [M][K]
+  uint16_t* X_O;       // [M][K] capacity, row stride K
+  uint32_t* flags;     // [ceil(K/32)]
+};
+
+// p[0 .. n) = v, as a kernel (a fill kernel rather than a memset node keeps the
+// sequence safe to capture in a HIP graph).
+hipError_t launch_fill_u32(uint32_t* p, int n, uint32_t v, hipStream_t stream);
+
+hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, float* sw,
+                                  hipStream_t stream);
+
+// Outlier column scan + row quantization (two kernels after a flag clear).
+// `enabled` false skips the scan: no column is an outlier.
+hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float threshold,
+                                      bool enabled, const Workspace& ws, hipStream_t stream);
+
+// int8 GEMM on the matrix cores.  With Y != nullptr: dequantize with sx/sw, add
+// the fp16 outlier product (X_O against rows idx of W_rows) and store fp16 Y.
+// With acc != nullptr: store the raw int32 accumulators instead.
+struct GemmArgs {
+  const int8_t* Xq;
+  const int8_t* Wq;
+  int M, N, K;
+  const float* sx;
+  const float* sw;
+  const int32_t* n_out;
+  const int32_t* idx;
+  const uint16_t* X_O;      // row stride K
+  const uint16_t* W_rows;   // [K][N]
+  uint16_t* Y;
+  int32_t* acc;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+// Small-M (decode) path: one fused kernel doing the activation stage, the
+// int8 product, the outlier product and the epilogue.  Applicable when
+// decode_fits(M, K) holds.
+bool decode_fits(int M, int K);
+hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
+                         int N, const uint16_t* W_rows, float threshold, bool enabled,
+                         uint16_t* Y, const Workspace& ws, hipStream_t stream);
+
+const char* gemm_tile_info();
+
+}  // namespace i8l

@@ -25,3 +25,15 @@ def read_golden(name):
             key, _, val = line.partition(":")
             out[key.strip()] = val.split()
     return out
+
+
+@pytest.fixture(scope="session")
+def i8l():
+    """The binding, with libint8lin.so built in-tree first if it is missing."""
+    import mixed_precision_quantized_int8_amd as pkg
+    from mixed_precision_quantized_int8_amd import _binding, build
+
+    if not os.path.exists(_binding.LIB_PATH):
+        build.build_library()
+    pkg.lib()
+    return pkg

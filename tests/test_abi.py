@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "int8lin.h")
+OK, INVALID, K_TOO_LARGE, WORKSPACE = 0, 1, 2, 3
+P16 = 0x10000      # fake, 16-byte aligned, never dereferenced: every call below fails
+                   # validation (or is an empty no-op) before touching the device
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", src)))
+
+
+def test_header_matches_binding(i8l):
+    assert declared_functions() == sorted(i8l.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(i8l):
+    from mixed_precision_quantized_int8_amd import _binding
+
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    text = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared_functions():
+        assert name in text, name
+        assert hasattr(i8l.lib(), name)
+
+
+def test_build_info(i8l):
+    info = i8l.build_info()
+    assert "gfx950" in info
+
+
+def _linear(L, X=P16, M=32, K=64, Wq=P16, sw=P16, N=32, W=P16, t=6.0, Y=P16, ws=P16,
+            wsb=1 << 40):
+    return L.int8_linear(X, M, K, Wq, sw, N, W, t, Y, ws, wsb, None)
+
+
+def test_linear_validation(i8l):
+    L = i8l.lib()
+    assert _linear(L, X=None) == INVALID and "X is NULL" in i8l.last_error()
+    assert _linear(L, Wq=None) == INVALID
+    assert _linear(L, sw=None) == INVALID
+    assert _linear(L, Y=None) == INVALID
+    assert _linear(L, ws=None) == INVALID
+    assert _linear(L, W=None) == INVALID and "W_outlier_rows" in i8l.last_error()
+    assert _linear(L, K=0) == INVALID
+    assert _linear(L, K=8) == INVALID
+    assert _linear(L, K=72) == INVALID
+    assert _linear(L, K=-16) == INVALID
+    assert _linear(L, M=-1) == INVALID
+    assert _linear(L, N=-1) == INVALID
+    assert _linear(L, K=133152) == K_TOO_LARGE
+    assert _linear(L, K=133136, M=0) == OK          # largest K accepted (empty call)
+    assert _linear(L, t=math.nan) == INVALID and "NaN" in i8l.last_error()
+    assert _linear(L, X=P16 + 8) == INVALID and "aligned" in i8l.last_error()
+    assert _linear(L, Y=P16 + 2) == INVALID
+    assert _linear(L, sw=P16 + 2) == INVALID
+    assert _linear(L, W=P16 + 1) == INVALID
+    assert _linear(L, ws=P16 + 4) == INVALID
+    need = i8l.workspace_bytes(32, 64, 32)
+    assert _linear(L, wsb=need - 1) == WORKSPACE and str(need) in i8l.last_error()
+
+
+def test_linear_empty_calls_are_noops(i8l):
+    L = i8l.lib()
+    assert _linear(L, M=0) == OK and i8l.last_error() == ""
+    assert _linear(L, N=0) == OK
+    # decomposition disabled: W may be NULL
+    for t in (0.0, -1.0, math.inf):
+        assert _linear(L, M=0, W=None, t=t) == OK
+
+
+def test_other_entry_points_validate(i8l):
+    L = i8l.lib()
+    assert L.int8_quantize_weight(None, 64, 32, P16, P16, None) == INVALID
+    assert L.int8_quantize_weight(P16, 64, 32, P16 + 8, P16, None) == INVALID
+    assert L.int8_quantize_weight(P16, 70, 32, P16, P16, None) == INVALID
+    assert L.int8_quantize_weight(P16, 200000, 32, P16, P16, None) == K_TOO_LARGE
+    assert L.int8_quantize_weight(P16, 64, 0, P16, P16, None) == OK
+    assert L.int8_gemm_i32(P16, P16, 4, 4, 24, P16, None) == INVALID
+    assert L.int8_gemm_i32(None, P16, 4, 4, 32, P16, None) == INVALID
+    assert L.int8_gemm_i32(P16, P16, 0, 4, 32, P16, None) == OK
+    args = [P16, 8, 64, 6.0, P16, P16, P16, P16, P16, P16, 1 << 40, None]
+    for i in (0, 4, 5, 6, 7, 8, 9):
+        bad = list(args)
+        bad[i] = None
+        assert L.int8_quantize_activation(*bad) == INVALID, i
+    bad = list(args)
+    bad[3] = math.nan
+    assert L.int8_quantize_activation(*bad) == INVALID
+    bad = list(args)
+    bad[10] = 16
+    assert L.int8_quantize_activation(*bad) == WORKSPACE
+
+
+def test_workspace_layout(i8l):
+    for (M, K) in [(1, 16), (16, 1024), (2048, 14336), (4096, 57344), (300, 272)]:
+        L = i8l.workspace_layout(M, K, 123)
+        offs = [L[k] for k in ("n_outliers", "outlier_idx", "sx", "flags", "Xq", "X_outliers")]
+        assert all(o % 256 == 0 for o in offs)
+        assert offs == sorted(offs)
+        assert L["outlier_idx"] - L["n_outliers"] >= 4
+        assert L["sx"] - L["outlier_idx"] >= 4 * K
+        assert L["flags"] - L["sx"] >= 4 * M
+        assert L["Xq"] - L["flags"] >= 4 * ((K + 31) // 32)
+        assert L["X_outliers"] - L["Xq"] >= M * K
+        assert L["total"] - L["X_outliers"] >= 2 * M * K
+        assert i8l.workspace_bytes(M, K, 7) == L["total"]
+    assert i8l.workspace_bytes(4, 70, 4) == 0
+    with pytest.raises(i8l.Int8LinError):
+        i8l.workspace_layout(4, 70)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    from mixed_precision_quantized_int8_amd import _binding
+
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", "/nonexistent/libint8lin.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        _binding.lib()

@@ -1,0 +1,300 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on MI355X.
+
+Integer work (outlier sets, codes, scales, int32 accumulators) must match
+bit-exactly; fp16 outputs must satisfy |Y - Y64| <= max(2e-3 |Y64|, 1e-2)
+against the oracle's fp64 value, with infinities matching exactly.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+
+from mixed_precision_quantized_int8_amd import workloads as wl
+from oracle import int8_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+RTOL, ATOL = 2e-3, 1e-2
+
+
+@pytest.fixture(scope="module")
+def lib(i8l):
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    return i8l
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def assert_y(Yg, Y64, Y16=None, what=""):
+    Yg = np.asarray(Yg)
+    y = Yg.astype(np.float64)
+    if Y16 is None:
+        with np.errstate(over="ignore"):
+            Y16 = Y64.astype(np.float16)
+    inf = np.isinf(Y16)
+    np.testing.assert_array_equal(Yg[inf], Y16[inf], err_msg=f"{what}: infinities differ")
+    fin = ~inf
+    err = np.abs(y[fin] - Y64[fin])
+    tol = np.maximum(RTOL * np.abs(Y64[fin]), ATOL)
+    bad = ~(err <= tol)
+    if bad.any():
+        k = np.argmax(err - tol)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst "
+                             f"gpu={y[fin][k]!r} ref={Y64[fin][k]!r}")
+
+
+def check_workspace(lib, ws, M, K, act, what=""):
+    Xq_o, sx_o, idx_o, XO_o = act
+    v = lib.workspace_views(ws, M, K)
+    n = int(host(v["n_out"])[0])
+    assert n == len(idx_o), f"{what}: n_out {n} != {len(idx_o)}"
+    np.testing.assert_array_equal(host(v["idx"])[:n], idx_o, err_msg=f"{what}: idx")
+    np.testing.assert_array_equal(host(v["sx"]).view(np.uint32), sx_o.view(np.uint32),
+                                  err_msg=f"{what}: sx")
+    np.testing.assert_array_equal(host(v["Xq"]), Xq_o, err_msg=f"{what}: Xq")
+    if n:
+        np.testing.assert_array_equal(host(v["X_O"])[:, :n].view(np.uint16),
+                                      XO_o.view(np.uint16), err_msg=f"{what}: X_O")
+
+
+def run_linear(lib, X, W, t, pass_w=True):
+    Xd, Wd = dev(X), dev(W)
+    Wq, sw = lib.quantize_weight(Wd)
+    M, K = X.shape
+    N = W.shape[1]
+    ws = lib.new_workspace(M, K, N, Xd.device)
+    Y = lib.linear(Xd, Wq, sw, Wd if pass_w else None, t, workspace=ws)
+    return Y, Wq, sw, ws
+
+
+# ---------------------------------------------------------------------------------
+# weight quantization
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("K,N,seed", [(1024, 4096, 1), (4096, 16384, 2), (272, 520, 3),
+                                      (64, 7, 4), (16, 1, 5), (1040, 33, 6)])
+def test_quantize_weight_bitexact(lib, K, N, seed):
+    say(f"quantize_weight K={K} N={N}")
+    W = wl.make_w(K, N, 0.02, seed)
+    if N > 3:
+        W[:, 1] = 0                                  # absmax 0
+        W[:, 2] = 0
+        W[0, 2] = np.float16(127 / 32)               # scale exactly 32: ties
+        W[1:6, 2] = np.array([5, -5, 7, 9, -9], np.float16) / np.float16(64)
+    Wq, sw = lib.quantize_weight(dev(W))
+    Wq_o, sw_o = O.quantize_weight(W)
+    np.testing.assert_array_equal(host(sw).view(np.uint32), sw_o.view(np.uint32))
+    np.testing.assert_array_equal(host(Wq), Wq_o)
+
+
+# ---------------------------------------------------------------------------------
+# activation stage (stage export)
+# ---------------------------------------------------------------------------------
+def _act_cases():
+    yield "tiny", *wl.make_x(16, 1024, 1.0, 2, 8, 20, 1), 6.0
+    yield "decode", *wl.make_x(8, 4096, 1.0, 4, 6.5, 40, 2), 6.0
+    yield "ragged", *wl.make_x(300, 272, 1.0, 5, 8, 20, 3), 6.0
+    yield "one_row", *wl.make_x(1, 16, 1.0, 0, 8, 20, 4), 6.0
+    yield "k_mod32_16", *wl.make_x(17, 1040, 1.0, 3, 8, 20, 5), 6.0
+    yield "many_outliers", *wl.make_x(40, 512, 1.0, 45, 8, 20, 6), 6.0
+    X, c = wl.make_x(33, 256, 1.0, 0, 8, 20, 7)
+    yield "all_outliers", X, c, 2.0 ** -24
+    yield "disabled_inf", X, c, math.inf
+    yield "disabled_zero", X, c, 0.0
+    X, c = wl.make_x(24, 128, 0.25, 0, 8, 20, 8)
+    X[3, 5] = 6.0
+    X[7, 9] = np.float16(5.99609375)
+    X[11, 100] = -6.0
+    X[5, :] = 0
+    yield "boundary", X, c, 6.0
+
+
+@pytest.mark.parametrize("case", list(_act_cases()), ids=lambda c: c[0])
+def test_quantize_activation_bitexact(lib, case):
+    name, X, _, t = case
+    say(f"quantize_activation {name} M={X.shape[0]} K={X.shape[1]} t={t}")
+    r = lib.quantize_activation(dev(X), t)
+    Xq_o, sx_o, idx_o, XO_o = O.quantize_activation(X, t)
+    n = int(host(r["n_out"])[0])
+    assert n == len(idx_o)
+    np.testing.assert_array_equal(host(r["idx"])[:n], idx_o)
+    np.testing.assert_array_equal(host(r["sx"]).view(np.uint32), sx_o.view(np.uint32))
+    np.testing.assert_array_equal(host(r["Xq"]), Xq_o)
+    np.testing.assert_array_equal(host(r["X_O"])[:, :n].view(np.uint16), XO_o.view(np.uint16))
+
+
+# ---------------------------------------------------------------------------------
+# exact int8 GEMM (stage export)
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,N", [(16, 1024, 4096), (300, 272, 520), (513, 1040, 257),
+                                   (256, 128, 256), (1, 16, 1)])
+def test_gemm_i32_bitexact(lib, M, K, N):
+    say(f"gemm_i32 M={M} K={K} N={N}")
+    rng = np.random.default_rng(M * 7 + K + N)
+    Xq = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    Wq = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    acc = lib.gemm_i32(dev(Xq), dev(Wq))
+    np.testing.assert_array_equal(host(acc), O.int8_matmul(Xq, Wq))
+
+
+def test_gemm_i32_extremes(lib):
+    say("gemm_i32 extremes")
+    M, N, K = 64, 80, 8192
+    Xq = np.full((M, K), 127, np.int8)
+    Xq[1::2] = -127
+    Wq = np.full((N, K), 127, np.int8)
+    Wq[::3, ::2] = -127
+    acc = lib.gemm_i32(dev(Xq), dev(Wq))
+    np.testing.assert_array_equal(host(acc), O.int8_matmul(Xq, Wq))
+
+
+# ---------------------------------------------------------------------------------
+# the whole layer through int8_linear (small M: fused decode kernel; larger M: GEMM)
+# ---------------------------------------------------------------------------------
+def _linear_cases():
+    # name, M, K, N, n_out, threshold, x_sigma
+    yield "decode_small", 8, 1024, 4096, 2, 6.0, 1.0
+    yield "decode_m1", 1, 512, 1000, 1, 6.0, 1.0
+    yield "decode_m16", 16, 4096, 512, 3, 6.0, 1.0
+    yield "decode_m12_k2048", 12, 2048, 300, 2, 6.0, 1.0
+    yield "decode_k8192", 8, 8192, 256, 5, 6.0, 1.0
+    yield "decode_k_mod64", 5, 1040, 200, 2, 6.0, 1.0
+    yield "decode_unfused_bigk", 8, 16384, 256, 4, 6.0, 1.0
+    yield "decode_many_outliers", 4, 1024, 130, 70, 6.0, 1.0
+    yield "prefill_m17", 17, 1024, 600, 2, 6.0, 1.0
+    yield "prefill_ragged", 300, 272, 520, 5, 6.0, 1.0
+    yield "prefill_tiles", 513, 1040, 769, 8, 6.0, 1.0
+    yield "prefill_chunks", 64, 512, 300, 45, 6.0, 1.0
+    yield "prefill_no_outliers", 260, 512, 512, 0, 6.0, 1.0
+    yield "prefill_disabled", 260, 512, 512, 3, math.inf, 1.0
+    yield "prefill_all_outliers", 70, 256, 96, 0, 2.0 ** -24, 1.0
+    yield "decode_all_outliers", 6, 256, 96, 0, 2.0 ** -24, 1.0
+
+
+@pytest.mark.parametrize("case", list(_linear_cases()), ids=lambda c: c[0])
+def test_linear_parity(lib, case):
+    name, M, K, N, n_out, t, xs = case
+    say(f"int8_linear {name} M={M} K={K} N={N} n_out={n_out} t={t}")
+    X, W, _ = wl.make_small(M, K, N, seed=zlib.crc32(name.encode()) % 1000, n_out=n_out, x_sigma=xs)
+    if name.startswith("prefill_ragged") or name.startswith("decode_m12"):
+        X[2, :] = 0                                   # zero row
+        W[:, 5] = 0                                   # zero output column
+    pass_w = not math.isinf(t)
+    Y, Wq, sw, ws = run_linear(lib, X, W, t, pass_w)
+    Wq_o, sw_o = O.quantize_weight(W)
+    np.testing.assert_array_equal(host(Wq), Wq_o)
+    r = O.int8_linear(X, Wq_o, sw_o, W, t)
+    check_workspace(lib, ws, M, K, (r["Xq"], r["sx"], r["idx"], r["X_O"]), name)
+    assert_y(host(Y), r["Y64"], r["Y"], name)
+
+
+def test_linear_overflow_to_inf(lib):
+    say("int8_linear overflow")
+    M, K, N = 20, 64, 32
+    X = np.full((M, K), 5.0, np.float16)
+    X[::2] = -5.0
+    W = np.full((K, N), 300.0, np.float16)
+    W[:, ::3] = 1.0
+    Y, *_ = run_linear(lib, X, W, 6.0)
+    Wq_o, sw_o = O.quantize_weight(W)
+    r = O.int8_linear(X, Wq_o, sw_o, W, 6.0)
+    assert np.isinf(r["Y"]).any()
+    assert_y(host(Y), r["Y64"], r["Y"], "overflow")
+
+
+def test_linear_empty(lib):
+    say("int8_linear empty")
+    W = np.zeros((64, 8), np.float16)
+    Wd = dev(W)
+    Wq, sw = lib.quantize_weight(Wd)
+    Y = lib.linear(dev(np.zeros((0, 64), np.float16)), Wq, sw, Wd, 6.0)
+    assert tuple(Y.shape) == (0, 8)
+    Wq0 = torch.empty((0, 64), dtype=torch.int8, device="cuda:0")
+    sw0 = torch.empty((0,), dtype=torch.float32, device="cuda:0")
+    Y0 = lib.linear(dev(np.ones((4, 64), np.float16)), Wq0, sw0, None, math.inf)
+    assert tuple(Y0.shape) == (4, 0)
+
+
+def test_linear_deterministic(lib):
+    say("int8_linear determinism")
+    for (M, K, N) in [(8, 4096, 2048), (300, 1024, 700)]:
+        X, W, _ = wl.make_small(M, K, N, seed=9, n_out=3)
+        Y1, *_ = run_linear(lib, X, W, 6.0)
+        Y2, *_ = run_linear(lib, X, W, 6.0)
+        np.testing.assert_array_equal(host(Y1).view(np.uint16), host(Y2).view(np.uint16))
+
+
+# ---------------------------------------------------------------------------------
+# the benchmark workloads at full size, in the launch configuration bench.py times
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_workload_full_oracle(lib, name):
+    w = wl.WORKLOADS[name]
+    say(f"workload {name} (full oracle)")
+    X, W, cols = wl.make_inputs(w)
+    Y, Wq, sw, ws = run_linear(lib, X, W, w.threshold)
+    Wq_o, sw_o = O.quantize_weight(W)
+    np.testing.assert_array_equal(host(Wq), Wq_o)
+    np.testing.assert_array_equal(host(sw).view(np.uint32), sw_o.view(np.uint32))
+    r = O.int8_linear(X, Wq_o, sw_o, W, w.threshold)
+    np.testing.assert_array_equal(r["idx"], np.sort(cols))
+    check_workspace(lib, ws, w.M, w.K, (r["Xq"], r["sx"], r["idx"], r["X_O"]), name)
+    assert_y(host(Y), r["Y64"], r["Y"], name)
+
+
+@pytest.mark.parametrize("name", ["qkv_prefill", "mlp_down_prefill", "square_0pct",
+                                  "square_0.1pct", "square_1pct"])
+def test_workload_full_sampled(lib, name):
+    w = wl.WORKLOADS[name]
+    say(f"workload {name} (sampled): generating inputs")
+    X, W, cols = wl.make_inputs(w)
+    say(f"workload {name}: running GPU")
+    Xd, Wd = dev(X), dev(W)
+    Wq, sw = lib.quantize_weight(Wd)
+    ws = lib.new_workspace(w.M, w.K, w.N, Xd.device)
+    Y = lib.linear(Xd, Wq, sw, Wd, w.threshold, workspace=ws)
+    torch.cuda.synchronize()
+    say(f"workload {name}: activation stage, full")
+    act = O.quantize_activation(X, w.threshold)
+    np.testing.assert_array_equal(act[2], np.sort(cols))
+    check_workspace(lib, ws, w.M, w.K, act, name)
+
+    rng = np.random.default_rng(1234)
+    ns = np.unique(np.concatenate([rng.integers(0, w.N, 48), [0, 255, 256, w.N - 1]]))
+    say(f"workload {name}: {len(ns)} weight rows")
+    Wq_r, sw_r = O.quantize_weight_rows(W, ns)
+    np.testing.assert_array_equal(host(Wq[torch.as_tensor(ns, device='cuda:0')]), Wq_r)
+    np.testing.assert_array_equal(host(sw[torch.as_tensor(ns, device='cuda:0')]).view(np.uint32),
+                                  sw_r.view(np.uint32))
+
+    # sampled outputs (inside, on tile edges and on the last row / column)
+    S = 3000
+    rows = np.concatenate([rng.integers(0, w.M, S), [0, w.M - 1, 255, 256, w.M - 1]])
+    pick = rng.integers(0, len(ns), len(rows))
+    colsel = ns[pick]
+    acc_o, Y64 = O.int8_linear_entries(X, Wq_r[pick], sw_r[pick], W, w.threshold, rows, colsel,
+                                       act=act)
+    ri = torch.as_tensor(rows, device="cuda:0")
+    ci = torch.as_tensor(colsel, device="cuda:0")
+    assert_y(host(Y[ri, ci]), Y64, what=name)
+    assert torch.isfinite(Y).all().item()
+    # exact int32 accumulators at the same entries via the GEMM stage
+    v = lib.workspace_views(ws, w.M, w.K)
+    acc = lib.gemm_i32(v["Xq"].contiguous(), Wq)
+    np.testing.assert_array_equal(host(acc[ri, ci]), acc_o)
+    del acc, Y, Wq, ws, Xd, Wd
+    torch.cuda.empty_cache()
