@@ -13,7 +13,8 @@
 // the matrix-core operands want: each lane feeds 16 consecutive k of one row.
 //
 // Tiling (256 threads = 4 waves of 64, one workgroup per CU):
-//   workgroup tile 256 x 256, K step 64 bytes, LDS double buffered (64 KB);
+//   workgroup tile 256 x 256, K step 64 bytes; a 4-stage LDS ring (128 KB) fed
+//   by direct global->LDS loads (global_load_lds_dwordx4), three stages ahead;
 //   each wave owns a 128 x 128 sub-tile = 8 x 8 blocks of v_mfma_i32_16x16x64_i8
 //   whose 256 int32 accumulators per lane live in the accumulation registers.
 //   LDS rows are 64 bytes = four 16-byte chunks; chunk c of row r is stored at
@@ -38,6 +39,7 @@ namespace i8l {
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 8;
+constexpr int kStages = 4;   // LDS ring depth (32 KB per stage)
 
 __device__ __forceinline__ int lds_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
@@ -56,10 +58,23 @@ __device__ __forceinline__ void tile_coords(int bid, int nTm, int nTn, int& tm, 
   tn = in / gm;
 }
 
+#define I8L_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+// Workgroup barrier without a memory fence (outstanding LDS-DMA loads stay in
+// flight); the memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <bool OUT_I32>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) int8_t sA[2][kBM * kBK];
-  __shared__ __attribute__((aligned(16))) int8_t sB[2][kBN * kBK];
+  // kStages ring buffers of [A 256 x 64 | B 256 x 64] bytes
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kStages][2][kBM * kBK];
 
   const int M = a.M, N = a.N, K = a.K;
   const int nTm = (M + kBM - 1) / kBM, nTn = (N + kBN - 1) / kBN;
@@ -72,29 +87,47 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   const int l16 = lane & 15, lg = lane >> 4;
 
-  // global -> register staging: 4 chunks of 16 bytes per operand per thread
-  v4i ra[4], rb[4];
-  auto load_tile = [&](int k0) {
+  // Direct global -> LDS loads.  One instruction moves 64 lanes x 16 bytes into
+  // 1 KB of LDS (16 rows of 64 bytes); lane l lands at row 16*blk + l/4,
+  // physical chunk l%4, so it fetches the logical chunk (l%4) ^ swz(row).
+  // Wave w fills blocks 4w .. 4w+3 of A and of B: 8 loads per stage.
+  // Rows past M (or N) are clamped to the last row: they only feed outputs
+  // that are never stored.  K-tail chunks are zeroed in LDS (zero_k_tail).
+  // Every address stays inside the operand.
+  uint32_t rowA[4], rowB[4];   // byte offset of the (clamped) row inside the tile
+  int cofs[4];                 // byte offset of the lane's logical 16-byte chunk
+  const int lastA = min(M - m0, kBM) - 1, lastB = min(N - n0, kBN) - 1;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int q = t + kGemmThreads * s;
-      const int row = q >> 2, c = q & 3;
-      const int k = k0 + c * 16;
-      const int gm = m0 + row, gn = n0 + row;
-      ra[s] = (gm < M && k < K) ? *reinterpret_cast<const v4i*>(a.Xq + (size_t)gm * K + k)
-                                : v4i{0, 0, 0, 0};
-      rb[s] = (gn < N && k < K) ? *reinterpret_cast<const v4i*>(a.Wq + (size_t)gn * K + k)
-                                : v4i{0, 0, 0, 0};
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wave * 4 + i) * 16 + (lane >> 2);
+    cofs[i] = ((lane & 3) ^ lds_swz(row)) * 16;
+    rowA[i] = (uint32_t)(min(row, lastA) * K);
+    rowB[i] = (uint32_t)(min(row, lastB) * K);
+  }
+  const int8_t* tileA = a.Xq + (size_t)m0 * K;
+  const int8_t* tileB = a.Wq + (size_t)n0 * K;
+  auto issue = [&](int stage, int kt) {
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // a chunk past K reads the row's first chunk instead (stays inside the
+      // operand); zero_k_tail overwrites it in LDS
+      const int kk = k0 + cofs[i] < K ? k0 + cofs[i] : 0;
+      __builtin_amdgcn_global_load_lds((const void*)(tileA + rowA[i] + kk),
+                                       I8L_LDS(&smem[stage][0][(wave * 4 + i) * 1024]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(tileB + rowB[i] + kk),
+                                       I8L_LDS(&smem[stage][1][(wave * 4 + i) * 1024]), 16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int q = t + kGemmThreads * s;
-      const int row = q >> 2, c = q & 3;
-      const int off = row * kBK + ((c ^ lds_swz(row)) << 4);
-      *reinterpret_cast<v4i*>(&sA[buf][off]) = ra[s];
-      *reinterpret_cast<v4i*>(&sB[buf][off]) = rb[s];
+  // Last stage when K % 64 != 0: the chunks at k >= K hold a copy of the
+  // row's first chunk; replace them by zeros.
+  const int ktail = K % kBK;
+  auto zero_k_tail = [&](int stage) {
+    for (int q = t; q < 2 * kBM * 4; q += kGemmThreads) {
+      const int op = q / (kBM * 4), row = (q / 4) % kBM, c = q & 3;
+      if (c * 16 >= ktail)
+        *reinterpret_cast<v4i*>(&smem[stage][op][row * kBK + ((c ^ lds_swz(row)) << 4)]) =
+            v4i{0, 0, 0, 0};
     }
   };
 
@@ -105,29 +138,72 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
   const int nk = (K + kBK - 1) / kBK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile((kt + 1) * kBK);
-    v4i fa[8];
+  // Fragment reads of one stage: 8 A blocks and 8 B blocks of 16 rows x 64 bytes.
+  auto read_frags = [&](int kt, v4i (&fa)[8], v4i (&fb)[8]) {
+    const int8_t* sA = smem[kt % kStages][0];
+    const int8_t* sB = smem[kt % kStages][1];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = wm + i * 16 + l16;
-      fa[i] = *reinterpret_cast<const v4i*>(&sA[buf][row * kBK + ((lg ^ lds_swz(row)) << 4)]);
+      fa[i] = *reinterpret_cast<const v4i*>(&sA[row * kBK + ((lg ^ lds_swz(row)) << 4)]);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = wn + j * 16 + l16;
-      const v4i fb = *reinterpret_cast<const v4i*>(&sB[buf][row * kBK + ((lg ^ lds_swz(row)) << 4)]);
+      fb[j] = *reinterpret_cast<const v4i*>(&sB[row * kBK + ((lg ^ lds_swz(row)) << 4)]);
+    }
+  };
+  // Make stage `kt` visible to every wave.  Stages after it stay in flight:
+  // at this point stages kt .. min(kt + kStages - 3, nk - 1) are outstanding.
+  auto wait_stage = [&](int kt) {
+    const int ahead = min(kStages - 3, nk - 1 - kt);
+    if (ahead >= 1) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+  };
+  // One k-step: 64 MFMAs on fragments already in registers (stage kt), while
+  // the fragments of stage kt + 1 are read from LDS.
+  auto step = [&](int kt, v4i (&ca)[8], v4i (&cb)[8], v4i (&na)[8], v4i (&nb)[8]) {
+    if (kt + 1 < nk) {
+      wait_stage(kt + 1);
+      if (ktail && kt + 2 == nk) {
+        zero_k_tail((kt + 1) % kStages);
+        lds_barrier();
+      }
+      // the buffer refilled here was last read for stage kt - 1, whose
+      // fragments every wave consumed before the barrier above
+      if (kt + kStages - 1 < nk) issue((kt + kStages - 1) % kStages, kt + kStages - 1);
+      read_frags(kt + 1, na, nb);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb, acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
-    __syncthreads();
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ca[i], cb[j], acc[i][j], 0, 0, 0);
+  };
+
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nk) issue(s, s);
+  v4i a0[8], b0[8], a1[8], b1[8];
+  // stage 0 must land; the other stages issued above may stay in flight
+  static_assert(kStages == 4, "wait counts below assume a 4-stage ring");
+  if (nk >= 3) wait_vmcnt<16>();
+  else if (nk == 2) wait_vmcnt<8>();
+  else wait_vmcnt<0>();
+  lds_barrier();
+  if (ktail && nk == 1) {
+    zero_k_tail(0);
+    lds_barrier();
   }
+  read_frags(0, a0, b0);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, a0, b0, a1, b1);
+    step(kt + 1, a1, b1, a0, b0);
+  }
+  if (kt < nk) step(kt, a0, b0, a1, b1);
+  __syncthreads();   // all waves done with the ring before the epilogue reuses it
 
   // D layout of a 16x16 block: lane holds rows 4*(lane/16) + r, column lane % 16.
   if constexpr (OUT_I32) {
@@ -147,8 +223,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     // (bounds the live fp32 values to 8 blocks; the int32 accumulators stay in
     // the accumulation registers until their block is converted)
     const int n_out = *a.n_out;
-    uint16_t* sAo = reinterpret_cast<uint16_t*>(&sA[0][0]);   // [256 rows][32 halves]
-    uint16_t* sBo = reinterpret_cast<uint16_t*>(&sB[0][0]);   // [256 cols][32 halves]
+    uint16_t* sAo = reinterpret_cast<uint16_t*>(&smem[0][0][0]);   // [256 rows][32 halves]
+    uint16_t* sBo = reinterpret_cast<uint16_t*>(&smem[0][1][0]);   // [256 cols][32 halves]
     // Stage outlier columns j0 .. j0+31 of X_O and the matching weight rows
     // (transposed to [column][outlier]); zero past n_out.
     auto stage_outliers = [&](int j0) {

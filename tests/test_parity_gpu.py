@@ -141,7 +141,8 @@ def test_quantize_activation_bitexact(lib, case):
 # exact int8 GEMM (stage export)
 # ---------------------------------------------------------------------------------
 @pytest.mark.parametrize("M,K,N", [(16, 1024, 4096), (300, 272, 520), (513, 1040, 257),
-                                   (256, 128, 256), (1, 16, 1)])
+                                   (256, 128, 256), (1, 16, 1), (257, 80, 300), (40, 144, 600),
+                                   (300, 48, 270), (1024, 4096, 1024)])
 def test_gemm_i32_bitexact(lib, M, K, N):
     say(f"gemm_i32 M={M} K={K} N={N}")
     rng = np.random.default_rng(M * 7 + K + N)
