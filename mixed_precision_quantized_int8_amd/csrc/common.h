@@ -44,6 +44,14 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
          ((uint32_t)(d & 0xff) << 24);
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses,
+// then s_barrier.  Unlike __syncthreads() it does not wait for outstanding
+// global loads, so loads issued earlier stay in flight across it.  The memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
   return v;

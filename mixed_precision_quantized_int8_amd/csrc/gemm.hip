@@ -13,20 +13,31 @@
 // the matrix-core operands want: each lane feeds 16 consecutive k of one row.
 //
 // Tiling (256 threads = 4 waves of 64, one workgroup per CU):
-//   workgroup tile 256 x 256, K step 64 bytes; a 4-stage LDS ring (128 KB) fed
-//   by direct global->LDS loads (global_load_lds_dwordx4), three stages ahead;
-//   each wave owns a 128 x 128 sub-tile = 8 x 8 blocks of v_mfma_i32_16x16x64_i8
-//   whose 256 int32 accumulators per lane live in the accumulation registers.
-//   LDS rows are 64 bytes = four 16-byte chunks; chunk c of row r is stored at
-//   c ^ (((r >> 1) ^ (r >> 3)) & 3), so the 16-byte fragment reads of 8 or 16
-//   consecutive rows fall into distinct banks.
-//   Tiles are handed out XCD by XCD: workgroup b runs on XCD b % 8, and each
-//   XCD takes a contiguous range of tiles ordered in groups of 8 tile-rows so
-//   that concurrently running tiles share operand panels in that XCD's L2.
-// Epilogue, one 16-column block of the wave tile at a time: the int32
+//   * workgroup tile 256 x 256, K step 64 bytes;
+//   * a 4-stage LDS ring (4 x 32 KB) fed by direct global->LDS loads
+//     (global_load_lds_dwordx4), issued three stages ahead of use, with
+//     explicit vmcnt waits and a fence-free barrier so they stay in flight;
+//     every iteration issues exactly one stage (past the last stage it
+//     re-reads valid memory into a consumed buffer), so the loop body has no
+//     branches and the loads can be interleaved with the MFMAs;
+//   * each wave owns a 128 x 128 sub-tile = 4 x 4 blocks of
+//     v_mfma_i32_32x32x32_i8 (256 int32 accumulators per lane, held in the
+//     accumulation registers).  On gfx950 this shape sustains ~93% of the int8
+//     peak in a bare loop, against ~79% for v_mfma_i32_16x16x64_i8;
+//   * software pipeline at half-step granularity: while the 16 MFMAs of one
+//     32-byte k half run, the 8 fragments of the next half are read from LDS
+//     into the other of two fixed register sets; reads and loads are placed
+//     one per MFMA with sched_group_barrier;
+//   * LDS rows are 64 bytes = four 16-byte chunks; chunk c of row r is stored
+//     at c ^ (((r >> 1) ^ (r >> 3)) & 3), so the 16-byte fragment reads of 8
+//     or 16 consecutive rows fall into distinct banks;
+//   * tiles are handed out XCD by XCD: workgroup b runs on XCD b % 8, and each
+//     XCD takes a contiguous range of tiles ordered in groups of 8 tile-rows so
+//     that concurrently running tiles share operand panels in that XCD's L2.
+// Epilogue, one 32-column block of the wave tile at a time: the int32
 // accumulators of the block are dequantized to fp32 (acc * sx * sw / 127^2),
 // then the outlier product is accumulated onto them with
-// v_mfma_f32_16x16x32_f16 from X_O[256 x 32] and the matching 32 weight rows
+// v_mfma_f32_32x32x16_f16 from X_O[256 x 32] and the matching 32 weight rows
 // (transposed to [256 x 32]) staged in LDS, and the block is stored as fp16.
 // With at most 32 outlier columns the staging happens once per tile.  The
 // outlier count is read from device memory, so no host synchronization is
@@ -36,11 +47,13 @@
 
 namespace i8l {
 
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
 constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kStages = 4;   // LDS ring depth (32 KB per stage)
 constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 8;
-constexpr int kStages = 4;   // LDS ring depth (32 KB per stage)
-
 __device__ __forceinline__ int lds_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
 // Tile assignment: contiguous tile ranges per XCD, grouped order inside.
@@ -58,6 +71,10 @@ __device__ __forceinline__ void tile_coords(int bid, int nTm, int nTn, int& tm, 
   tn = in / gm;
 }
 
+// 16 bytes of zeros per lane for K-tail chunks (k >= K): the direct LDS loads
+// always write their 16 bytes.
+__device__ __attribute__((aligned(64))) int8_t g_zero_page[64];
+
 #define I8L_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and [15:14]).
@@ -66,10 +83,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt((0xf) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
 // Workgroup barrier without a memory fence (outstanding LDS-DMA loads stay in
 // flight); the memory clobber keeps the compiler from moving LDS accesses
 // across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// D layout of a 32x32 MFMA block: lane l holds column l % 32 and, in register
+// r, row 8 * (r / 4) + 4 * (l / 32) + r % 4.
+__device__ __forceinline__ int d_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
 
 template <bool OUT_I32>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
@@ -77,6 +103,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) int8_t smem[kStages][2][kBM * kBK];
 
   const int M = a.M, N = a.N, K = a.K;
+  const int nk = (K + kBK - 1) / kBK;   // k-steps of 64 bytes
   const int nTm = (M + kBM - 1) / kBM, nTn = (N + kBN - 1) / kBN;
   int tm, tn;
   tile_coords(blockIdx.x, nTm, nTn, tm, tn);
@@ -85,15 +112,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
-  const int l16 = lane & 15, lg = lane >> 4;
+  const int l32 = lane & 31, lh = lane >> 5;
 
   // Direct global -> LDS loads.  One instruction moves 64 lanes x 16 bytes into
   // 1 KB of LDS (16 rows of 64 bytes); lane l lands at row 16*blk + l/4,
   // physical chunk l%4, so it fetches the logical chunk (l%4) ^ swz(row).
   // Wave w fills blocks 4w .. 4w+3 of A and of B: 8 loads per stage.
   // Rows past M (or N) are clamped to the last row: they only feed outputs
-  // that are never stored.  K-tail chunks are zeroed in LDS (zero_k_tail).
-  // Every address stays inside the operand.
+  // that are never stored.  K-tail chunks read zeros from a device zero page.
+  // Every address stays inside the operands.
   uint32_t rowA[4], rowB[4];   // byte offset of the (clamped) row inside the tile
   int cofs[4];                 // byte offset of the lane's logical 16-byte chunk
   const int lastA = min(M - m0, kBM) - 1, lastB = min(N - n0, kBN) - 1;
@@ -106,122 +133,125 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   }
   const int8_t* tileA = a.Xq + (size_t)m0 * K;
   const int8_t* tileB = a.Wq + (size_t)n0 * K;
+  // Loads of stage kt into ring buffer `stage`; branch-free so that they can
+  // be interleaved with the MFMAs (K-tail chunks select the zero page per lane).
   auto issue = [&](int stage, int kt) {
     const int k0 = kt * kBK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // a chunk past K reads the row's first chunk instead (stays inside the
-      // operand); zero_k_tail overwrites it in LDS
-      const int kk = k0 + cofs[i] < K ? k0 + cofs[i] : 0;
-      __builtin_amdgcn_global_load_lds((const void*)(tileA + rowA[i] + kk),
+      const int kk = k0 + cofs[i];
+      const bool in = kk < K;
+      const int8_t* ga = in ? tileA + rowA[i] + kk : g_zero_page;
+      const int8_t* gb = in ? tileB + rowB[i] + kk : g_zero_page;
+      __builtin_amdgcn_global_load_lds((const void*)ga,
                                        I8L_LDS(&smem[stage][0][(wave * 4 + i) * 1024]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(tileB + rowB[i] + kk),
+      __builtin_amdgcn_global_load_lds((const void*)gb,
                                        I8L_LDS(&smem[stage][1][(wave * 4 + i) * 1024]), 16, 0, 0);
     }
   };
-  // Last stage when K % 64 != 0: the chunks at k >= K hold a copy of the
-  // row's first chunk; replace them by zeros.
-  const int ktail = K % kBK;
-  auto zero_k_tail = [&](int stage) {
-    for (int q = t; q < 2 * kBM * 4; q += kGemmThreads) {
-      const int op = q / (kBM * 4), row = (q / 4) % kBM, c = q & 3;
-      if (c * 16 >= ktail)
-        *reinterpret_cast<v4i*>(&smem[stage][op][row * kBK + ((c ^ lds_swz(row)) << 4)]) =
-            v4i{0, 0, 0, 0};
-    }
-  };
 
-  v4i acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
-  const int nk = (K + kBK - 1) / kBK;
-  // Fragment reads of one stage: 8 A blocks and 8 B blocks of 16 rows x 64 bytes.
-  auto read_frags = [&](int kt, v4i (&fa)[8], v4i (&fb)[8]) {
+  // Fragments of one 32-byte k half `h` of stage kt: 4 A blocks and 4 B blocks
+  // of 32 rows; lane l reads row l % 32, logical chunk 2h + l / 32.
+  auto read_half = [&](int kt, int h, v4i (&fa)[4], v4i (&fb)[4]) {
     const int8_t* sA = smem[kt % kStages][0];
     const int8_t* sB = smem[kt % kStages][1];
+    const int c = 2 * h + lh;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = wm + i * 16 + l16;
-      fa[i] = *reinterpret_cast<const v4i*>(&sA[row * kBK + ((lg ^ lds_swz(row)) << 4)]);
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm + i * 32 + l32;
+      fa[i] = *reinterpret_cast<const v4i*>(&sA[row * kBK + ((c ^ lds_swz(row)) << 4)]);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = wn + j * 16 + l16;
-      fb[j] = *reinterpret_cast<const v4i*>(&sB[row * kBK + ((lg ^ lds_swz(row)) << 4)]);
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn + j * 32 + l32;
+      fb[j] = *reinterpret_cast<const v4i*>(&sB[row * kBK + ((c ^ lds_swz(row)) << 4)]);
     }
-  };
-  // Make stage `kt` visible to every wave.  Stages after it stay in flight:
-  // at this point stages kt .. min(kt + kStages - 3, nk - 1) are outstanding.
-  auto wait_stage = [&](int kt) {
-    const int ahead = min(kStages - 3, nk - 1 - kt);
-    if (ahead >= 1) wait_vmcnt<8>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-  };
-  // One k-step: 64 MFMAs on fragments already in registers (stage kt), while
-  // the fragments of stage kt + 1 are read from LDS.
-  auto step = [&](int kt, v4i (&ca)[8], v4i (&cb)[8], v4i (&na)[8], v4i (&nb)[8]) {
-    if (kt + 1 < nk) {
-      wait_stage(kt + 1);
-      if (ktail && kt + 2 == nk) {
-        zero_k_tail((kt + 1) % kStages);
-        lds_barrier();
-      }
-      // the buffer refilled here was last read for stage kt - 1, whose
-      // fragments every wave consumed before the barrier above
-      if (kt + kStages - 1 < nk) issue((kt + kStages - 1) % kStages, kt + kStages - 1);
-      read_frags(kt + 1, na, nb);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ca[i], cb[j], acc[i][j], 0, 0, 0);
   };
 
+  v16i acc[4][4];
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) issue(s, s);
-  v4i a0[8], b0[8], a1[8], b1[8];
-  // stage 0 must land; the other stages issued above may stay in flight
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
+  auto mfma_one = [&](const v4i (&fa)[4], const v4i (&fb)[4], int q) {
+    const int i = q & 3, j = q >> 2;
+    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
+  constexpr int kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100;
+
+  // Every loop iteration issues exactly one stage of 8 loads per wave (past the
+  // last stage it re-reads stage nk-1 into the buffer of a consumed stage), so
+  // the number of loads issued after any stage is constant: when stage kt+1 is
+  // waited for, the kStages-3 newer stages may stay in flight.
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) issue(s, min(s, nk - 1));
   static_assert(kStages == 4, "wait counts below assume a 4-stage ring");
-  if (nk >= 3) wait_vmcnt<16>();
-  else if (nk == 2) wait_vmcnt<8>();
-  else wait_vmcnt<0>();
+  wait_vmcnt<16>();   // stage 0 landed, stages 1-2 in flight
   lds_barrier();
-  if (ktail && nk == 1) {
-    zero_k_tail(0);
+
+  v4i f0a[4], f0b[4], f1a[4], f1b[4];
+  read_half(0, 0, f0a, f0b);
+  for (int kt = 0; kt < nk; ++kt) {
+    // ---- half 0 of stage kt: MFMAs on f0, with the 8 reads of half 1 of
+    // stage kt interleaved one per MFMA.  The only outstanding LDS reads here
+    // are those of f0, so draining lgkmcnt first costs little and keeps the
+    // compiler from waiting for the new reads before the MFMAs.
+    wait_lgkmcnt0();
+    read_half(kt, 1, f1a, f1b);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mfma_one(f0a, f0b, q);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt0();
+    // ---- half 1: the first MFMA goes out before the stage wait and the
+    // barrier, so the matrix pipe is busy while the waves synchronize.
+    mfma_one(f1a, f1b, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // Stage kt+1 must have landed in every wave's view.
+    wait_vmcnt<8 * (kStages - 3)>();
     lds_barrier();
+    // The buffer refilled here held stage kt-1, whose fragments every wave
+    // finished reading before the barrier above.
+    issue((kt + kStages - 1) % kStages, min(kt + kStages - 1, nk - 1));
+    // On the last step this re-reads stage kt (landed, unused), so that the
+    // registers keep fixed roles.
+    read_half(kt + 1 < nk ? kt + 1 : kt, 0, f0a, f0b);
+#pragma unroll
+    for (int q = 1; q < 16; ++q) mfma_one(f1a, f1b, q);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 7, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  read_frags(0, a0, b0);
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, a0, b0, a1, b1);
-    step(kt + 1, a1, b1, a0, b0);
-  }
-  if (kt < nk) step(kt, a0, b0, a1, b1);
+  wait_vmcnt<0>();
+  wait_lgkmcnt0();
   __syncthreads();   // all waves done with the ring before the epilogue reuses it
 
-  // D layout of a 16x16 block: lane holds rows 4*(lane/16) + r, column lane % 16.
   if constexpr (OUT_I32) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn + j * 32 + l32;
+        if (n >= N) continue;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm + i * 16 + lg * 4 + r;
-          const int n = n0 + wn + j * 16 + l16;
-          if (m < M && n < N) a.acc[(size_t)m * N + n] = acc[i][j][r];
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm + i * 32 + d_row(r, lane);
+          if (m < M) a.acc[(size_t)m * N + n] = acc[i][j][r];
         }
+      }
     return;
   } else {
-    // ---- epilogue, one 16-column block of the wave tile at a time -----------
-    // (bounds the live fp32 values to 8 blocks; the int32 accumulators stay in
-    // the accumulation registers until their block is converted)
     const int n_out = *a.n_out;
     uint16_t* sAo = reinterpret_cast<uint16_t*>(&smem[0][0][0]);   // [256 rows][32 halves]
     uint16_t* sBo = reinterpret_cast<uint16_t*>(&smem[0][1][0]);   // [256 cols][32 halves]
@@ -265,68 +295,77 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
         *reinterpret_cast<v4i*>(&sBo[col * 32 + ((c ^ lds_swz(col)) << 3)]) = v;
       }
     };
-    auto load_ao = [&](v8h (&fa)[8]) {
+    // fp16 fragments for v_mfma_f32_32x32x16_f16: half h covers outliers
+    // 16h .. 16h+15; lane l reads row l % 32, logical chunk 2h + l / 32.
+    auto load_ao = [&](v8h (&fa)[4][2]) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = wm + i * 16 + l16;
-        fa[i] = *reinterpret_cast<const v8h*>(&sAo[row * 32 + ((lg ^ lds_swz(row)) << 3)]);
-      }
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = wm + i * 32 + l32;
+          fa[i][h] = *reinterpret_cast<const v8h*>(
+              &sAo[row * 32 + (((2 * h + lh) ^ lds_swz(row)) << 3)]);
+        }
     };
-    auto load_bo = [&](int j) {
-      const int col = wn + j * 16 + l16;
-      return *reinterpret_cast<const v8h*>(&sBo[col * 32 + ((lg ^ lds_swz(col)) << 3)]);
+    auto load_bo = [&](int j, v8h (&fb)[2]) {
+      const int col = wn + j * 32 + l32;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        fb[h] = *reinterpret_cast<const v8h*>(
+            &sBo[col * 32 + (((2 * h + lh) ^ lds_swz(col)) << 3)]);
     };
 
     const bool one_chunk = n_out <= 32;
-    v8h fo[8];
+    v8h fo[4][2];
     if (n_out > 0 && one_chunk) {
       stage_outliers(0);
       __syncthreads();
       load_ao(fo);
     }
-    float sxv[8][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm + i * 16 + lg * 4 + r;
-        sxv[i][r] = m < M ? a.sx[m] : 0.0f;
-      }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = n0 + wn + j * 16 + l16;
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + j * 32 + l32;
       const float swj = n < N ? a.sw[n] * (1.0f / 16129.0f) : 0.0f;
-      v4f y[8];
+      v16f y[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[i][r] = (float)acc[i][j][r] * (sxv[i][r] * swj);
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm + i * 32 + d_row(r, lane);
+          const float sxm = m < M ? a.sx[m] : 0.0f;
+          y[i][r] = (float)acc[i][j][r] * (sxm * swj);
+        }
       if (n_out > 0) {
         if (one_chunk) {
-          const v8h fb = load_bo(j);
+          v8h fb[2];
+          load_bo(j, fb);
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            y[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fo[i], fb, y[i], 0, 0, 0);
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              y[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fo[i][h], fb[h], y[i], 0, 0, 0);
         } else {
           for (int j0 = 0; j0 < n_out; j0 += 32) {
             __syncthreads();
             stage_outliers(j0);
             __syncthreads();
-            v8h fa[8];
+            v8h fa[4][2], fb[2];
             load_ao(fa);
-            const v8h fb = load_bo(j);
+            load_bo(j, fb);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-              y[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, y[i], 0, 0, 0);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                y[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i][h], fb[h], y[i], 0, 0, 0);
           }
         }
       }
       if (n < N) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = m0 + wm + i * 16 + lg * 4 + r;
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm + i * 32 + d_row(r, lane);
             if (m < M) a.Y[(size_t)m * N + n] = f2h(y[i][r]);
           }
       }
@@ -345,8 +384,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
 }
 
 const char* gemm_tile_info() {
-  return "gemm: 256x256x64 tile, 4 waves of 128x128, v_mfma_i32_16x16x64_i8, "
-         "v_mfma_f32_16x16x32_f16 outlier tail";
+  return "gemm: 256x256x64 tile, 4-stage LDS-DMA ring, 4 waves of 128x128, "
+         "v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_f16 outlier tail";
 }
 
 }  // namespace i8l

@@ -56,6 +56,11 @@ hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, cons
                          int N, const uint16_t* W_rows, float threshold, bool enabled,
                          uint16_t* Y, const Workspace& ws, hipStream_t stream);
 
+// Streaming part alone, reading the activation-stage results from `ws`.
+hipError_t launch_decode_unfused(const uint16_t* X, int M, int K, const int8_t* Wq,
+                                 const float* sw, int N, const uint16_t* W_rows, uint16_t* Y,
+                                 const Workspace& ws, hipStream_t stream);
+
 const char* gemm_tile_info();
 
 }  // namespace i8l
