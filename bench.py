@@ -7,6 +7,11 @@ resident in HBM; the weight is quantized once, untimed, as the layer does when
 it is placed on the GPU.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload decode]
+    python bench.py --copy-calibration 512   # plain 512 MiB device copy only
+
+--copy-calibration runs nothing but torch's device-to-device copy of a buffer
+of known size; under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it gives the
+factor that turns those counters into bytes.
 
 The default workload is the decode shape X 8x4096 . W 4096x16384 with 4
 outlier columns.  To keep the 256 MB Infinity Cache from serving the weight,
@@ -87,6 +92,38 @@ def cpu_baseline(w, X, W, budget_s=12.0):
     }, out, Wq, sw
 
 
+def copy_ceiling(torch, dev, mib=1024, reps=10):
+    """Device-to-device copy rate (bytes read + written per second) of torch's copy kernel."""
+    src = torch.empty((mib << 20,), dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(reps):
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return 2 * (mib << 20) / (best * 1e-3) / 1e9
+
+
+def copy_calibration(mib):
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    src = torch.empty((mib << 20,), dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": mib << 20,
+                      "copy_calibration_bytes_written": mib << 20, "launches": 3}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,12 +132,18 @@ def main():
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: auto, >512 MB)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB buffer three times (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
@@ -175,7 +218,9 @@ def main():
     roof["traffic"] = tr["bytes"] if tr and tr["src"] == src_hash else None
     roof["kernel"] = kname
     roof["kernel_ms"] = round(ms_launch, 5)
+    roof["kernel_ms_p10_p50_p90"] = [round(float(np.percentile(per_launch, q)), 5) for q in (10, 50, 90)]
     roof["kernel_src"] = src_hash
+    roof["measured_copy_GBs"] = round(copy_ceiling(torch, dev), 1)
 
     result = {
         "metric": "int8_linear TOPS and % of int8-MFMA / HBM roofline on one MI355X",

@@ -52,6 +52,25 @@ __device__ __forceinline__ void lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Raw buffer loads: the hardware checks every access against the size in the
+// resource and returns zeros past it without touching memory, so an
+// out-of-range lane needs no branch and no pointer select, only an offset at or
+// past the end (kBufOff).  Offsets are in bytes; the resource holds the base
+// and size (dword 3 = 0x00020000 is the gfx9 data format for raw byte access).
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+constexpr uint32_t kBufOff = 0x80000000u;
+constexpr int kBufNT = 2;   // cache policy: nontemporal (streamed once)
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+template <int AUX = 0>
+__device__ __forceinline__ v4i buf_load16(buf_rsrc r, uint32_t off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
+}
+__device__ __forceinline__ uint16_t buf_load_u16(buf_rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
   return v;

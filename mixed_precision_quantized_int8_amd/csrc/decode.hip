@@ -1,33 +1,35 @@
-// Small-M ("decode") LLM.int8() linear layer: the whole layer in one launch.
+// Small-M ("decode") LLM.int8() linear layer.
 //
 // Same method as the prefill path ([blog, "A gentle summary of LLM.int8()"],
 // [blog, "A closer look at the MatMul"]), shaped for M <= 16 rows, where the
-// time is the single read of the int8 weight from HBM.
+// time is the single read of the int8 weight from HBM and a second launch
+// costs more than the whole activation stage.
 //
-// Each workgroup (8 waves) owns 64 output features (4 blocks of 16) and
-// streams their int8 weight rows once; the 8 waves split K.
-//   1. A wave's weight loads (8 k-steps x 4 blocks = 128 VGPRs at a time)
-//      are issued right after the few activation loads, so the HBM latency
-//      overlaps the whole activation stage; the K chunk a wave streams is
-//      rotated by the workgroup index to spread concurrent requests.
-//   2. Fused variant (M*K small): every workgroup redundantly runs the
-//      activation stage on the tiny X (L2-resident): each thread owns whole
-//      8-column chunks over all M rows, so it decides their outlier flags
-//      locally; row absmax over the regular columns is reduced across the
-//      workgroup; codes go to LDS [M][K].  Workgroup 0 also writes the
-//      intermediates (Xq, sx, outlier list, X_O) to the workspace.
-//      Unfused variant: reads those intermediates, written by the activation
-//      kernels, from the workspace.
-//   3. The outlier values of X are gathered into LDS during the prologue (up
-//      to 64), and each epilogue lane loads its outlier weight values (up to 8)
-//      into registers as soon as the outlier list is known, so the epilogue
-//      issues no dependent global loads in the common case; more outliers
-//      take slower loops over global memory.
-//   4. v_mfma_i32_16x16x64_i8 with the activations as the 16-row operand
-//      (rows >= M are zero) and 16 weight rows as the other; int32 partials of
-//      the 8 waves are summed through LDS (exact, order-free).
-//   5. Epilogue: dequantize with sx * sw / 127^2, add the fp32 outlier
-//      products, store fp16.
+// Fused kernel (K <= 4096): the whole layer in one launch.  Each workgroup
+// (8 waves) owns 64 output features (4 blocks of 16); the 8 waves split K into
+// 8 chunks, and a wave owns its chunk of X over ALL rows, held in registers in
+// the operand layout of v_mfma_i32_16x16x64_i8 (lane = row lr, 16-column
+// group g).  Consequences:
+//   * the outlier test of a column needs only the wave's own registers: an OR
+//     of hit masks over the 16 lanes of a column group;
+//   * the row absmax over the regular columns is the only workgroup-wide
+//     dependency: one LDS exchange and one barrier;
+//   * the codes are computed in registers, already in MFMA operand layout;
+//   * each wave adds the fp16 product of its own outlier columns (weight rows
+//     loaded as soon as the columns are known, long before they are needed);
+//   * a second barrier sums the 8 waves' int32 partials (exact) and fp32
+//     outlier partials, then the epilogue dequantizes and stores fp16.
+// The weight is streamed with 16-byte nontemporal loads; the first PRE
+// k-steps of a wave are issued before the activation stage and the rest right
+// after its barrier.  The K chunk a wave streams is rotated by the workgroup
+// index (measured ~15% more HBM bandwidth than all starting at chunk 0).
+// Workgroup 0 also writes the intermediates (Xq, sx, outlier list, X_O) to the
+// workspace.
+//
+// Stream kernel (larger K): reads the intermediates written by the activation
+// kernels and does the product and epilogue the same way.
+#include <cmath>
+
 #include "common.h"
 #include "launch.h"
 
@@ -37,13 +39,13 @@ constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kDecP = 4;                      // 16-feature blocks per workgroup
 constexpr int kDecCols = 16 * kDecP;
-constexpr int kDecMaxK = 8192;                // fused variant
-constexpr int kDecLdsXq = 65536;              // fused variant: M * Kpad <= this
-constexpr int kDecRedBytes = kDecWaves * kDecP * 64 * 16;
-constexpr int kDecMaxOutLds = 64;             // outlier values of X gathered into LDS
-constexpr int kDecOutReg = 8;                 // outlier weight values held per lane
+constexpr int kDecMaxKS = 8;                  // fused kernel: k-steps per wave
+constexpr int kDecOutPre = 2;                 // outlier columns per wave preloaded
+constexpr int kDecMaxOutLds = 64;             // stream kernel: outlier values in LDS
+constexpr int kDecOutReg = 8;                 // stream kernel: outlier weights per lane
 
-// 16 zero bytes for lanes whose load is out of range (loads stay unconditional).
+// Zero bytes for lanes whose load is out of range (loads stay unconditional,
+// so the number of loads in flight is fixed and waits stay exact).
 __device__ __attribute__((aligned(64))) int8_t g_dec_zero[64];
 
 struct DecodeArgs {
@@ -52,8 +54,8 @@ struct DecodeArgs {
   const int8_t* Wq;
   const float* sw;
   const uint16_t* W_rows;
-  float threshold;
-  int enabled;
+  uint32_t thr_add;    // (0x8000 - T) in both 16-bit halves, T = smallest outlier
+                       // magnitude pattern; 0 when the decomposition is off
   uint16_t* Y;
   int32_t* n_out;
   int32_t* idx;
@@ -62,66 +64,302 @@ struct DecodeArgs {
   uint16_t* X_O;
 };
 
-bool decode_fits(int M, int K) {
-  const int kpad = (K + 63) / 64 * 64;
-  if (M < 1 || M > 16 || K > kDecMaxK || M * kpad > kDecLdsXq) return false;
-  return M <= 8 || K <= kDecThreads * 8;   // rows x chunks held per thread <= 16
+bool decode_fits(int M, int K) { return M >= 1 && M <= 16 && K <= kDecWaves * kDecMaxKS * 64; }
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t half_at(const v4i (&v)[2], int e) {
+  return ((uint32_t)v[e >> 3][(e & 7) >> 1] >> ((e & 1) * 16)) & 0xffffu;
 }
 
-template <int BS>
-__device__ __forceinline__ int dec_block_excl_scan(int v, int* s_tmp, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = wave_incl_scan(v);
-  if (lane == 63) s_tmp[wave] = incl;
-  lds_sync();
-  if (wave == 0) {
-    int w = lane < BS / 64 ? s_tmp[lane] : 0;
-    int wi = wave_incl_scan(w);
-    if (lane < BS / 64) s_tmp[lane] = wi - w;
-    if (lane == 63) s_tmp[BS / 64] = wi;
-  }
-  lds_sync();
-  int r = s_tmp[wave] + incl - v;
-  *total = s_tmp[BS / 64];
-  lds_sync();
-  return r;
-}
-
-// MR: rows of X held per thread in the fused prologue (8 or 16, >= M);
-// QC: 8-column chunks per thread (K <= kDecThreads * 8 * QC);
-// kDecU: k-steps of 64 bytes per weight load batch (register budget).
-template <bool FUSED, int MR, int QC, int kDecU, int kDecPre = 2>
+// KS: k-steps of 64 per wave held in registers (>= ceil(K / 64 / 8));
+// PRE: weight k-steps issued before the activation stage.
+template <int KS, int PRE>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
-  constexpr int kUnion = (FUSED ? kDecLdsXq : 0) > kDecRedBytes ? kDecLdsXq : kDecRedBytes;
-  __shared__ __attribute__((aligned(16))) int8_t sU[kUnion];   // Xq [M][Kpad], later partials
-  __shared__ int sIdx[FUSED ? kDecMaxK : 1];
-  __shared__ uint32_t sFlags[FUSED ? kDecMaxK / 32 : 1];
-  __shared__ int sRank[FUSED ? kDecMaxK / 32 : 1];
-  __shared__ float sXO[16][kDecMaxOutLds];        // X at the outlier columns
-  __shared__ int sTmp[kDecWaves + 1];
-  __shared__ uint32_t sRowMax[kDecWaves][16];
+  __shared__ v4i sRed[kDecWaves][kDecP][64];        // int32 partials, D layout
+  __shared__ float sYo[kDecWaves][16][kDecCols];    // fp32 outlier partials [m][col]
+  __shared__ uint32_t sRowMax[kDecWaves][16];       // per chunk, per row
+  __shared__ int sCnt[kDecWaves];                   // outliers per K chunk
+  __shared__ int sHasOut[kDecWaves];
   __shared__ float sSx[16];
-  __shared__ int sNout;
+  __shared__ v4i sQ[16][KS * kDecWaves * 4 + 4];    // codes [m][16-byte chunk] + spare
+
+  const int M = d.M, K = d.K, N = d.N;
+  const int lane = threadIdx.x & 63;
+  // the wave index is uniform; saying so keeps everything derived from it
+  // (chunk bounds, outlier columns, resources) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * kDecCols;
+  const int nsteps = (K + 63) >> 6;
+  const int kc = (wave + blockIdx.x) % kDecWaves;
+  const int s0 = kc * nsteps / kDecWaves, s1 = (kc + 1) * nsteps / kDecWaves;   // s1 - s0 <= KS
+
+  // ---- loads: X chunk of this wave, the output feature's scale, the weight ----
+  // X rows >= M and columns outside this wave's chunk read as zero (buffer
+  // range check); weight rows >= N read as zero, and weight bytes outside the
+  // chunk meet zero codes.
+  const buf_rsrc rx = make_rsrc(d.X, (uint32_t)(M * K * 2));
+  v4i xr[KS][2];   // X[lr][(s0+s)*64 + 16g + 8h .. +8] as fp16
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int k = (s0 + s) * 64 + 16 * g;
+    const uint32_t off = s0 + s < s1 && k < K ? (uint32_t)(lr * K + k) * 2u : kBufOff;
+    xr[s][0] = buf_load16(rx, off);
+    xr[s][1] = buf_load16(rx, off + 16u);
+  }
+  const int ne = n0 + (wave & (kDecP - 1)) * 16 + lr;   // epilogue feature of this lane
+  const float swv = d.sw[ne < N ? ne : N - 1];
+
+  const int nrows = N - n0 < kDecCols ? N - n0 : kDecCols;
+  const buf_rsrc rw = make_rsrc(d.Wq + (size_t)n0 * K, (uint32_t)(nrows * K));
+  const uint32_t wb = (uint32_t)(lr * K + s0 * 64 + 16 * g);
+  v4i fb[KS][kDecP];
+  auto load_b = [&](int u0, int u1) {
+#pragma unroll
+    for (int u = u0; u < u1; ++u)
+#pragma unroll
+      for (int c = 0; c < kDecP; ++c)
+        fb[u][c] = buf_load16<kBufNT>(rw, wb + (uint32_t)(c * 16 * K + u * 64));
+  };
+  constexpr int kPre = PRE < KS ? PRE : KS;
+  load_b(0, kPre);
+
+  __builtin_amdgcn_sched_barrier(0);   // the stream goes out before the stage below
+
+  // ---- outlier columns of this chunk --------------------------------------------
+  // Two fp16 values per 32-bit word: with m = magnitude bits (<= 0x7fff) and
+  // c = 0x8000 - T in both halves, m + c sets bit 15 of a half exactly when
+  // m >= T, with no carry between halves.
+  // hm[s] bit e: some row has |X| >= t in column (s0+s)*64 + 16g + e
+  uint32_t hm[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t t2 = ((uint32_t)xr[s][i >> 2][i & 3] & 0x7fff7fffu) + d.thr_add;
+      m |= ((t2 >> 15) & 1u) << (2 * i) | ((t2 >> 31) & 1u) << (2 * i + 1);
+    }
+    hm[s] = m;
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) hm[s] |= __shfl_xor(hm[s], off, 64);
+  auto step_mask = [&](int s) -> uint64_t { return __ballot((hm[s] >> lr) & 1u); };
+  int wcount = 0;
+  int ko[kDecOutPre];
+#pragma unroll
+  for (int j = 0; j < kDecOutPre; ++j) ko[j] = -1;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    uint64_t w = step_mask(s);
+    wcount += __popcll(w);
+#pragma unroll
+    for (int j = 0; j < kDecOutPre; ++j) {
+      if (w != 0 && ko[j] < 0) {
+        ko[j] = (s0 + s) * 64 + __builtin_ctzll(w);
+        w &= w - 1;
+      }
+    }
+  }
+  const int found = wcount < kDecOutPre ? wcount : kDecOutPre;
+  // X values (lane = row) and weight-row values (lane = feature) of the first
+  // kDecOutPre outlier columns, loaded now and used after the product
+  uint16_t xo[kDecOutPre], wo[kDecOutPre];
+#pragma unroll
+  for (int j = 0; j < kDecOutPre; ++j) {
+    const bool ok = j < found;
+    xo[j] = buf_load_u16(rx, ok ? (uint32_t)(lane * K + ko[j]) * 2u : kBufOff);
+    const buf_rsrc ro = make_rsrc(ok ? d.W_rows + (size_t)ko[j] * N + n0 : d.W_rows,
+                                  ok ? (uint32_t)nrows * 2u : 0u);
+    wo[j] = buf_load_u16(ro, (uint32_t)lane * 2u);
+  }
+
+  // row absmax over the regular columns of this chunk (packed u16 maxima);
+  // the empty asm makes the compiler re-derive the magnitudes from the loaded
+  // words instead of keeping 128 unpacked values alive from the test above
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(xr[s][0]), "+v"(xr[s][1]));
+  u16x2 rmv = {0, 0};
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t b0 = (hm[s] >> (2 * i)) & 1u, b1 = (hm[s] >> (2 * i + 1)) & 1u;
+      const uint32_t keep = ((b0 - 1u) & 0xffffu) | ((b1 - 1u) << 16);
+      const uint32_t v = (uint32_t)xr[s][i >> 2][i & 3] & 0x7fff7fffu & keep;
+      rmv = __builtin_elementwise_max(rmv, __builtin_bit_cast(u16x2, v));
+    }
+  uint32_t rm = rmv[0] > rmv[1] ? rmv[0] : rmv[1];
+  {
+    uint32_t o = __shfl_xor(rm, 16, 64);
+    rm = o > rm ? o : rm;
+    o = __shfl_xor(rm, 32, 64);
+    rm = o > rm ? o : rm;
+  }
+  if (g == 0) sRowMax[kc][lr] = rm;
+  if (lane == 0) sCnt[kc] = wcount;
+  lds_sync();
+
+  load_b(kPre, KS);
+
+  // ---- codes (in MFMA operand layout) and the int8 product, one k-step at a time ----
+  uint32_t mx = 0;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) mx = sRowMax[w][lr] > mx ? sRowMax[w][lr] : mx;
+  const float inv = quant_scale(h2f((uint16_t)mx));
+  if (wave == 0 && lane < 16) sSx[lane] = h2f((uint16_t)mx);   // rows >= M: 0
+  v4i acc[kDecP];
+#pragma unroll
+  for (int c = 0; c < kDecP; ++c) acc[c] = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(xr[s][0]), "+v"(xr[s][1]));
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    int q[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      q[e] = quant_code(h2f((uint16_t)half_at(xr[s], e)), inv) & (int)(((hm[s] >> e) & 1u) - 1u);
+    const v4i a = {(int)pack4_i8(q[0], q[1], q[2], q[3]), (int)pack4_i8(q[4], q[5], q[6], q[7]),
+                   (int)pack4_i8(q[8], q[9], q[10], q[11]),
+                   (int)pack4_i8(q[12], q[13], q[14], q[15])};
+    // codes also go to LDS (all workgroups: no branch near the loads); workgroup
+    // 0 copies them to the workspace at the end
+    // (steps past this wave's chunk land in a spare slot, not the next chunk's)
+    sQ[lr][s0 + s < s1 ? (s0 + s) * 4 + g : KS * kDecWaves * 4 + g] = a;
+#pragma unroll
+    for (int c = 0; c < kDecP; ++c)
+      acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, fb[s][c], acc[c], 0, 0, 0);
+  }
+
+  // ---- outlier product of this chunk's columns (lane = feature n0 + lane) ----------
+  if (wcount > 0) {
+    float yo[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) yo[m] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kDecOutPre; ++j) {
+      if (j < found) {
+        const float wv = h2f(wo[j]);
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+          if (m < M) yo[m] += h2f((uint16_t)__builtin_amdgcn_readlane((int)xo[j], m)) * wv;
+      }
+    }
+    if (wcount > kDecOutPre) {   // the rest, straight from memory
+      int j = 0;
+      for (int s = 0; s < KS; ++s) {
+        uint64_t w = step_mask(s);
+        while (w) {
+          const int k = (s0 + s) * 64 + __builtin_ctzll(w);
+          w &= w - 1;
+          if (j++ < kDecOutPre) continue;
+          const float wv = n0 + lane < N ? h2f(d.W_rows[(size_t)k * N + n0 + lane]) : 0.0f;
+          const int xv = lane < M ? (int)d.X[(size_t)lane * K + k] : 0;
+#pragma unroll
+          for (int m = 0; m < 16; ++m)
+            if (m < M) yo[m] += h2f((uint16_t)__builtin_amdgcn_readlane(xv, m)) * wv;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) sYo[wave][m][lane] = yo[m];
+  }
+  if (lane == 0) sHasOut[wave] = wcount > 0;
+
+  // ---- sum the partials of the 8 waves ------------------------------------------------
+#pragma unroll
+  for (int c = 0; c < kDecP; ++c) sRed[wave][c][lane] = acc[c];
+  lds_sync();
+
+  // ---- workspace intermediates (workgroup 0) ----------------------------------------
+  if (blockIdx.x == 0) {
+    // codes: Xq[m][k] for the k-steps of this wave's chunk
+    for (int i = lane; i < M * (s1 - s0) * 4; i += 64) {
+      const int m = i / ((s1 - s0) * 4), q = (s0 * 4) + i % ((s1 - s0) * 4);
+      if (q * 16 < K) *reinterpret_cast<v4i*>(d.Xq + (size_t)m * K + q * 16) = sQ[m][q];
+    }
+    int rank = 0;
+    for (int w = 0; w < kc; ++w) rank += sCnt[w];
+#pragma unroll
+    for (int j = 0; j < kDecOutPre; ++j) {
+      if (j < found) {
+        if (lane == 0) d.idx[rank + j] = ko[j];
+        if (lane < M) d.X_O[(size_t)lane * K + rank + j] = xo[j];
+      }
+    }
+    if (wcount > kDecOutPre) {
+      int j = 0;
+      for (int s = 0; s < KS; ++s) {
+        uint64_t w = step_mask(s);
+        while (w) {
+          const int k = (s0 + s) * 64 + __builtin_ctzll(w);
+          w &= w - 1;
+          if (j >= kDecOutPre) {
+            if (lane == 0) d.idx[rank + j] = k;
+            if (lane < M) d.X_O[(size_t)lane * K + rank + j] = d.X[(size_t)lane * K + k];
+          }
+          ++j;
+        }
+      }
+    }
+    if (wave == 0) {
+      if (lane < M) d.sx[lane] = sSx[lane];
+      if (lane == 0) {
+        int tot = 0;
+        for (int w = 0; w < kDecWaves; ++w) tot += sCnt[w];
+        *d.n_out = tot;
+      }
+    }
+  }
+
+  if (wave >= kDecP) return;
+  const int c = wave;
+  v4i tot = {0, 0, 0, 0};
+  float yo4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int mb = g * 4;   // D rows of this lane: mb .. mb + 3
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) {
+    const v4i p = sRed[w][c][lane];
+    tot[0] += p[0]; tot[1] += p[1]; tot[2] += p[2]; tot[3] += p[3];
+    if (sHasOut[w]) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yo4[r] += sYo[w][mb + r][c * 16 + lr];
+    }
+  }
+
+  // ---- epilogue ----------------------------------------------------------------------
+  const int n = ne;
+  if (n >= N || mb >= M) return;
+  const float swn = swv * (1.0f / 16129.0f);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = mb + r;
+    if (m < M) d.Y[(size_t)m * N + n] = f2h((float)tot[r] * (sSx[m] * swn) + yo4[r]);
+  }
+}
+
+// Stream kernel for small M with larger K: the activation kernels have written
+// the codes, the row scales and the outlier list to the workspace.
+__global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d) {
+  constexpr int kU = 8;
+  __shared__ v4i sRed[kDecWaves][kDecP][64];
+  __shared__ float sXO[16][kDecMaxOutLds];
 
   const int M = d.M, K = d.K, N = d.N;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int lr = lane & 15, kl = (lane >> 4) * 16;
   const int n0 = blockIdx.x * kDecCols;
-  const int kpad = (K + 63) & ~63;
-  const int nsteps = kpad >> 6;
-  // K chunk of this wave, rotated by the workgroup index so that concurrently
-  // running workgroups start their weight streams at different offsets
-  // (measured ~15% more HBM bandwidth than all starting at chunk 0).
+  const int nsteps = (K + 63) >> 6;
   const int kc = (wave + blockIdx.x) % kDecWaves;
   const int s0 = kc * nsteps / kDecWaves, s1 = (kc + 1) * nsteps / kDecWaves;
-  const int lr = lane & 15;             // operand row inside a 16-block
-  const int kl = (lane >> 4) * 16;      // 16-byte k chunk of this lane
 
-  // Weight loads are unconditional (out-of-range lanes read the zero page):
-  // with a fixed number of loads in flight the compiler can wait for the
-  // activation loads issued before them without waiting for the whole stream.
-  auto load_b = [&](int s, v4i (&fb)[kDecU][kDecP], int u0, int u1) {
+  v4i fb[kU][kDecP];
+  auto load_b = [&](int s) {
 #pragma unroll
-    for (int u = u0; u < u1; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int k = (s + u) * 64 + kl;
 #pragma unroll
       for (int c = 0; c < kDecP; ++c) {
@@ -132,266 +370,71 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
       }
     }
   };
-
-  // Fused variant: the activation rows this thread owns are loaded before the
-  // weight stream, so the activation stage only waits for them (loads retire
-  // in order) and runs while the weight is in flight.
-  constexpr int kXR = FUSED ? MR : 1, kXC = FUSED ? QC : 1;
-  v4i xv[kXC][kXR];
-  if constexpr (FUSED) {
-    const int nq = K >> 3;
-#pragma unroll
-    for (int h = 0; h < QC; ++h) {
-      const int q = t + h * kDecThreads;
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        const bool in = q < nq && m < M;
-        const void* p = in ? (const void*)(d.X + (size_t)m * K + q * 8) : (const void*)g_dec_zero;
-        xv[h][m] = *reinterpret_cast<const v4i*>(p);
-      }
-    }
-  }
-  // Only the first kDecPre k-steps go out before the activation stage: with a
-  // full memory queue, waves stall on issue and the stage's barriers would wait
-  // for the whole stream; the rest is issued right after the stage.
-  v4i fb[kDecU][kDecP];
-  load_b(s0, fb, 0, kDecPre);
-
-  // Outlier weight values of this lane's output feature (epilogue lanes of
-  // waves 0..kDecP-1), loaded into registers as soon as the outlier list is
-  // known and used only in the epilogue: loads retire in order, so nothing
-  // waits for them before the weight stream has arrived anyway.
-  // Unconditional raw fp16 loads (out-of-range lanes read the zero page),
-  // converted only in the epilogue, so nothing waits for them here.
-  uint16_t wo[kDecOutReg];
-  auto load_wo = [&](int nout, const int* idx_src) {
-    const int n = n0 + (wave & (kDecP - 1)) * 16 + lr;
-#pragma unroll
-    for (int j = 0; j < kDecOutReg; ++j) {
-      const bool in = wave < kDecP && j < nout && n < N;
-      const int k = in ? idx_src[j] : 0;
-      const uint16_t* p = in ? d.W_rows + (size_t)k * N + n
-                             : reinterpret_cast<const uint16_t*>(g_dec_zero);
-      wo[j] = *p;
-    }
-  };
-
-  int nout;
-  // ---- activation stage ------------------------------------------------------
-  if constexpr (FUSED) {
-    const int nq = K >> 3;              // 8-column chunks; nq <= kDecThreads * QC
-    uint32_t um[MR];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) um[m] = 0;
-#pragma unroll
-    for (int h = 0; h < QC; ++h) {
-      const int q = t + h * kDecThreads;
-      uint32_t cm[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) cm[e] = 0;
-#pragma unroll
-      for (int m = 0; m < MR; ++m)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t b = ((uint32_t)xv[h][m][e >> 1] >> ((e & 1) * 16)) & 0x7fffu;
-          cm[e] = b > cm[e] ? b : cm[e];
-        }
-      uint32_t ob = 0;
-      if (d.enabled) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (h2f((uint16_t)cm[e]) >= d.threshold) ob |= 1u << e;
-      }
-      // bytes past the last chunk (K % 32 == 16) complete the last word with zeros
-      if (q < 4 * ((K + 31) >> 5)) reinterpret_cast<uint8_t*>(sFlags)[q] = q < nq ? (uint8_t)ob : 0;
-#pragma unroll
-      for (int m = 0; m < MR; ++m)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t b = ((uint32_t)xv[h][m][e >> 1] >> ((e & 1) * 16)) & 0x7fffu;
-          if (!((ob >> e) & 1u)) um[m] = b > um[m] ? b : um[m];
-        }
-    }
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const uint32_t w = wave_max_u32(um[m]);
-      if (lane == 0) sRowMax[wave][m] = w;
-    }
-    lds_sync();
-    if (t < MR) {
-      uint32_t mm = 0;
-#pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) mm = sRowMax[w][t] > mm ? sRowMax[w][t] : mm;
-      sSx[t] = h2f((uint16_t)mm);
-    }
-    // outlier list: prefix popcount over the flag words
-    const int nw = (K + 31) >> 5;
-    const uint32_t fw = t < nw ? sFlags[t] : 0u;   // nw <= 256 < kDecThreads
-    int total;
-    const int rank = dec_block_excl_scan<kDecThreads>(__builtin_popcount(fw), sTmp, &total);
-    if (t < nw) sRank[t] = rank;
-    {
-      uint32_t f = fw;
-      int r = rank;
-      while (f) {
-        sIdx[r++] = t * 32 + __builtin_ctz(f);
-        f &= f - 1u;
-      }
-    }
-    if (t == 0) sNout = total;
-    lds_sync();   // sSx, sIdx, sRank, sNout visible
-    nout = sNout;
-    load_wo(nout, sIdx);
-    // codes -> LDS; outlier values -> LDS (and, in workgroup 0, all of it to
-    // the workspace)
-#pragma unroll
-    for (int h = 0; h < QC; ++h) {
-      const int q = t + h * kDecThreads;
-      if (q < nq) {
-        const uint32_t ob = reinterpret_cast<const uint8_t*>(sFlags)[q];
-        const int word = q >> 2, sh = (q & 3) * 8;
-        const int rb0 = sRank[word] + __builtin_popcount(sFlags[word] & ((1u << sh) - 1u));
-#pragma unroll
-        for (int m = 0; m < MR; ++m) {
-          if (m < M) {
-            const float inv = quant_scale(sSx[m]);
-            int code[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint16_t hb =
-                  (uint16_t)(((uint32_t)xv[h][m][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-              code[e] = ((ob >> e) & 1u) ? 0 : quant_code(h2f(hb), inv);
-            }
-            v2i packed = {(int)pack4_i8(code[0], code[1], code[2], code[3]),
-                          (int)pack4_i8(code[4], code[5], code[6], code[7])};
-            *reinterpret_cast<v2i*>(&sU[m * kpad + q * 8]) = packed;
-            if (blockIdx.x == 0) *reinterpret_cast<v2i*>(d.Xq + (size_t)m * K + q * 8) = packed;
-            if (ob) {
-              int rb = rb0;   // rank of this chunk's first outlier column
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if ((ob >> e) & 1u) {
-                  const uint16_t hb =
-                      (uint16_t)(((uint32_t)xv[h][m][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-                  if (rb < kDecMaxOutLds) sXO[m][rb] = h2f(hb);
-                  if (blockIdx.x == 0) d.X_O[(size_t)m * K + rb] = hb;
-                  ++rb;
-                }
-            }
-          }
-        }
-      }
-    }
-    // zero the K padding of each row so partial k-steps read zeros
-    if (kpad > K) {
-      for (int i = t; i < M * (kpad - K); i += kDecThreads) {
-        const int m = i / (kpad - K), k = K + i % (kpad - K);
-        sU[m * kpad + k] = 0;
-      }
-    }
-    if (blockIdx.x == 0) {
-      if (t < M) d.sx[t] = sSx[t];
-      for (int j = t; j < nout; j += kDecThreads) d.idx[j] = sIdx[j];
-      if (t == 0) *d.n_out = nout;
-    }
-    lds_sync();
-  } else {
-    nout = 0;   // read after the main loop (see below)
-  }
-
-  load_b(s0, fb, kDecPre, kDecU);
-
-  // ---- int8 product --------------------------------------------------------------
+  load_b(s0);
   v4i acc[kDecP];
 #pragma unroll
   for (int c = 0; c < kDecP; ++c) acc[c] = v4i{0, 0, 0, 0};
-  for (int s = s0; s < s1; s += kDecU) {
-    v4i fa[kDecU];
+  for (int s = s0; s < s1; s += kU) {
+    v4i fa[kU];
 #pragma unroll
-    for (int u = 0; u < kDecU; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int k = (s + u) * 64 + kl;
-      if constexpr (FUSED) {
-        fa[u] = (s + u < s1 && lr < M) ? *reinterpret_cast<const v4i*>(&sU[lr * kpad + k])
-                                        : v4i{0, 0, 0, 0};
-      } else {
-        fa[u] = (s + u < s1 && lr < M && k < K)
-                    ? *reinterpret_cast<const v4i*>(d.Xq + (size_t)lr * K + k)
-                    : v4i{0, 0, 0, 0};
-      }
+      const bool in = s + u < s1 && lr < M && k < K;
+      const void* p = in ? (const void*)(d.Xq + (size_t)lr * K + k) : (const void*)g_dec_zero;
+      fa[u] = *reinterpret_cast<const v4i*>(p);
     }
 #pragma unroll
-    for (int u = 0; u < kDecU; ++u)
+    for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int c = 0; c < kDecP; ++c)
         acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[u], fb[u][c], acc[c], 0, 0, 0);
-    if (s + kDecU < s1) load_b(s + kDecU, fb, 0, kDecU);
+    if (s + kU < s1) load_b(s + kU);
   }
 
-  if constexpr (!FUSED) {
-    // The activation kernels wrote the outlier list and values; read them now
-    // that the weight stream has been consumed.
-    nout = *d.n_out;
-    load_wo(nout, d.idx);
-    const int nl = min(nout, kDecMaxOutLds);
-    for (int e = t; e < nl * M; e += kDecThreads) {
-      const int m = e / nl, j = e % nl;
-      sXO[m][j] = h2f(d.X_O[(size_t)m * K + j]);
-    }
-  }
-
-  // ---- sum the partials of the 8 waves -----------------------------------------
-  lds_sync();   // everyone is done reading the LDS codes
-  v4i* red = reinterpret_cast<v4i*>(sU);
+  const int nout = *d.n_out;
+  const int n = n0 + (wave & (kDecP - 1)) * 16 + lr;
+  float wo[kDecOutReg];
 #pragma unroll
-  for (int c = 0; c < kDecP; ++c) red[(wave * kDecP + c) * 64 + lane] = acc[c];
+  for (int j = 0; j < kDecOutReg; ++j)
+    wo[j] = (wave < kDecP && j < nout && n < N) ? h2f(d.W_rows[(size_t)d.idx[j] * N + n]) : 0.0f;
+  const int nl = min(nout, kDecMaxOutLds);
+  for (int e = t; e < nl * M; e += kDecThreads) {
+    const int m = e / nl, j = e % nl;
+    sXO[m][j] = h2f(d.X_O[(size_t)m * K + j]);
+  }
+#pragma unroll
+  for (int c = 0; c < kDecP; ++c) sRed[wave][c][lane] = acc[c];
   lds_sync();
   if (wave >= kDecP) return;
   const int c = wave;
   v4i tot = {0, 0, 0, 0};
 #pragma unroll
   for (int w = 0; w < kDecWaves; ++w) {
-    const v4i p = red[(w * kDecP + c) * 64 + lane];
+    const v4i p = sRed[w][c][lane];
     tot[0] += p[0]; tot[1] += p[1]; tot[2] += p[2]; tot[3] += p[3];
   }
-
-  // ---- epilogue --------------------------------------------------------------------
-  const int n = n0 + c * 16 + lr;
-  const int mb = (lane >> 4) * 4;       // D rows of this lane: mb .. mb + 3
+  const int mb = (lane >> 4) * 4;
   if (n >= N || mb >= M) return;
   const float swn = d.sw[n] * (1.0f / 16129.0f);
   float y[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = mb + r;
-    const float sxm = (m < M) ? (FUSED ? sSx[m] : d.sx[m]) : 0.0f;
-    y[r] = (float)tot[r] * (sxm * swn);
+    y[r] = m < M ? (float)tot[r] * (d.sx[m] * swn) : 0.0f;
   }
 #pragma unroll
-  for (int j = 0; j < kDecOutReg; ++j) {
+  for (int j = 0; j < kDecOutReg; ++j)
     if (j < nout) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (mb + r < M) y[r] += sXO[mb + r][j] * h2f(wo[j]);
+        if (mb + r < M) y[r] += sXO[mb + r][j] * wo[j];
     }
-  }
-  const int nl = min(nout, kDecMaxOutLds);
-  for (int j = kDecOutReg; j < nl; ++j) {   // weight values beyond the registers
-    const int k = FUSED ? sIdx[j] : d.idx[j];
-    const float w = h2f(d.W_rows[(size_t)k * N + n]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (mb + r < M) y[r] += sXO[mb + r][j] * w;
-  }
-  for (int j = nl; j < nout; ++j) {   // beyond the LDS gather: straight from memory
-    const int k = FUSED ? sIdx[j] : d.idx[j];
-    const float w = h2f(d.W_rows[(size_t)k * N + n]);
+  for (int j = kDecOutReg; j < nout; ++j) {
+    const float w = h2f(d.W_rows[(size_t)d.idx[j] * N + n]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = mb + r;
-      if (m < M) {
-        const float x = FUSED ? h2f(d.X[(size_t)m * K + k]) : h2f(d.X_O[(size_t)m * K + j]);
-        y[r] += x * w;
-      }
+      if (m < M) y[r] += (j < kDecMaxOutLds ? sXO[m][j] : h2f(d.X_O[(size_t)m * K + j])) * w;
     }
   }
 #pragma unroll
@@ -401,34 +444,44 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   }
 }
 
+namespace {
+
+float half_bits_value(uint32_t b) {   // non-negative fp16 pattern (inf counts as 2^16)
+  const int e = (int)((b >> 10) & 31), m = (int)(b & 1023);
+  return e == 0 ? std::ldexp((float)m, -24) : std::ldexp((float)(m | 1024), e - 25);
+}
+
+// Smallest fp16 magnitude pattern whose value is >= t (t > 0): comparing the
+// magnitude bits of an fp16 value with it is the same as |x| >= t.
+uint32_t threshold_bits(float t) {
+  uint32_t lo = 0, hi = 0x7c00;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) / 2;
+    if (half_bits_value(mid) >= t) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+}  // namespace
+
 hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
                          int N, const uint16_t* W_rows, float threshold, bool enabled,
                          uint16_t* Y, const Workspace& ws, hipStream_t stream) {
-  DecodeArgs d{X, M, K, N, Wq, sw, W_rows, threshold, enabled ? 1 : 0, Y,
-               ws.n_out, ws.idx, ws.sx, ws.Xq, ws.X_O};
-  const dim3 grid((N + kDecCols - 1) / kDecCols);
+  const uint32_t c16 = enabled ? 0x8000u - threshold_bits(threshold) : 0u;
+  DecodeArgs d{X, M, K, N, Wq, sw, W_rows, c16 * 0x10001u, Y, ws.n_out, ws.idx, ws.sx, ws.Xq, ws.X_O};
+  const dim3 grid((N + kDecCols - 1) / kDecCols), block(kDecThreads);
   if (decode_fits(M, K)) {
-    // decode_fits bounds M * K, so rows held per thread times chunks is <= 16
-    if (M <= 8 && K <= kDecThreads * 8)
-      hipLaunchKernelGGL((decode_kernel<true, 8, 1, 8>), grid, dim3(kDecThreads), 0, stream, d);
-    else if (M <= 8)
-      hipLaunchKernelGGL((decode_kernel<true, 8, 2, 4>), grid, dim3(kDecThreads), 0, stream, d);
-    else
-      hipLaunchKernelGGL((decode_kernel<true, 16, 1, 4>), grid, dim3(kDecThreads), 0, stream, d);
-  } else {
-    hipError_t e = launch_quantize_activation(X, M, K, threshold, enabled, ws, stream);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_kernel<false, 8, 1, 8>), grid, dim3(kDecThreads), 0, stream, d);
+    const int ks = ((K + 63) / 64 + kDecWaves - 1) / kDecWaves;   // k-steps per wave
+    if (ks <= 1) hipLaunchKernelGGL((decode_kernel<1, 2>), grid, block, 0, stream, d);
+    else if (ks <= 2) hipLaunchKernelGGL((decode_kernel<2, 2>), grid, block, 0, stream, d);
+    else if (ks <= 4) hipLaunchKernelGGL((decode_kernel<4, 2>), grid, block, 0, stream, d);
+    else hipLaunchKernelGGL((decode_kernel<8, 2>), grid, block, 0, stream, d);
+    return hipGetLastError();
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_unfused(const uint16_t* X, int M, int K, const int8_t* Wq,
-                                 const float* sw, int N, const uint16_t* W_rows, uint16_t* Y,
-                                 const Workspace& ws, hipStream_t stream) {
-  DecodeArgs d{X, M, K, N, Wq, sw, W_rows, 0.0f, 0, Y, ws.n_out, ws.idx, ws.sx, ws.Xq, ws.X_O};
-  const dim3 grid((N + kDecCols - 1) / kDecCols);
-  hipLaunchKernelGGL((decode_kernel<false, 8, 1, 8>), grid, dim3(kDecThreads), 0, stream, d);
+  hipError_t e = launch_quantize_activation(X, M, K, threshold, enabled, ws, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_stream_kernel, grid, block, 0, stream, d);
   return hipGetLastError();
 }
 

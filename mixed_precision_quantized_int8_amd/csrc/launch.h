@@ -48,18 +48,14 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
-// Small-M (decode) path: one fused kernel doing the activation stage, the
-// int8 product, the outlier product and the epilogue.  Applicable when
-// decode_fits(M, K) holds.
+// Small-M (decode) path, M <= 16: when decode_fits(M, K) one fused kernel does
+// the activation stage, the int8 product, the outlier product and the
+// epilogue; otherwise the activation kernels run first and a streaming kernel
+// does the rest.
 bool decode_fits(int M, int K);
 hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
                          int N, const uint16_t* W_rows, float threshold, bool enabled,
                          uint16_t* Y, const Workspace& ws, hipStream_t stream);
-
-// Streaming part alone, reading the activation-stage results from `ws`.
-hipError_t launch_decode_unfused(const uint16_t* X, int M, int K, const int8_t* Wq,
-                                 const float* sw, int N, const uint16_t* W_rows, uint16_t* Y,
-                                 const Workspace& ws, hipStream_t stream);
 
 const char* gemm_tile_info();
 
