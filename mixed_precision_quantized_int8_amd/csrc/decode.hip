@@ -54,8 +54,8 @@ struct DecodeArgs {
   const int8_t* Wq;
   const float* sw;
   const uint16_t* W_rows;
-  uint32_t thr_add;    // (0x8000 - T) in both 16-bit halves, T = smallest outlier
-                       // magnitude pattern; 0 when the decomposition is off
+  uint32_t thr;        // smallest fp16 magnitude pattern that is an outlier
+                       // (0x10000 when the decomposition is off: never reached)
   uint16_t* Y;
   int32_t* n_out;
   int32_t* idx;
@@ -72,10 +72,41 @@ __device__ __forceinline__ uint32_t half_at(const v4i (&v)[2], int e) {
   return ((uint32_t)v[e >> 3][(e & 7) >> 1] >> ((e & 1) * 16)) & 0xffffu;
 }
 
-// KS: k-steps of 64 per wave held in registers (>= ceil(K / 64 / 8));
+// RHAZ(v) for |v| < 2^15, from w = trunc(v * 2^16): floor((|w| + 2^15) / 2^16)
+// with the sign of w, computed as (w + 2^15 + (w < 0 ? -1 : 0)) >> 16
+// (arithmetic shift); the code byte is byte 2 of that sum.
+__device__ __forceinline__ uint32_t rhaz_sum(float v65) {
+  const int w = (int)v65;   // truncates toward zero
+  return (uint32_t)(w + 0x8000 + (w >> 31));
+}
+
+// 16 codes of one lane: round-half-away(x * inv) with inv65 = inv * 2^16
+// (exact power-of-two scaling).  No clamp is needed: outlier values are
+// zeroed beforehand and every other |x| <= absmax, so |x * inv| < 127.5.
+__device__ __forceinline__ v4i codes16(const v4i (&x)[2], float inv65) {
+  v4i a;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {   // output dword i: elements 4i .. 4i+3
+    uint32_t t[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = rhaz_sum(h2f((uint16_t)half_at(x, 4 * i + e)) * inv65);
+    const uint32_t p01 = __builtin_amdgcn_perm(t[1], t[0], 0x06020602u);   // t0.b2 t1.b2 ..
+    const uint32_t p23 = __builtin_amdgcn_perm(t[3], t[2], 0x06020602u);   // .. t2.b2 t3.b2
+    a[i] = (int)__builtin_amdgcn_perm(p23, p01, 0x07060100u);
+  }
+  return a;
+}
+
+// KS: k-steps of 64 per wave (>= ceil(K / 64 / 8));
+// R: k-steps packed into one register set (M <= 16 / R): lane row lr holds X
+//    row lr % (16/R) of k-step (lr / (16/R)) of the set, so padding rows >= M
+//    carry real data instead of zeros; the codes are moved to the MFMA operand
+//    rows by lane shuffles;
 // PRE: weight k-steps issued before the activation stage.
-template <int KS, int PRE>
+template <int KS, int R, int PRE>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
+  constexpr int MR = 16 / R;         // X rows per slot
+  constexpr int NSET = KS / R;       // register sets
   __shared__ v4i sRed[kDecWaves][kDecP][64];        // int32 partials, D layout
   __shared__ float sYo[kDecWaves][16][kDecCols];    // fp32 outlier partials [m][col]
   __shared__ uint32_t sRowMax[kDecWaves][16];       // per chunk, per row
@@ -90,6 +121,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   // (chunk bounds, outlier columns, resources) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, g = lane >> 4;
+  const int rr = lr % MR, q = lr / MR;   // X row and slot of this lane
   const int n0 = blockIdx.x * kDecCols;
   const int nsteps = (K + 63) >> 6;
   const int kc = (wave + blockIdx.x) % kDecWaves;
@@ -100,13 +132,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   // range check); weight rows >= N read as zero, and weight bytes outside the
   // chunk meet zero codes.
   const buf_rsrc rx = make_rsrc(d.X, (uint32_t)(M * K * 2));
-  v4i xr[KS][2];   // X[lr][(s0+s)*64 + 16g + 8h .. +8] as fp16
+  v4i xr[NSET][2];   // X[rr][(s0 + j*R + q)*64 + 16g + 8h .. +8] as fp16
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const int k = (s0 + s) * 64 + 16 * g;
-    const uint32_t off = s0 + s < s1 && k < K ? (uint32_t)(lr * K + k) * 2u : kBufOff;
-    xr[s][0] = buf_load16(rx, off);
-    xr[s][1] = buf_load16(rx, off + 16u);
+  for (int j = 0; j < NSET; ++j) {
+    const int t = s0 + j * R + q, k = t * 64 + 16 * g;
+    const uint32_t off = t < s1 && k < K ? (uint32_t)(rr * K + k) * 2u : kBufOff;
+    xr[j][0] = buf_load16(rx, off);
+    xr[j][1] = buf_load16(rx, off + 16u);
   }
   const int ne = n0 + (wave & (kDecP - 1)) * 16 + lr;   // epilogue feature of this lane
   const float swv = d.sw[ne < N ? ne : N - 1];
@@ -124,43 +156,68 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   };
   constexpr int kPre = PRE < KS ? PRE : KS;
   load_b(0, kPre);
-
   __builtin_amdgcn_sched_barrier(0);   // the stream goes out before the stage below
 
-  // ---- outlier columns of this chunk --------------------------------------------
-  // Two fp16 values per 32-bit word: with m = magnitude bits (<= 0x7fff) and
-  // c = 0x8000 - T in both halves, m + c sets bit 15 of a half exactly when
-  // m >= T, with no carry between halves.
-  // hm[s] bit e: some row has |X| >= t in column (s0+s)*64 + 16g + e
-  uint32_t hm[KS];
+  // ---- outlier columns and row absmax of this chunk ------------------------------
+  // Per register set: the packed u16 maximum of the magnitudes decides whether
+  // any value reaches the threshold; only then (rare) are the per-column hit
+  // masks built, OR-ed over the rows of the slot, and the outlier values
+  // zeroed in registers (so the row max and the codes need no masking).
+  const uint32_t T = d.thr;
+  u16x2 rmv = {0, 0};
+  uint32_t hm[NSET];         // this lane's 16 columns: outlier bits (0 if the set has none)
+  uint32_t hitsets = 0;      // uniform: sets with an outlier column
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    uint32_t m = 0;
+  for (int j = 0; j < NSET; ++j) {
+    u16x2 smax = {0, 0};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t t2 = ((uint32_t)xr[s][i >> 2][i & 3] & 0x7fff7fffu) + d.thr_add;
-      m |= ((t2 >> 15) & 1u) << (2 * i) | ((t2 >> 31) & 1u) << (2 * i + 1);
+    for (int i = 0; i < 8; ++i)
+      smax = __builtin_elementwise_max(
+          smax, __builtin_bit_cast(u16x2, (uint32_t)xr[j][i >> 2][i & 3] & 0x7fff7fffu));
+    const uint32_t lmax = smax[0] > smax[1] ? smax[0] : smax[1];
+    hm[j] = 0;
+    if (__ballot(lmax >= T) != 0) {
+      uint32_t h = 0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) h |= (habs_bits(half_at(xr[j], e)) >= T ? 1u : 0u) << e;
+#pragma unroll
+      for (int off = 1; off < MR; off <<= 1) h |= __shfl_xor(h, off, 64);
+      hm[j] = h;
+      smax = u16x2{0, 0};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b0 = (h >> (2 * i)) & 1u, b1 = (h >> (2 * i + 1)) & 1u;
+        const uint32_t keep = ((b0 - 1u) & 0xffffu) | ((b1 - 1u) << 16);
+        xr[j][i >> 2][i & 3] &= (int)keep;
+        smax = __builtin_elementwise_max(
+            smax, __builtin_bit_cast(u16x2, (uint32_t)xr[j][i >> 2][i & 3] & 0x7fff7fffu));
+      }
+      hitsets |= 1u << j;
     }
-    hm[s] = m;
+    rmv = __builtin_elementwise_max(rmv, smax);
   }
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-    for (int s = 0; s < KS; ++s) hm[s] |= __shfl_xor(hm[s], off, 64);
-  auto step_mask = [&](int s) -> uint64_t { return __ballot((hm[s] >> lr) & 1u); };
+  // outlier columns of chunk step t as a wave-wide mask: bit l <-> column
+  // (s0+t)*64 + l, so ascending column order is (t, bit)
+  auto step_mask = [&](int t) -> uint64_t {
+    const int j = t / R, qq = t % R;
+    if (!((hitsets >> j) & 1u)) return 0;
+    const uint32_t h = __shfl(hm[j], (lane & ~15) | (qq * MR), 64);
+    return __ballot((h >> lr) & 1u);
+  };
   int wcount = 0;
   int ko[kDecOutPre];
 #pragma unroll
   for (int j = 0; j < kDecOutPre; ++j) ko[j] = -1;
+  if (hitsets) {
+    for (int t = 0; t < KS; ++t) {
+      uint64_t w = step_mask(t);
+      wcount += __popcll(w);
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    uint64_t w = step_mask(s);
-    wcount += __popcll(w);
-#pragma unroll
-    for (int j = 0; j < kDecOutPre; ++j) {
-      if (w != 0 && ko[j] < 0) {
-        ko[j] = (s0 + s) * 64 + __builtin_ctzll(w);
-        w &= w - 1;
+      for (int j = 0; j < kDecOutPre; ++j) {
+        if (w != 0 && ko[j] < 0) {
+          ko[j] = (s0 + t) * 64 + __builtin_ctzll(w);
+          w &= w - 1;
+        }
       }
     }
   }
@@ -177,61 +234,53 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     wo[j] = buf_load_u16(ro, (uint32_t)lane * 2u);
   }
 
-  // row absmax over the regular columns of this chunk (packed u16 maxima);
-  // the empty asm makes the compiler re-derive the magnitudes from the loaded
-  // words instead of keeping 128 unpacked values alive from the test above
-#pragma unroll
-  for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(xr[s][0]), "+v"(xr[s][1]));
-  u16x2 rmv = {0, 0};
-#pragma unroll
-  for (int s = 0; s < KS; ++s)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t b0 = (hm[s] >> (2 * i)) & 1u, b1 = (hm[s] >> (2 * i + 1)) & 1u;
-      const uint32_t keep = ((b0 - 1u) & 0xffffu) | ((b1 - 1u) << 16);
-      const uint32_t v = (uint32_t)xr[s][i >> 2][i & 3] & 0x7fff7fffu & keep;
-      rmv = __builtin_elementwise_max(rmv, __builtin_bit_cast(u16x2, v));
-    }
   uint32_t rm = rmv[0] > rmv[1] ? rmv[0] : rmv[1];
-  {
-    uint32_t o = __shfl_xor(rm, 16, 64);
-    rm = o > rm ? o : rm;
-    o = __shfl_xor(rm, 32, 64);
+#pragma unroll
+  for (int off = MR; off < 64; off <<= 1) {   // over the slots, then the column groups
+    const uint32_t o = __shfl_xor(rm, off, 64);
     rm = o > rm ? o : rm;
   }
-  if (g == 0) sRowMax[kc][lr] = rm;
+  if (lane < MR) sRowMax[kc][lane] = rm;
   if (lane == 0) sCnt[kc] = wcount;
   lds_sync();
 
   load_b(kPre, KS);
 
-  // ---- codes (in MFMA operand layout) and the int8 product, one k-step at a time ----
+  // ---- codes and the int8 product, one register set at a time ---------------------
   uint32_t mx = 0;
 #pragma unroll
-  for (int w = 0; w < kDecWaves; ++w) mx = sRowMax[w][lr] > mx ? sRowMax[w][lr] : mx;
-  const float inv = quant_scale(h2f((uint16_t)mx));
-  if (wave == 0 && lane < 16) sSx[lane] = h2f((uint16_t)mx);   // rows >= M: 0
+  for (int w = 0; w < kDecWaves; ++w) mx = sRowMax[w][rr] > mx ? sRowMax[w][rr] : mx;
+  const float inv65 = quant_scale(h2f((uint16_t)mx)) * 65536.0f;
+  if (wave == 0 && lane < 16) sSx[lane] = lane < MR ? h2f((uint16_t)mx) : 0.0f;
   v4i acc[kDecP];
 #pragma unroll
   for (int c = 0; c < kDecP; ++c) acc[c] = v4i{0, 0, 0, 0};
 #pragma unroll
-  for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(xr[s][0]), "+v"(xr[s][1]));
+  for (int j = 0; j < NSET; ++j) asm volatile("" : "+v"(xr[j][0]), "+v"(xr[j][1]));
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    int q[16];
+  for (int j = 0; j < NSET; ++j) {
+    const v4i cj = codes16(xr[j], inv65);
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      q[e] = quant_code(h2f((uint16_t)half_at(xr[s], e)), inv) & (int)(((hm[s] >> e) & 1u) - 1u);
-    const v4i a = {(int)pack4_i8(q[0], q[1], q[2], q[3]), (int)pack4_i8(q[4], q[5], q[6], q[7]),
-                   (int)pack4_i8(q[8], q[9], q[10], q[11]),
-                   (int)pack4_i8(q[12], q[13], q[14], q[15])};
-    // codes also go to LDS (all workgroups: no branch near the loads); workgroup
-    // 0 copies them to the workspace at the end
-    // (steps past this wave's chunk land in a spare slot, not the next chunk's)
-    sQ[lr][s0 + s < s1 ? (s0 + s) * 4 + g : KS * kDecWaves * 4 + g] = a;
+    for (int qq = 0; qq < R; ++qq) {
+      const int t = j * R + qq;
+      // operand row lr < MR takes the codes of row lr, slot qq (lane lr + qq*MR)
+      v4i a;
+      if (qq == 0) {
+        a = cj;
+      } else {
+        const int src = (lane & ~15) | ((lr + qq * MR) & 15);
 #pragma unroll
-    for (int c = 0; c < kDecP; ++c)
-      acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, fb[s][c], acc[c], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) a[i] = __shfl(cj[i], src, 64);
+      }
+      if (R > 1 && lr >= MR) a = v4i{0, 0, 0, 0};
+      // codes also go to LDS (all workgroups: no branch near the loads); workgroup
+      // 0 copies them to the workspace at the end (steps past this wave's chunk
+      // land in a spare slot, not the next chunk's)
+      sQ[lr][s0 + t < s1 ? (s0 + t) * 4 + g : KS * kDecWaves * 4 + g] = a;
+#pragma unroll
+      for (int c = 0; c < kDecP; ++c)
+        acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, fb[t][c], acc[c], 0, 0, 0);
+    }
   }
 
   // ---- outlier product of this chunk's columns (lane = feature n0 + lane) ----------
@@ -465,18 +514,25 @@ uint32_t threshold_bits(float t) {
 
 }  // namespace
 
+typedef void (*kfn)(DecodeArgs);
+
 hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
                          int N, const uint16_t* W_rows, float threshold, bool enabled,
                          uint16_t* Y, const Workspace& ws, hipStream_t stream) {
-  const uint32_t c16 = enabled ? 0x8000u - threshold_bits(threshold) : 0u;
-  DecodeArgs d{X, M, K, N, Wq, sw, W_rows, c16 * 0x10001u, Y, ws.n_out, ws.idx, ws.sx, ws.Xq, ws.X_O};
+  const uint32_t thr = enabled ? threshold_bits(threshold) : 0x10000u;
+  DecodeArgs d{X, M, K, N, Wq, sw, W_rows, thr, Y, ws.n_out, ws.idx, ws.sx, ws.Xq, ws.X_O};
   const dim3 grid((N + kDecCols - 1) / kDecCols), block(kDecThreads);
   if (decode_fits(M, K)) {
-    const int ks = ((K + 63) / 64 + kDecWaves - 1) / kDecWaves;   // k-steps per wave
-    if (ks <= 1) hipLaunchKernelGGL((decode_kernel<1, 2>), grid, block, 0, stream, d);
-    else if (ks <= 2) hipLaunchKernelGGL((decode_kernel<2, 2>), grid, block, 0, stream, d);
-    else if (ks <= 4) hipLaunchKernelGGL((decode_kernel<4, 2>), grid, block, 0, stream, d);
-    else hipLaunchKernelGGL((decode_kernel<8, 2>), grid, block, 0, stream, d);
+    const int steps = ((K + 63) / 64 + kDecWaves - 1) / kDecWaves;   // k-steps per wave
+    const int ks = steps <= 1 ? 1 : steps <= 2 ? 2 : steps <= 4 ? 4 : 8;
+    int r = 1;   // k-steps packed per register set: M <= 16 / r, r <= ks
+    while (r < ks && M <= 16 / (2 * r)) r *= 2;
+    kfn f = nullptr;
+#define I8L_DEC(KS_, R_) if (ks == KS_ && r == R_) f = decode_kernel<KS_, R_, 2>;
+    I8L_DEC(1, 1) I8L_DEC(2, 1) I8L_DEC(2, 2) I8L_DEC(4, 1) I8L_DEC(4, 2) I8L_DEC(4, 4)
+    I8L_DEC(8, 1) I8L_DEC(8, 2) I8L_DEC(8, 4) I8L_DEC(8, 8)
+#undef I8L_DEC
+    hipLaunchKernelGGL(f, grid, block, 0, stream, d);
     return hipGetLastError();
   }
   hipError_t e = launch_quantize_activation(X, M, K, threshold, enabled, ws, stream);
