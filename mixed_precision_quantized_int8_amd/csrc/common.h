@@ -59,7 +59,6 @@ __device__ __forceinline__ void lds_sync() {
 // and size (dword 3 = 0x00020000 is the gfx9 data format for raw byte access).
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
 constexpr uint32_t kBufOff = 0x80000000u;
-constexpr int kBufNT = 2;   // cache policy: nontemporal (streamed once)
 __device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }

@@ -19,7 +19,8 @@
 //     loaded as soon as the columns are known, long before they are needed);
 //   * a second barrier sums the 8 waves' int32 partials (exact) and fp32
 //     outlier partials, then the epilogue dequantizes and stores fp16.
-// The weight is streamed with 16-byte nontemporal loads; the first PRE
+// The weight is streamed with 16-byte buffer loads (default cache policy:
+// measured faster here than the nontemporal hint); the first PRE
 // k-steps of a wave are issued before the activation stage and the rest right
 // after its barrier.  The K chunk a wave streams is rotated by the workgroup
 // index (measured ~15% more HBM bandwidth than all starting at chunk 0).
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     for (int u = u0; u < u1; ++u)
 #pragma unroll
       for (int c = 0; c < kDecP; ++c)
-        fb[u][c] = buf_load16<kBufNT>(rw, wb + (uint32_t)(c * 16 * K + u * 64));
+        fb[u][c] = buf_load16(rw, wb + (uint32_t)(c * 16 * K + u * 64));
   };
   constexpr int kPre = PRE < KS ? PRE : KS;
   load_b(0, kPre);
@@ -257,6 +258,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   for (int c = 0; c < kDecP; ++c) acc[c] = v4i{0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < NSET; ++j) asm volatile("" : "+v"(xr[j][0]), "+v"(xr[j][1]));
+  // all codes first (the weight is still in flight), then the products in the
+  // order the weight arrives
+  v4i a[KS];
 #pragma unroll
   for (int j = 0; j < NSET; ++j) {
     const v4i cj = codes16(xr[j], inv65);
@@ -264,24 +268,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     for (int qq = 0; qq < R; ++qq) {
       const int t = j * R + qq;
       // operand row lr < MR takes the codes of row lr, slot qq (lane lr + qq*MR)
-      v4i a;
       if (qq == 0) {
-        a = cj;
+        a[t] = cj;
       } else {
         const int src = (lane & ~15) | ((lr + qq * MR) & 15);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = __shfl(cj[i], src, 64);
+        for (int i = 0; i < 4; ++i) a[t][i] = __shfl(cj[i], src, 64);
       }
-      if (R > 1 && lr >= MR) a = v4i{0, 0, 0, 0};
+      if (R > 1 && lr >= MR) a[t] = v4i{0, 0, 0, 0};
       // codes also go to LDS (all workgroups: no branch near the loads); workgroup
       // 0 copies them to the workspace at the end (steps past this wave's chunk
       // land in a spare slot, not the next chunk's)
-      sQ[lr][s0 + t < s1 ? (s0 + t) * 4 + g : KS * kDecWaves * 4 + g] = a;
-#pragma unroll
-      for (int c = 0; c < kDecP; ++c)
-        acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, fb[t][c], acc[c], 0, 0, 0);
+      sQ[lr][s0 + t < s1 ? (s0 + t) * 4 + g : KS * kDecWaves * 4 + g] = a[t];
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int c = 0; c < kDecP; ++c)
+      acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], fb[t][c], acc[c], 0, 0, 0);
 
   // ---- outlier product of this chunk's columns (lane = feature n0 + lane) ----------
   if (wcount > 0) {

@@ -299,3 +299,36 @@ def test_workload_full_sampled(lib, name):
     np.testing.assert_array_equal(host(acc[ri, ci]), acc_o)
     del acc, Y, Wq, ws, Xd, Wd
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------------
+# graph capture: replays of a captured int8_linear equal the eager call
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,N", [(8, 1024, 4096), (300, 272, 520)])
+def test_linear_graph_replay(lib, M, K, N):
+    say(f"int8_linear graph replay M={M} K={K} N={N}")
+    X, W, _ = wl.make_small(M, K, N, seed=M + K, n_out=3, x_sigma=1.0)
+    X2, _, _ = wl.make_small(M, K, N, seed=M + K + 1, n_out=2, x_sigma=1.0)
+    Xd, Wd, X2d = dev(X), dev(W), dev(X2)
+    Wq, sw = lib.quantize_weight(Wd)
+    ws = lib.new_workspace(M, K, N, Xd.device)
+    Y_eager = lib.linear(Xd, Wq, sw, Wd, 6.0, workspace=ws).clone()
+    Yg = torch.empty_like(Y_eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lib.linear(Xd, Wq, sw, Wd, 6.0, workspace=ws, out=Yg)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.linear(Xd, Wq, sw, Wd, 6.0, workspace=ws, out=Yg)
+    for rep in range(3):
+        Yg.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(Yg).view(np.uint16), host(Y_eager).view(np.uint16),
+                                      err_msg=f"replay {rep}")
+        # eager work on other inputs (same workspace) between the replays
+        lib.linear(X2d, Wq, sw, Wd, 6.0, workspace=ws)
+        torch.cuda.synchronize()
