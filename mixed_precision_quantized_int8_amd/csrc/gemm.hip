@@ -133,12 +133,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   }
   const int8_t* tileA = a.Xq + (size_t)m0 * K;
   const int8_t* tileB = a.Wq + (size_t)n0 * K;
-  // Loads of stage kt into ring buffer `stage`; branch-free so that they can
-  // be interleaved with the MFMAs (K-tail chunks select the zero page per lane).
-  auto issue = [&](int stage, int kt) {
+  // Loads of stage kt into ring buffer `stage`, in two groups of 4 (blocks
+  // 4w, 4w+1 of A and B; blocks 4w+2, 4w+3) that go out in different halves of
+  // an iteration; branch-free so that they can be interleaved with the MFMAs
+  // (K-tail chunks select the zero page per lane).
+  auto issue_group = [&](int stage, int kt, int grp) {
     const int k0 = kt * kBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 2 * grp; i < 2 * grp + 2; ++i) {
       const int kk = k0 + cofs[i];
       const bool in = kk < K;
       const int8_t* ga = in ? tileA + rowA[i] + kk : g_zero_page;
@@ -180,33 +182,48 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
   constexpr int kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100;
 
-  // Every loop iteration issues exactly one stage of 8 loads per wave (past the
-  // last stage it re-reads stage nk-1 into the buffer of a consumed stage), so
-  // the number of loads issued after any stage is constant: when stage kt+1 is
-  // waited for, the kStages-3 newer stages may stay in flight.
+  // Ring schedule.  The buffer of stage kt is free once every wave has read
+  // its half-1 fragments, i.e. after the barrier in the middle of iteration kt,
+  // so stage kt+4 can go there.  Each stage's 8 loads per wave go out in two
+  // groups: group 0 of stage kt+4 in the second half of iteration kt, group 1
+  // in the first half of iteration kt+1, one load per ~4 MFMAs, so that the
+  // four waves do not flood the load pipeline at the same moment.  Every
+  // iteration issues exactly 8 loads (past the last stage they re-read stage
+  // nk-1 into a consumed buffer), so when stage kt+1 is waited for, the 16
+  // loads of stages kt+2 and kt+3 may stay in flight.
+  issue_group(0, 0, 0);
+  issue_group(0, 0, 1);
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue(s, min(s, nk - 1));
+  for (int s = 1; s < kStages - 1; ++s) {
+    issue_group(s, min(s, nk - 1), 0);
+    issue_group(s, min(s, nk - 1), 1);
+  }
+  issue_group(kStages - 1, min(kStages - 1, nk - 1), 0);
   static_assert(kStages == 4, "wait counts below assume a 4-stage ring");
-  wait_vmcnt<16>();   // stage 0 landed, stages 1-2 in flight
+  wait_vmcnt<20>();   // stage 0 landed
   lds_barrier();
 
   v4i f0a[4], f0b[4], f1a[4], f1b[4];
   read_half(0, 0, f0a, f0b);
   for (int kt = 0; kt < nk; ++kt) {
-    // ---- half 0 of stage kt: MFMAs on f0, with the 8 reads of half 1 of
-    // stage kt interleaved one per MFMA.  The only outstanding LDS reads here
-    // are those of f0, so draining lgkmcnt first costs little and keeps the
-    // compiler from waiting for the new reads before the MFMAs.
+    // ---- half 0 of stage kt: MFMAs on f0; the 8 reads of half 1 of stage kt
+    // and group 1 of stage kt+3 (its buffer held stage kt-1, consumed before
+    // the previous iteration's barrier) interleaved.  The only outstanding LDS
+    // reads here are those of f0, so draining lgkmcnt first costs little.
     wait_lgkmcnt0();
     read_half(kt, 1, f1a, f1b);
+    issue_group((kt + 3) % kStages, min(kt + 3, nk - 1), 1);
 #pragma unroll
     for (int q = 0; q < 16; ++q) mfma_one(f0a, f0b, q);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
       __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt0();
     // ---- half 1: the first MFMA goes out before the stage wait and the
@@ -214,23 +231,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     mfma_one(f1a, f1b, 0);
     __builtin_amdgcn_sched_barrier(0);
     // Stage kt+1 must have landed in every wave's view.
-    wait_vmcnt<8 * (kStages - 3)>();
+    wait_vmcnt<16>();
     lds_barrier();
-    // The buffer refilled here held stage kt-1, whose fragments every wave
-    // finished reading before the barrier above.
-    issue((kt + kStages - 1) % kStages, min(kt + kStages - 1, nk - 1));
-    // On the last step this re-reads stage kt (landed, unused), so that the
-    // registers keep fixed roles.
+    // Stage kt is fully read: its buffer takes group 0 of stage kt+4.  On the
+    // last step the fragment reads re-read stage kt (landed, unused), so that
+    // the registers keep fixed roles.
     read_half(kt + 1 < nk ? kt + 1 : kt, 0, f0a, f0b);
+    issue_group(kt % kStages, min(kt + 4, nk - 1), 0);
 #pragma unroll
     for (int q = 1; q < 16; ++q) mfma_one(f1a, f1b, q);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
       __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 7, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 3, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   wait_vmcnt<0>();
@@ -252,16 +270,33 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
       }
     return;
   } else {
+    // Epilogue, one 32x32 block of the wave tile at a time (16 values per lane
+    // live, so the accumulators can stay in the accumulation registers): the
+    // int32 block is dequantized to fp32 (acc * sx[m] * sw[n] / 127^2), the
+    // outlier product is accumulated onto it by the fp16 matrix cores from
+    // X_O and the matching weight rows staged in LDS, and it is stored as fp16.
+    // Up to kOutG outlier columns are staged once per tile; beyond that the
+    // fragments are read straight from memory per block (correct, slower;
+    // such inputs are rare).
+    constexpr int kOutG = 96;                  // 3 chunks of 32 outlier columns
+    constexpr int kOutC = kOutG / 8;           // 16-byte chunks per staged row
     const int n_out = *a.n_out;
-    uint16_t* sAo = reinterpret_cast<uint16_t*>(&smem[0][0][0]);   // [256 rows][32 halves]
-    uint16_t* sBo = reinterpret_cast<uint16_t*>(&smem[0][1][0]);   // [256 cols][32 halves]
-    // Stage outlier columns j0 .. j0+31 of X_O and the matching weight rows
-    // (transposed to [column][outlier]); zero past n_out.
+    const int ngroups = (n_out + kOutG - 1) / kOutG;
+    uint16_t* sAo = reinterpret_cast<uint16_t*>(&smem[0][0][0]);   // [256 rows][96 halves]
+    uint16_t* sBo = sAo + kBM * kOutG;                             // [256 cols][96 halves]
+    float* sSx = reinterpret_cast<float*>(sBo + kBN * kOutG);      // [256]
+    float* sSw = sSx + kBM;                                        // [256], includes 1/127^2
+    // 16-byte chunk c of staged row r sits at c ^ ((r >> 2) & 3): conflict-free
+    // fragment reads with the 192-byte row stride
+    auto och = [](int r, int c) { return (c ^ ((r >> 2) & 3)) << 3; };
+    sSx[t] = m0 + t < M ? a.sx[m0 + t] : 0.0f;
+    sSw[t] = n0 + t < N ? a.sw[n0 + t] * (1.0f / 16129.0f) : 0.0f;
+
+    // X_O[., j0 ..] and rows idx[j0 ..] of W (transposed to [column][outlier]);
+    // zero past n_out and outside the matrix
     auto stage_outliers = [&](int j0) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int q = t + kGemmThreads * s;
-        const int row = q >> 2, c = q & 3;
+      for (int q = t; q < kBM * kOutC; q += kGemmThreads) {
+        const int row = q / kOutC, c = q % kOutC;
         const int gm = m0 + row;
         const int jj = j0 + c * 8;
         v4i v = {0, 0, 0, 0};
@@ -275,99 +310,77 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
             v = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
           }
         }
-        *reinterpret_cast<v4i*>(&sAo[row * 32 + ((c ^ lds_swz(row)) << 3)]) = v;
+        *reinterpret_cast<v4i*>(&sAo[row * kOutG + och(row, c)]) = v;
       }
       const int col = t;   // 256 threads = 256 columns
       const int gn = n0 + col;
-      uint32_t w[16];
+      for (int c = 0; c < kOutC; ++c) {
+        uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int e = 0; e < 16; ++e) w[e] = 0;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int j = j0 + e;
-        uint32_t h = 0;
-        if (j < n_out && gn < N) h = a.W_rows[(size_t)a.idx[j] * N + gn];
-        w[e >> 1] |= h << ((e & 1) * 16);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        v4i v = {(int)w[4 * c], (int)w[4 * c + 1], (int)w[4 * c + 2], (int)w[4 * c + 3]};
-        *reinterpret_cast<v4i*>(&sBo[col * 32 + ((c ^ lds_swz(col)) << 3)]) = v;
-      }
-    };
-    // fp16 fragments for v_mfma_f32_32x32x16_f16: half h covers outliers
-    // 16h .. 16h+15; lane l reads row l % 32, logical chunk 2h + l / 32.
-    auto load_ao = [&](v8h (&fa)[4][2]) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = wm + i * 32 + l32;
-          fa[i][h] = *reinterpret_cast<const v8h*>(
-              &sAo[row * 32 + (((2 * h + lh) ^ lds_swz(row)) << 3)]);
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + c * 8 + e;
+          const uint32_t h = (j < n_out && gn < N) ? a.W_rows[(size_t)a.idx[j] * N + gn] : 0u;
+          w[e >> 1] |= h << ((e & 1) * 16);
         }
+        *reinterpret_cast<v4i*>(&sBo[col * kOutG + och(col, c)]) =
+            v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      }
     };
-    auto load_bo = [&](int j, v8h (&fb)[2]) {
-      const int col = wn + j * 32 + l32;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        fb[h] = *reinterpret_cast<const v8h*>(
-            &sBo[col * 32 + (((2 * h + lh) ^ lds_swz(col)) << 3)]);
-    };
+    if (ngroups == 1) stage_outliers(0);
+    __syncthreads();
 
-    const bool one_chunk = n_out <= 32;
-    v8h fo[4][2];
-    if (n_out > 0 && one_chunk) {
-      stage_outliers(0);
-      __syncthreads();
-      load_ao(fo);
-    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn + j * 32 + l32;
-      const float swj = n < N ? a.sw[n] * (1.0f / 16129.0f) : 0.0f;
-      v16f y[4];
+    for (int i = 0; i < 4; ++i) {
+      float sxv[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int q = 0; q < 4; ++q) {   // rows 8q + 4*lh .. +3 of block i are contiguous
+        const v4f v = *reinterpret_cast<const v4f*>(&sSx[wm + i * 32 + 8 * q + 4 * lh]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm + i * 32 + d_row(r, lane);
-          const float sxm = m < M ? a.sx[m] : 0.0f;
-          y[i][r] = (float)acc[i][j][r] * (sxm * swj);
-        }
-      if (n_out > 0) {
-        if (one_chunk) {
-          v8h fb[2];
-          load_bo(j, fb);
+        for (int e = 0; e < 4; ++e) sxv[4 * q + e] = v[e];
+      }
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn + j * 32 + l32;
+        const float swv = sSw[wn + j * 32 + l32];
+        v16f y;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-              y[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fo[i][h], fb[h], y[i], 0, 0, 0);
-        } else {
-          for (int j0 = 0; j0 < n_out; j0 += 32) {
-            __syncthreads();
-            stage_outliers(j0);
-            __syncthreads();
-            v8h fa[4][2], fb[2];
-            load_ao(fa);
-            load_bo(j, fb);
+        for (int r = 0; r < 16; ++r) y[r] = (float)acc[i][j][r] * (sxv[r] * swv);
+        if (ngroups == 1) {   // uniform: staged fragments
+          for (int cc = 0; cc < 3 && cc * 32 < n_out; ++cc) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-              for (int h = 0; h < 2; ++h)
-                y[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i][h], fb[h], y[i], 0, 0, 0);
+            for (int h = 0; h < 2; ++h) {
+              const int row = wm + i * 32 + l32, col = wn + j * 32 + l32;
+              const int c = cc * 4 + 2 * h + lh;
+              const v8h fa = *reinterpret_cast<const v8h*>(&sAo[row * kOutG + och(row, c)]);
+              const v8h fb = *reinterpret_cast<const v8h*>(&sBo[col * kOutG + och(col, c)]);
+              y = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb, y, 0, 0, 0);
+            }
+          }
+        } else if (ngroups > 1) {   // many outliers: fragments straight from memory
+          const int gm = m0 + wm + i * 32 + l32;
+          for (int j0 = 0; j0 < n_out; j0 += 16) {
+            const int jb = j0 + 8 * lh;
+            uint32_t wa[4] = {0, 0, 0, 0}, wb[4] = {0, 0, 0, 0};
+            for (int e = 0; e < 8; ++e) {
+              const int jj = jb + e;
+              if (jj < n_out) {
+                if (gm < M) wa[e >> 1] |= (uint32_t)a.X_O[(size_t)gm * K + jj] << ((e & 1) * 16);
+                if (n < N) wb[e >> 1] |= (uint32_t)a.W_rows[(size_t)a.idx[jj] * N + n] << ((e & 1) * 16);
+              }
+            }
+            const v8h fa = __builtin_bit_cast(v8h, v4i{(int)wa[0], (int)wa[1], (int)wa[2], (int)wa[3]});
+            const v8h fb = __builtin_bit_cast(v8h, v4i{(int)wb[0], (int)wb[1], (int)wb[2], (int)wb[3]});
+            y = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb, y, 0, 0, 0);
           }
         }
-      }
-      if (n < N) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
+        if (n < N) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int m = m0 + wm + i * 32 + d_row(r, lane);
-            if (m < M) a.Y[(size_t)m * N + n] = f2h(y[i][r]);
+            if (m < M) a.Y[(size_t)m * N + n] = f2h(y[r]);
           }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one block at a time: bounded live ranges
       }
     }
   }
