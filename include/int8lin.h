@@ -69,7 +69,10 @@ typedef enum {
  *   X_outliers   fp16  [M][K] cap outlier values, element (i, j) at i*K + j,
  *                                 j < n_out, j-th outlier column in ascending order
  *   flags        uint32 [ceil(K/32)] internal: outlier column bitmask
- * `total` is the size the call requires. */
+ *   gemm_counters, gemm_partials   internal (M > 16): arrival counters and
+ *                                 int32 partial tiles of the GEMM's split-K
+ *                                 tail; gemm_slices partial tiles of 256x256
+ * `total` is the size the call requires; it depends on M, K and N. */
 typedef struct {
   size_t total;
   size_t n_outliers;
@@ -78,9 +81,12 @@ typedef struct {
   size_t Xq;
   size_t X_outliers;
   size_t flags;
+  size_t gemm_counters;
+  size_t gemm_partials;
+  size_t gemm_slices;
 } i8l_workspace_layout;
 
-/* Fills *layout for an int8_linear call of this shape (N does not change it).
+/* Fills *layout for an int8_linear call of this shape.
  * Returns I8L_ERR_INVALID_ARG / I8L_ERR_K_TOO_LARGE on a bad shape. */
 i8l_status i8l_linear_workspace(int64_t M, int64_t K, int64_t N, i8l_workspace_layout *layout);
 

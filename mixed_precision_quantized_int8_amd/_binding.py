@@ -50,6 +50,9 @@ class WorkspaceLayout(ctypes.Structure):
         ("Xq", ctypes.c_size_t),
         ("X_outliers", ctypes.c_size_t),
         ("flags", ctypes.c_size_t),
+        ("gemm_counters", ctypes.c_size_t),
+        ("gemm_partials", ctypes.c_size_t),
+        ("gemm_slices", ctypes.c_size_t),
     ]
 
 

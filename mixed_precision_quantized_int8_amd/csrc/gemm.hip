@@ -42,6 +42,8 @@
 // With at most 32 outlier columns the staging happens once per tile.  The
 // outlier count is read from device memory, so no host synchronization is
 // needed.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -56,12 +58,9 @@ constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 8;
 __device__ __forceinline__ int lds_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-// Tile assignment: contiguous tile ranges per XCD, grouped order inside.
-__device__ __forceinline__ void tile_coords(int bid, int nTm, int nTn, int& tm, int& tn) {
-  const int T = nTm * nTn;
-  const int q = T >> 3, r = T & 7;
-  const int xcd = bid & 7, local = bid >> 3;
-  const int tile = xcd * q + min(xcd, r) + local;
+// Tile order: linear tile index -> (tile row, tile column), in groups of
+// kGroupM tile rows so that concurrently running tiles share operand panels.
+__device__ __forceinline__ void tile_of(int tile, int nTm, int nTn, int& tm, int& tn) {
   const int per_group = kGroupM * nTn;
   const int g = tile / per_group;
   const int first_m = g * kGroupM;
@@ -69,6 +68,13 @@ __device__ __forceinline__ void tile_coords(int bid, int nTm, int nTn, int& tm, 
   const int in = tile - g * per_group;
   tm = first_m + in % gm;
   tn = in / gm;
+}
+// Workgroup b runs on XCD b % 8: each XCD takes a contiguous range of the
+// first `count` tiles, so that its L2 serves neighbouring tiles.
+__device__ __forceinline__ int xcd_tile(int bid, int count) {
+  const int q = count >> 3, r = count & 7;
+  const int xcd = bid & 7, local = bid >> 3;
+  return xcd * q + min(xcd, r) + local;
 }
 
 // 16 bytes of zeros per lane for K-tail chunks (k >= K): the direct LDS loads
@@ -97,16 +103,33 @@ __device__ __forceinline__ int d_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-template <bool OUT_I32>
+// SPLIT: the workgroups are the split tiles of the tail (S per tile), each on
+// its own range of k-steps; a separate instantiation, so that the whole-tile
+// kernel carries none of the split bookkeeping.
+template <bool OUT_I32, bool SPLIT>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   // kStages ring buffers of [A 256 x 64 | B 256 x 64] bytes
   __shared__ __attribute__((aligned(1024))) int8_t smem[kStages][2][kBM * kBK];
 
+  __shared__ int sLast;
+
   const int M = a.M, N = a.N, K = a.K;
-  const int nk = (K + kBK - 1) / kBK;   // k-steps of 64 bytes
+  const int nkt = (K + kBK - 1) / kBK;   // k-steps of 64 bytes
   const int nTm = (M + kBM - 1) / kBM, nTn = (N + kBN - 1) / kBN;
+  // Whole tiles first; then the split tiles of the tail, S workgroups each,
+  // every one on its own range of k-steps [kb, kb + nk).
+  int tile, kb = 0, nk = nkt, slot = -1, sidx = 0;
+  if constexpr (!SPLIT) {
+    tile = xcd_tile(blockIdx.x, a.full_tiles);
+  } else {
+    slot = blockIdx.x / a.split_S;
+    sidx = blockIdx.x % a.split_S;
+    tile = a.full_tiles + slot;
+    kb = sidx * nkt / a.split_S;
+    nk = (sidx + 1) * nkt / a.split_S - kb;
+  }
   int tm, tn;
-  tile_coords(blockIdx.x, nTm, nTn, tm, tn);
+  tile_of(tile, nTm, nTn, tm, tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
 
   const int t = threadIdx.x;
@@ -137,8 +160,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   // 4w, 4w+1 of A and B; blocks 4w+2, 4w+3) that go out in different halves of
   // an iteration; branch-free so that they can be interleaved with the MFMAs
   // (K-tail chunks select the zero page per lane).
-  auto issue_group = [&](int stage, int kt, int grp) {
-    const int k0 = kt * kBK;
+  auto issue_group = [&](int stage, int kt, int grp) {   // kt: step inside [kb, kb + nk)
+    const int k0 = (kb + kt) * kBK;
 #pragma unroll
     for (int i = 2 * grp; i < 2 * grp + 2; ++i) {
       const int kk = k0 + cofs[i];
@@ -255,6 +278,29 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   wait_lgkmcnt0();
   __syncthreads();   // all waves done with the ring before the epilogue reuses it
 
+  if constexpr (!OUT_I32 && SPLIT) {
+    // Split tile: publish this K range's int32 partial, count the arrival; the
+    // last of the S workgroups runs the epilogue on the sum of the S partials
+    // (exact integer sums, in any order), read back block by block.
+    constexpr int kTile = kBM * kBN;
+    int32_t* mine = a.part + (size_t)(slot * a.split_S + sidx) * kTile;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          mine[(wm + i * 32 + d_row(r, lane)) * kBN + wn + j * 32 + l32] = acc[i][j][r];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    __threadfence();
+    __syncthreads();
+    if (t == 0) sLast = atomicAdd(&a.cnt[slot], 1) == a.split_S - 1;
+    __syncthreads();
+    if (!sLast) return;
+    __threadfence();   // the partials are read in the epilogue, block by block
+  }
+
   if constexpr (OUT_I32) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -342,9 +388,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
       for (int j = 0; j < 4; ++j) {
         const int n = n0 + wn + j * 32 + l32;
         const float swv = sSw[wn + j * 32 + l32];
+        int tot[16];
+        if constexpr (SPLIT) {
+          // all S partials from memory (this workgroup's own included), so the
+          // accumulators are only stored after the loop and keep their registers
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tot[r] = 0;
+          for (int s2 = 0; s2 < a.split_S; ++s2) {   // uniform
+            const int32_t* part = a.part + (size_t)(slot * a.split_S + s2) * (kBM * kBN);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              tot[r] += part[(wm + i * 32 + d_row(r, lane)) * kBN + wn + j * 32 + l32];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tot[r] = acc[i][j][r];
+        }
         v16f y;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) y[r] = (float)acc[i][j][r] * (sxv[r] * swv);
+        for (int r = 0; r < 16; ++r) y[r] = (float)tot[r] * (sxv[r] * swv);
         if (ngroups == 1) {   // uniform: staged fragments
           for (int cc = 0; cc < 3 && cc * 32 < n_out; ++cc) {
 #pragma unroll
@@ -386,13 +448,63 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   }
 }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
+GemmSplit gemm_split_plan(int M, int N, int K, int cus) {
+  const int nTm = (M + kBM - 1) / kBM, nTn = (N + kBN - 1) / kBN;
+  const int T = nTm * nTn, nk = (K + kBK - 1) / kBK;
+  GemmSplit p{T, 0, 1};
+  if (cus <= 0 || T <= 0) return p;
+  const int rem = T % cus;
+  // Measured under the chip's power limit: a mostly empty last round runs at a
+  // higher clock and splitting it costs more than it saves, so only a last
+  // round that is at least half full (or a problem smaller than one round) is
+  // split.
+  if (rem == 0 || (T > cus && 2 * rem < cus)) return p;
+  // each split keeps at least 16 k-steps, so the fix-up stays a small part
+  const int S = std::min(cus / rem, nk / 16);
+  if (S < 2) return p;
+  return GemmSplit{T - rem, rem, S};
+}
+
+namespace {
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cache[dev] = n > 0 ? n : -1;
+  }
+  return cache[dev] > 0 ? std::min(cache[dev], kGemmMaxSlices) : 0;
+}
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& in, hipStream_t stream) {
+  GemmArgs a = in;
   const int nTm = (a.M + kBM - 1) / kBM, nTn = (a.N + kBN - 1) / kBN;
-  const dim3 grid(nTm * nTn);
-  if (a.acc)
-    hipLaunchKernelGGL(gemm_i8_kernel<true>, grid, dim3(kGemmThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(gemm_i8_kernel<false>, grid, dim3(kGemmThreads), 0, stream, a);
+  GemmSplit p{nTm * nTn, 0, 1};
+  if (!a.acc && a.part && a.cnt && a.part_slices > 0) {
+    const GemmSplit q = gemm_split_plan(a.M, a.N, a.K, device_cus());
+    if (q.split_tiles > 0 && q.split_tiles * q.S <= a.part_slices) p = q;
+  }
+  a.full_tiles = p.full_tiles;
+  a.split_S = p.S;
+  if (p.split_tiles > 0) {
+    hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(a.cnt), p.split_tiles, 0u, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (a.acc) {
+    hipLaunchKernelGGL((gemm_i8_kernel<true, false>), dim3(p.full_tiles), dim3(kGemmThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
+  // whole tiles, then the split tail (both launches fill the chip)
+  if (p.full_tiles > 0)
+    hipLaunchKernelGGL((gemm_i8_kernel<false, false>), dim3(p.full_tiles), dim3(kGemmThreads), 0,
+                       stream, a);
+  if (p.split_tiles > 0)
+    hipLaunchKernelGGL((gemm_i8_kernel<false, true>), dim3(p.split_tiles * p.S),
+                       dim3(kGemmThreads), 0, stream, a);
   return hipGetLastError();
 }
 

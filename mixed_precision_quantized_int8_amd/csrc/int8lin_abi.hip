@@ -55,7 +55,9 @@ i8l_status check_shape(const char* fn, int64_t M, int64_t K, int64_t N) {
   return I8L_OK;
 }
 
-i8l_workspace_layout layout_of(int64_t M, int64_t K) {
+// The GEMM's split-K tail (M > 16) needs arrival counters and int32 partial
+// tiles; they are sized for a device with up to kGemmMaxSlices compute units.
+i8l_workspace_layout layout_of(int64_t M, int64_t K, int64_t N) {
   i8l_workspace_layout L;
   size_t off = 0;
   L.n_outliers = off; off += up(sizeof(int32_t));
@@ -64,6 +66,14 @@ i8l_workspace_layout layout_of(int64_t M, int64_t K) {
   L.flags = off; off += up((size_t)((K + 31) / 32) * sizeof(uint32_t));
   L.Xq = off; off += up((size_t)M * (size_t)K);
   L.X_outliers = off; off += up((size_t)M * (size_t)K * sizeof(uint16_t));
+  int slices = 0;
+  if (M > 16 && N > 0) {
+    const i8l::GemmSplit p = i8l::gemm_split_plan((int)M, (int)N, (int)K, i8l::kGemmMaxSlices);
+    slices = p.split_tiles * p.S;
+  }
+  L.gemm_counters = off; off += up(slices > 0 ? i8l::kGemmMaxSlices * sizeof(int32_t) : 0);
+  L.gemm_partials = off; off += up((size_t)slices * 256 * 256 * sizeof(int32_t));
+  L.gemm_slices = (size_t)slices;
   L.total = off;
   return L;
 }
@@ -77,6 +87,9 @@ i8l::Workspace carve(void* ws, const i8l_workspace_layout& L) {
   w.Xq = reinterpret_cast<int8_t*>(b + L.Xq);
   w.X_O = reinterpret_cast<uint16_t*>(b + L.X_outliers);
   w.flags = reinterpret_cast<uint32_t*>(b + L.flags);
+  w.gemm_cnt = reinterpret_cast<int32_t*>(b + L.gemm_counters);
+  w.gemm_part = reinterpret_cast<int32_t*>(b + L.gemm_partials);
+  w.gemm_slices = (int)L.gemm_slices;
   return w;
 }
 
@@ -99,13 +112,13 @@ I8L_API i8l_status i8l_linear_workspace(int64_t M, int64_t K, int64_t N,
   i8l_status s = check_shape("i8l_linear_workspace", M, K, N);
   if (s != I8L_OK) return s;
   if (!layout) return fail(I8L_ERR_INVALID_ARG, "i8l_linear_workspace: layout is NULL");
-  *layout = layout_of(M, K);
+  *layout = layout_of(M, K, N);
   return ok();
 }
 
 I8L_API size_t i8l_linear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   if (check_shape("i8l_linear_workspace_bytes", M, K, N) != I8L_OK) return 0;
-  return layout_of(M, K).total;
+  return layout_of(M, K, N).total;
 }
 
 I8L_API i8l_status int8_quantize_weight(const uint16_t* W, int64_t K, int64_t N, int8_t* Wq,
@@ -140,7 +153,7 @@ I8L_API i8l_status int8_linear(const uint16_t* X, int64_t M, int64_t K, const in
   if (enabled) REQUIRE_PTR(fn, W_outlier_rows, 2);
   else if (W_outlier_rows && !aligned(W_outlier_rows, 2))
     return fail(I8L_ERR_INVALID_ARG, "%s: W_outlier_rows must be 2-byte aligned", fn);
-  const i8l_workspace_layout L = layout_of(M, K);
+  const i8l_workspace_layout L = layout_of(M, K, N);
   if (workspace_bytes < L.total)
     return fail(I8L_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn,
                 workspace_bytes, L.total);
@@ -154,7 +167,8 @@ I8L_API i8l_status int8_linear(const uint16_t* X, int64_t M, int64_t K, const in
   }
   hipError_t e = i8l::launch_quantize_activation(X, m, k, threshold, enabled, w, st);
   if (e != hipSuccess) return hip_status(fn, e);
-  i8l::GemmArgs g{w.Xq, Wq, m, n, k, w.sx, sw, w.n_out, w.idx, w.X_O, W_outlier_rows, Y, nullptr};
+  i8l::GemmArgs g{w.Xq, Wq, m, n, k, w.sx, sw, w.n_out, w.idx, w.X_O, W_outlier_rows, Y, nullptr,
+                  w.gemm_cnt, w.gemm_part, w.gemm_slices, 0, 1};
   return hip_status(fn, i8l::launch_gemm(g, st));
 }
 
@@ -182,7 +196,7 @@ I8L_API i8l_status int8_quantize_activation(const uint16_t* X, int64_t M, int64_
   REQUIRE_PTR(fn, n_outliers, 4);
   REQUIRE_PTR(fn, X_outliers, 16);
   REQUIRE_PTR(fn, workspace, 16);
-  const i8l_workspace_layout L = layout_of(M, K);
+  const i8l_workspace_layout L = layout_of(M, K, 0);
   if (workspace_bytes < L.total)
     return fail(I8L_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn,
                 workspace_bytes, L.total);
@@ -208,7 +222,7 @@ I8L_API i8l_status int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, 
   REQUIRE_PTR(fn, acc, 16);
   (void)hipGetLastError();
   i8l::GemmArgs g{Xq, Wq, (int)M, (int)N, (int)K, nullptr, nullptr, nullptr, nullptr,
-                  nullptr, nullptr, nullptr, acc};
+                  nullptr, nullptr, nullptr, acc, nullptr, nullptr, 0, 0, 1};
   return hip_status(fn, i8l::launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 

@@ -16,7 +16,20 @@ struct Workspace {
   int8_t* Xq;          // [M][K]
   uint16_t* X_O;       // [M][K] capacity, row stride K
   uint32_t* flags;     // [ceil(K/32)]
+  int32_t* gemm_cnt;   // [kGemmMaxSlices] arrival counters of split tiles
+  int32_t* gemm_part;  // [gemm_slices][256][256] int32 partial tiles
+  int gemm_slices;     // partial tiles the workspace holds
 };
+
+// Split-K tail of the GEMM: the tiles of the last, partial round over the
+// compute units are split along K so that the round fills the chip.
+constexpr int kGemmMaxSlices = 256;
+struct GemmSplit {
+  int full_tiles;    // tiles computed whole (a multiple of the CU count)
+  int split_tiles;   // tiles after them, each split into S K ranges
+  int S;
+};
+GemmSplit gemm_split_plan(int M, int N, int K, int cus);
 
 // p[0 .. n) = v, as a kernel (a fill kernel rather than a memset node keeps the
 // sequence safe to capture in a HIP graph).
@@ -45,6 +58,11 @@ struct GemmArgs {
   const uint16_t* W_rows;   // [K][N]
   uint16_t* Y;
   int32_t* acc;
+  int32_t* cnt;      // split-K tail (Y output only): workspace counters / partials
+  int32_t* part;
+  int part_slices;   // 0: never split
+  // set by launch_gemm
+  int full_tiles, split_S;
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 

@@ -116,8 +116,21 @@ def test_workspace_layout(i8l):
         assert L["flags"] - L["sx"] >= 4 * M
         assert L["Xq"] - L["flags"] >= 4 * ((K + 31) // 32)
         assert L["X_outliers"] - L["Xq"] >= M * K
-        assert L["total"] - L["X_outliers"] >= 2 * M * K
-        assert i8l.workspace_bytes(M, K, 7) == L["total"]
+        assert L["gemm_counters"] - L["X_outliers"] >= 2 * M * K
+        assert L["gemm_partials"] >= L["gemm_counters"]
+        assert L["total"] - L["gemm_partials"] >= L["gemm_slices"] * 256 * 256 * 4
+        if L["gemm_slices"]:
+            assert L["gemm_partials"] - L["gemm_counters"] >= 4 * 256
+        assert i8l.workspace_bytes(M, K, 123) == L["total"]
+    # split-K tail of the GEMM: tiles of a last round over 256 compute units that
+    # is at least half full (or of a problem below one round), split along K (at
+    # least 16 k-steps per split); none for decode shapes
+    assert i8l.workspace_layout(16, 4096, 16384)["gemm_slices"] == 0
+    assert i8l.workspace_layout(2048, 14336, 43008)["gemm_slices"] == 0        # 1344 tiles
+    assert i8l.workspace_layout(2048, 2048, 12200)["gemm_slices"] == 128 * 2   # 384 tiles
+    assert i8l.workspace_layout(4096, 57344, 14336)["gemm_slices"] == 128 * 2  # 896 tiles
+    assert i8l.workspace_layout(8192, 8192, 8192)["gemm_slices"] == 0         # 1024 tiles
+    assert i8l.workspace_layout(520, 2048, 1300)["gemm_slices"] == 18 * 2     # 18 tiles
     assert i8l.workspace_bytes(4, 70, 4) == 0
     with pytest.raises(i8l.Int8LinError):
         i8l.workspace_layout(4, 70)

@@ -180,6 +180,8 @@ def _linear_cases():
     yield "prefill_ragged", 300, 272, 520, 5, 6.0, 1.0
     yield "prefill_tiles", 513, 1040, 769, 8, 6.0, 1.0
     yield "prefill_chunks", 64, 512, 300, 45, 6.0, 1.0
+    yield "prefill_many_outliers", 70, 1024, 300, 130, 6.0, 1.0   # > 96: unstaged path
+    yield "prefill_split_k", 520, 2048, 1300, 6, 6.0, 1.0         # 18 tiles, K split in 2
     yield "prefill_no_outliers", 260, 512, 512, 0, 6.0, 1.0
     yield "prefill_disabled", 260, 512, 512, 3, math.inf, 1.0
     yield "prefill_all_outliers", 70, 256, 96, 0, 2.0 ** -24, 1.0
@@ -332,3 +334,37 @@ def test_linear_graph_replay(lib, M, K, N):
         # eager work on other inputs (same workspace) between the replays
         lib.linear(X2d, Wq, sw, Wd, 6.0, workspace=ws)
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------------
+# GEMM split-K tail: 384 tiles = 256 whole + 128 split along K (sampled outputs)
+# ---------------------------------------------------------------------------------
+def test_linear_split_tail_sampled(lib):
+    M, K, N = 2048, 2048, 12200
+    say(f"int8_linear split tail M={M} K={K} N={N}")
+    assert lib.workspace_layout(M, K, N)["gemm_slices"] == 128 * 2
+    X, W, _ = wl.make_small(M, K, N, seed=77, n_out=5, x_sigma=1.0)
+    Xd, Wd = dev(X), dev(W)
+    Wq, sw = lib.quantize_weight(Wd)
+    ws = lib.new_workspace(M, K, N, Xd.device)
+    Y = lib.linear(Xd, Wq, sw, Wd, 6.0, workspace=ws)
+    torch.cuda.synchronize()
+    act = O.quantize_activation(X, 6.0)
+    check_workspace(lib, ws, M, K, act, "split tail")
+    rng = np.random.default_rng(99)
+    # columns of the split tiles (tile columns 32..47) and elsewhere
+    ns = np.unique(np.concatenate([rng.integers(8192, N, 24), rng.integers(0, 8192, 16),
+                                   [0, 8191, 8192, N - 1]]))
+    Wq_r, sw_r = O.quantize_weight_rows(W, ns)
+    S = 2500
+    rows = np.concatenate([rng.integers(0, M, S), [0, 255, 256, M - 1]])
+    pick = rng.integers(0, len(ns), len(rows))
+    cols = ns[pick]
+    acc_o, Y64 = O.int8_linear_entries(X, Wq_r[pick], sw_r[pick], W, 6.0, rows, cols, act=act)
+    ri = torch.as_tensor(rows, device="cuda:0")
+    ci = torch.as_tensor(cols, device="cuda:0")
+    assert_y(host(Y[ri, ci]), Y64, what="split tail")
+    # a second call on the same workspace (counters are re-armed per call)
+    Y2 = lib.linear(Xd, Wq, sw, Wd, 6.0, workspace=ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(Y2).view(np.uint16), host(Y).view(np.uint16))
