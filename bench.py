@@ -39,7 +39,13 @@ PEAK_INT8_TOPS = 5000.0
 # HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs,
 # scaled by the copy-kernel calibration factor; valid only for the kernel
 # source it was measured on (sha256 of the listed files).
-TRAFFIC = {}
+# (profiles/traffic-decode.md: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB, the
+# factors a 512 MiB device copy gives).
+TRAFFIC = {
+    ("decode_kernel", "decode"): {"bytes": 68624496, "src": "cb5bcc7a282cc020"},
+    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2314256549, "src": "75d3f4421d0b4027"},
+    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 2802323812, "src": "75d3f4421d0b4027"},
+}
 
 
 def kernel_source_hash(files):
