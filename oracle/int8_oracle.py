@@ -43,6 +43,9 @@ its reason in the design notes of the repository):
   r9  the dequantization scale of the weight indexes the OUTPUT feature; the
       Usage section's printed dequantization broadcasts it along the other axis
       of a square matrix, which is a display artefact, not the method.
+  r10 when no fp16 weight is kept, the outlier rows are rebuilt from the codes
+      as the Usage section does, on fp32 values (code x scale, then / 127),
+      and rounded to fp16 for the fp16 outlier product.
 
 Layouts (row-major numpy arrays):
   X  fp16 [M][K]        W  fp16 [K][N]  (math layout, Y = X @ W)
@@ -281,11 +284,15 @@ def int8_linear_entries(X16, Wq_rows, sw_rows, W16, threshold, rows, cols, act=N
 
 
 def dequantize_weight(Wq, sw) -> np.ndarray:
-    """fp16 weight rebuilt from its codes: W[k, n] ~ Wq[n, k] * sw[n] / 127 (r9).
+    """fp16 weight rebuilt from its codes: W[k, n] ~ Wq[n, k] * sw[n] / 127 (r9, r10).
 
     [blog, "Usage"]: the int8 weight times its per-output scale over 127 gives
-    the fp16 weight back.  Returned in math layout [K][N], rounded to fp16.
+    the fp16 weight back; the page forms it on fp32 tensors (code times scale,
+    exact in fp32; then one IEEE fp32 division by 127) and the outlier product
+    uses it as an fp16 operand, so the value is rounded once more, to fp16
+    (round to nearest even).  Returned in math layout [K][N].
     """
-    Wq = np.asarray(Wq, dtype=np.int8).astype(np.float64)
-    sw = np.asarray(sw, dtype=np.float64)
-    return ((Wq * sw[:, None]) / float(INT8_MAX)).T.astype(np.float16)
+    q = np.asarray(Wq, dtype=np.int8).astype(np.float32)
+    s = np.asarray(sw, dtype=np.float32)
+    prod = q * s[:, None]                       # exact: 8-bit integer x fp16 value
+    return (prod / np.float32(INT8_MAX)).T.astype(np.float16)

@@ -428,3 +428,26 @@ def test_sampled_entries_match_full():
     acc, Y64 = O.int8_linear_entries(X, Wq_r, sw_r, W, 6.0, rows, cs)
     np.testing.assert_array_equal(acc, full["acc"][rows, cs])
     np.testing.assert_allclose(Y64, full["Y64"][rows, cs], rtol=1e-12, atol=1e-15)
+
+
+def test_dequantize_weight_closed_forms():
+    """Rebuilt weight rows (no fp16 copy kept): fp16(fl32(q * s) / 127), indexed
+    by the output feature.  Scales that make the result exact pin the formula."""
+    q = np.array([[127, -127, 1, 0, -64, 5],
+                  [127, -1, 32, 64, -32, 96]], dtype=np.int8)        # Wq [N=2][K=6]
+    sw = np.array([127.0, 127.0 / 32.0], dtype=np.float32)          # both fp16-exact
+    W = O.dequantize_weight(q, sw)                                    # [K][N]
+    assert W.shape == (6, 2) and W.dtype == np.float16
+    np.testing.assert_array_equal(W[:, 0], q[0].astype(np.float16))   # s = 127: w = q
+    np.testing.assert_array_equal(W[:, 1], (q[1] / 32.0).astype(np.float16))   # q / 32
+    # an inexact case: 1 * 0.1 / 127 in fp32, then fp16
+    w = O.dequantize_weight(np.array([[1]], np.int8), np.array([np.float32(np.float16(0.1))]))
+    want = np.float16(np.float32(np.float32(np.float16(0.1)) / np.float32(127)))
+    assert w[0, 0] == want
+    # round trip: within half a code step of the original weight
+    rng = np.random.default_rng(5)
+    W0 = (rng.standard_normal((40, 9)) * 0.02).astype(np.float16)
+    Wq, s = O.quantize_weight(W0)
+    back = O.dequantize_weight(Wq, s).astype(np.float64)
+    assert np.all(np.abs(back - W0) <= s.astype(np.float64)[None, :] / 254 * 1.001
+                  + np.abs(W0) * 2.0 ** -11 + 1e-8)
