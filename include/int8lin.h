@@ -107,8 +107,11 @@ i8l_status int8_quantize_weight(const uint16_t *W, int64_t K, int64_t N,
  *   X               fp16 [M][K]  hidden states, read only
  *   Wq, sw          from int8_quantize_weight for the same K, N
  *   W_outlier_rows  fp16 [K][N]  the fp16 weight in math layout; only rows
- *                   that are outlier columns of X are read.  May be NULL only
- *                   when the decomposition is disabled (see threshold).
+ *                   that are outlier columns of X are read.  NULL: no fp16
+ *                   weight is kept, and each outlier weight value is rebuilt
+ *                   from its code as fp16(fl32(Wq[n][k] * sw[n]) / 127)
+ *                   ([blog, "Usage"]: the int8 weight times its per-output
+ *                   scale over 127 gives the weight back).
  *   threshold       finite > 0: columns of X with any |x| >= threshold are
  *                   outliers; <= 0 or +inf: no decomposition (pure int8);
  *                   NaN: I8L_ERR_INVALID_ARG.

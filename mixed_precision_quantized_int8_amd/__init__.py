@@ -80,8 +80,9 @@ def new_workspace(M, K, N, device):
 def linear(X, Wq, sw, W=None, threshold=6.0, workspace=None, out=None):
     """LLM.int8() linear layer: X fp16 [M][K] -> Y fp16 [M][N].
 
-    W (fp16 [K][N]) supplies the weight rows of the outlier columns; it may be
-    None when ``threshold`` disables the decomposition (<= 0 or inf).
+    W (fp16 [K][N]) supplies the weight rows of the outlier columns.  With
+    W None no fp16 weight is kept: those rows are rebuilt from the codes as
+    fp16(Wq[n][k] * sw[n] / 127).
     """
     torch = _torch()
     _require(X, torch.float16, "X")

@@ -34,6 +34,9 @@ CFLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     # keep the compiler from emitting packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # honour every `#pragma unroll` (a partially unrolled loop over the
+    # accumulator blocks would index them at run time and move them to scratch)
+    "-mllvm", "-pragma-unroll-threshold=1000000",
     "-I", os.path.join(ROOT, "include"),
     "-Wall", "-Wno-unused-function",
 ]

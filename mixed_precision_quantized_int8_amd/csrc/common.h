@@ -69,6 +69,16 @@ __device__ __forceinline__ v4i buf_load16(buf_rsrc r, uint32_t off) {
 __device__ __forceinline__ uint16_t buf_load_u16(buf_rsrc r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
+__device__ __forceinline__ uint8_t buf_load_u8(buf_rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+
+// Weight value rebuilt from its int8 code when no fp16 copy is kept:
+// fp16(fl32(q * s) / 127), the product exact, one IEEE division, then round to
+// nearest even ([blog, "Usage"]: code times the output feature's scale over 127).
+__device__ __forceinline__ uint16_t dequant_w16(int q, float s) {
+  return f2h(((float)q * s) / 127.0f);
+}
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));

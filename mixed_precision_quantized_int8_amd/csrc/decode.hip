@@ -225,15 +225,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   const int found = wcount < kDecOutPre ? wcount : kDecOutPre;
   // X values (lane = row) and weight-row values (lane = feature) of the first
   // kDecOutPre outlier columns, loaded now and used after the product
+  // Without an fp16 weight (W_rows NULL) the value is rebuilt from the code
+  // Wq[n][k] and sw[n]; both loads are always issued (the unused one reads
+  // nothing), so the number of loads in flight stays fixed.
+  const bool rebuild = d.W_rows == nullptr;
+  const float swl = d.sw[n0 + lane < N ? n0 + lane : N - 1];
   uint16_t xo[kDecOutPre], wo[kDecOutPre];
+  uint8_t wc[kDecOutPre];
 #pragma unroll
   for (int j = 0; j < kDecOutPre; ++j) {
     const bool ok = j < found;
     xo[j] = buf_load_u16(rx, ok ? (uint32_t)(lane * K + ko[j]) * 2u : kBufOff);
-    const buf_rsrc ro = make_rsrc(ok ? d.W_rows + (size_t)ko[j] * N + n0 : d.W_rows,
-                                  ok ? (uint32_t)nrows * 2u : 0u);
+    const buf_rsrc ro = make_rsrc(ok && !rebuild ? d.W_rows + (size_t)ko[j] * N + n0 : d.W_rows,
+                                  ok && !rebuild ? (uint32_t)nrows * 2u : 0u);
     wo[j] = buf_load_u16(ro, (uint32_t)lane * 2u);
+    wc[j] = buf_load_u8(rw, ok && rebuild ? (uint32_t)(lane * K + ko[j]) : kBufOff);
   }
+  auto wval = [&](int j) -> float {
+    return rebuild ? h2f(dequant_w16((int)(int8_t)wc[j], swl)) : h2f(wo[j]);
+  };
 
   uint32_t rm = rmv[0] > rmv[1] ? rmv[0] : rmv[1];
 #pragma unroll
@@ -297,7 +307,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
 #pragma unroll
     for (int j = 0; j < kDecOutPre; ++j) {
       if (j < found) {
-        const float wv = h2f(wo[j]);
+        const float wv = wval(j);
 #pragma unroll
         for (int m = 0; m < 16; ++m)
           if (m < M) yo[m] += h2f((uint16_t)__builtin_amdgcn_readlane((int)xo[j], m)) * wv;
@@ -311,7 +321,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
           const int k = (s0 + s) * 64 + __builtin_ctzll(w);
           w &= w - 1;
           if (j++ < kDecOutPre) continue;
-          const float wv = n0 + lane < N ? h2f(d.W_rows[(size_t)k * N + n0 + lane]) : 0.0f;
+          float wv = 0.0f;
+          if (n0 + lane < N)
+            wv = rebuild ? h2f(dequant_w16(d.Wq[(size_t)(n0 + lane) * K + k], swl))
+                         : h2f(d.W_rows[(size_t)k * N + n0 + lane]);
           const int xv = lane < M ? (int)d.X[(size_t)lane * K + k] : 0;
 #pragma unroll
           for (int m = 0; m < 16; ++m)
@@ -448,10 +461,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
 
   const int nout = *d.n_out;
   const int n = n0 + (wave & (kDecP - 1)) * 16 + lr;
+  // outlier weight value: the fp16 row, or rebuilt from the code (W_rows NULL)
+  const float swn_raw = d.sw[n < N ? n : N - 1];
+  auto wval = [&](int k) -> float {
+    return d.W_rows ? h2f(d.W_rows[(size_t)k * N + n])
+                    : h2f(dequant_w16(d.Wq[(size_t)n * K + k], swn_raw));
+  };
   float wo[kDecOutReg];
 #pragma unroll
   for (int j = 0; j < kDecOutReg; ++j)
-    wo[j] = (wave < kDecP && j < nout && n < N) ? h2f(d.W_rows[(size_t)d.idx[j] * N + n]) : 0.0f;
+    wo[j] = (wave < kDecP && j < nout && n < N) ? wval(d.idx[j]) : 0.0f;
   const int nl = min(nout, kDecMaxOutLds);
   for (int e = t; e < nl * M; e += kDecThreads) {
     const int m = e / nl, j = e % nl;
@@ -470,7 +489,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
   }
   const int mb = (lane >> 4) * 4;
   if (n >= N || mb >= M) return;
-  const float swn = d.sw[n] * (1.0f / 16129.0f);
+  const float swn = swn_raw * (1.0f / 16129.0f);
   float y[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -485,7 +504,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
         if (mb + r < M) y[r] += sXO[mb + r][j] * wo[j];
     }
   for (int j = kDecOutReg; j < nout; ++j) {
-    const float w = h2f(d.W_rows[(size_t)d.idx[j] * N + n]);
+    const float w = wval(d.idx[j]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = mb + r;

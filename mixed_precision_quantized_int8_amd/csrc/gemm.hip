@@ -338,6 +338,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     sSx[t] = m0 + t < M ? a.sx[m0 + t] : 0.0f;
     sSw[t] = n0 + t < N ? a.sw[n0 + t] * (1.0f / 16129.0f) : 0.0f;
 
+    // fp16 bits of the outlier weight W[k][n]: the caller's fp16 row, or, with
+    // W_rows NULL, rebuilt from the code Wq[n][k] and sw[n]
+    auto wbits = [&](int k, int n) -> uint32_t {
+      return a.W_rows ? (uint32_t)a.W_rows[(size_t)k * N + n]
+                      : (uint32_t)dequant_w16(a.Wq[(size_t)n * K + k], a.sw[n]);
+    };
     // X_O[., j0 ..] and rows idx[j0 ..] of W (transposed to [column][outlier]);
     // zero past n_out and outside the matrix
     auto stage_outliers = [&](int j0) {
@@ -365,7 +371,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = j0 + c * 8 + e;
-          const uint32_t h = (j < n_out && gn < N) ? a.W_rows[(size_t)a.idx[j] * N + gn] : 0u;
+          const uint32_t h = (j < n_out && gn < N) ? wbits(a.idx[j], gn) : 0u;
           w[e >> 1] |= h << ((e & 1) * 16);
         }
         *reinterpret_cast<v4i*>(&sBo[col * kOutG + och(col, c)]) =
@@ -427,7 +433,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
               const int jj = jb + e;
               if (jj < n_out) {
                 if (gm < M) wa[e >> 1] |= (uint32_t)a.X_O[(size_t)gm * K + jj] << ((e & 1) * 16);
-                if (n < N) wb[e >> 1] |= (uint32_t)a.W_rows[(size_t)a.idx[jj] * N + n] << ((e & 1) * 16);
+                if (n < N) wb[e >> 1] |= wbits(a.idx[jj], n) << ((e & 1) * 16);
               }
             }
             const v8h fa = __builtin_bit_cast(v8h, v4i{(int)wa[0], (int)wa[1], (int)wa[2], (int)wa[3]});

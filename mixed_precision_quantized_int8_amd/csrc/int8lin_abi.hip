@@ -150,8 +150,8 @@ I8L_API i8l_status int8_linear(const uint16_t* X, int64_t M, int64_t K, const in
   REQUIRE_PTR(fn, sw, 4);
   REQUIRE_PTR(fn, Y, 16);
   REQUIRE_PTR(fn, workspace, 16);
-  if (enabled) REQUIRE_PTR(fn, W_outlier_rows, 2);
-  else if (W_outlier_rows && !aligned(W_outlier_rows, 2))
+  // NULL W_outlier_rows: the outlier rows are rebuilt from Wq and sw
+  if (W_outlier_rows && !aligned(W_outlier_rows, 2))
     return fail(I8L_ERR_INVALID_ARG, "%s: W_outlier_rows must be 2-byte aligned", fn);
   const i8l_workspace_layout L = layout_of(M, K, N);
   if (workspace_bytes < L.total)

@@ -54,7 +54,9 @@ def test_linear_validation(i8l):
     assert _linear(L, sw=None) == INVALID
     assert _linear(L, Y=None) == INVALID
     assert _linear(L, ws=None) == INVALID
-    assert _linear(L, W=None) == INVALID and "W_outlier_rows" in i8l.last_error()
+    # W_outlier_rows may be NULL (rows rebuilt from Wq, sw): a bad shape is still
+    # caught before any HIP call
+    assert _linear(L, W=None, K=8) == INVALID
     assert _linear(L, K=0) == INVALID
     assert _linear(L, K=8) == INVALID
     assert _linear(L, K=72) == INVALID
@@ -67,7 +69,7 @@ def test_linear_validation(i8l):
     assert _linear(L, X=P16 + 8) == INVALID and "aligned" in i8l.last_error()
     assert _linear(L, Y=P16 + 2) == INVALID
     assert _linear(L, sw=P16 + 2) == INVALID
-    assert _linear(L, W=P16 + 1) == INVALID
+    assert _linear(L, W=P16 + 1) == INVALID and "W_outlier_rows" in i8l.last_error()
     assert _linear(L, ws=P16 + 4) == INVALID
     need = i8l.workspace_bytes(32, 64, 32)
     assert _linear(L, wsb=need - 1) == WORKSPACE and str(need) in i8l.last_error()

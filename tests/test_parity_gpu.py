@@ -368,3 +368,38 @@ def test_linear_split_tail_sampled(lib):
     Y2 = lib.linear(Xd, Wq, sw, Wd, 6.0, workspace=ws)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(Y2).view(np.uint16), host(Y).view(np.uint16))
+
+
+# ---------------------------------------------------------------------------------
+# no fp16 weight kept: outlier rows rebuilt from the codes (W_outlier_rows NULL)
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,M,K,N,n_out", [
+    ("decode", 8, 4096, 1000, 3),            # fused decode kernel
+    ("decode_m1", 1, 1040, 300, 2),
+    ("decode_many", 4, 1024, 130, 9),        # more outliers than a wave preloads
+    ("decode_bigk", 8, 16384, 256, 4),       # activation kernels + streaming kernel
+    ("prefill", 300, 1040, 520, 5),          # GEMM, staged outlier rows
+    ("prefill_many", 70, 1024, 300, 130),    # GEMM, rows straight from memory
+    ("prefill_split", 520, 2048, 1300, 6),   # GEMM split-K tail
+])
+def test_linear_rebuilt_outlier_rows(lib, name, M, K, N, n_out):
+    say(f"int8_linear without fp16 weight: {name} M={M} K={K} N={N} n_out={n_out}")
+    X, W, _ = wl.make_small(M, K, N, seed=zlib.crc32(name.encode()) % 1000 + 7, n_out=n_out,
+                            x_sigma=1.0)
+    Xd, Wd = dev(X), dev(W)
+    Wq, sw = lib.quantize_weight(Wd)
+    del Wd
+    ws = lib.new_workspace(M, K, N, Xd.device)
+    Y = lib.linear(Xd, Wq, sw, None, 6.0, workspace=ws)
+    torch.cuda.synchronize()
+    Wq_o, sw_o = O.quantize_weight(W)
+    np.testing.assert_array_equal(host(Wq), Wq_o)
+    W_deq = O.dequantize_weight(Wq_o, sw_o)
+    r = O.int8_linear(X, Wq_o, sw_o, W_deq, 6.0)
+    assert len(r["idx"]) == n_out
+    check_workspace(lib, ws, M, K, (r["Xq"], r["sx"], r["idx"], r["X_O"]), name)
+    assert_y(host(Y), r["Y64"], r["Y"], name)
+    # and it differs from the result with the original fp16 rows only by the
+    # rebuilt weight values (a sanity check that the rebuilt path is used)
+    r16 = O.int8_linear(X, Wq_o, sw_o, W, 6.0)
+    assert not np.array_equal(r16["Y64"], r["Y64"])
