@@ -225,24 +225,27 @@ def outlier_matmul(X_O: np.ndarray, W16: np.ndarray, idx: np.ndarray) -> np.ndar
     return X_O @ WO
 
 
-def dequantize_add(acc, sx, sw, Yo):
-    """Y64 = acc * sx[i] * sw[n] / 127^2 + Yo; Y16 = fp16(Y64) (r8, r9).
+def dequantize_add(acc, sx, sw, Yo, bias=None):
+    """Y64 = acc * sx[i] * sw[n] / 127^2 + Yo (+ bias[n]); Y16 = fp16(Y64) (r8, r9).
 
     [blog, "Introduction to model quantization"]: denormalise by the outer
     product of the row and column absmax vectors (each code carries a factor
     127 / absmax, hence the 127^2).  [blog, "A gentle summary of LLM.int8()"],
-    step 3: add the outlier product.
+    step 3: add the outlier product.  [blog, "Usage"]: the 8-bit layer keeps
+    nn.Linear's bias, added to the output (before the one rounding, r8).
     """
     acc = np.asarray(acc, dtype=np.float64)
     sx = np.asarray(sx, dtype=np.float64)
     sw = np.asarray(sw, dtype=np.float64)
     Y64 = acc * np.multiply.outer(sx, sw) / float(INT8_MAX * INT8_MAX) + Yo
+    if bias is not None:
+        Y64 = Y64 + np.asarray(bias, dtype=np.float16).astype(np.float64)[None, :]
     with np.errstate(over="ignore"):
         Y16 = Y64.astype(np.float16)
     return Y64, Y16
 
 
-def int8_linear(X16, Wq, sw, W16, threshold):
+def int8_linear(X16, Wq, sw, W16, threshold, bias=None):
     """The whole LLM.int8() linear layer on the CPU.
 
     Returns a dict with every intermediate: Xq, sx, idx, X_O, acc, Yo, Y64, Y.
@@ -256,11 +259,12 @@ def int8_linear(X16, Wq, sw, W16, threshold):
         Yo = outlier_matmul(X_O, W16, idx)
     else:
         Yo = np.zeros((M, N))
-    Y64, Y = dequantize_add(acc, sx, sw, Yo)
+    Y64, Y = dequantize_add(acc, sx, sw, Yo, bias)
     return dict(Xq=Xq, sx=sx, idx=idx, X_O=X_O, acc=acc, Yo=Yo, Y64=Y64, Y=Y)
 
 
-def int8_linear_entries(X16, Wq_rows, sw_rows, W16, threshold, rows, cols, act=None):
+def int8_linear_entries(X16, Wq_rows, sw_rows, W16, threshold, rows, cols, act=None,
+                        bias=None):
     """Y64 at sampled (rows[j], cols[j]) pairs, each computed on its own.
 
     ``Wq_rows`` / ``sw_rows`` hold the quantized weight rows for ``cols`` (in the
@@ -280,6 +284,8 @@ def int8_linear_entries(X16, Wq_rows, sw_rows, W16, threshold, rows, cols, act=N
         W = np.asarray(W16, dtype=np.float16)
         WO = W[idx.astype(np.int64)][:, cols].astype(np.float64)    # [n_out][len]
         Y64 = Y64 + np.einsum("jo,oj->j", X_O[rows].astype(np.float64), WO)
+    if bias is not None:
+        Y64 = Y64 + np.asarray(bias, dtype=np.float16).astype(np.float64)[cols]
     return acc.astype(np.int32), Y64
 
 

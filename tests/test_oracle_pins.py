@@ -451,3 +451,24 @@ def test_dequantize_weight_closed_forms():
     back = O.dequantize_weight(Wq, s).astype(np.float64)
     assert np.all(np.abs(back - W0) <= s.astype(np.float64)[None, :] / 254 * 1.001
                   + np.abs(W0) * 2.0 ** -11 + 1e-8)
+
+
+def test_bias_added_before_the_single_rounding():
+    rng = np.random.default_rng(8)
+    K, N = 64, 24
+    W = (rng.standard_normal((K, N)) * 0.02).astype(np.float16)
+    b = (rng.standard_normal(N) * 3).astype(np.float16)
+    Wq, sw = O.quantize_weight(W)
+    # X = 0: every product vanishes and Y is the bias itself
+    r = O.int8_linear(np.zeros((3, K), np.float16), Wq, sw, W, 6.0, bias=b)
+    np.testing.assert_array_equal(r["Y"], np.broadcast_to(b, (3, N)))
+    # otherwise Y64 moves by exactly the bias, and Y is one rounding of the sum
+    X = (rng.standard_normal((5, K))).astype(np.float16)
+    X[:, 3] = 9.0
+    a0 = O.int8_linear(X, Wq, sw, W, 6.0)
+    a1 = O.int8_linear(X, Wq, sw, W, 6.0, bias=b)
+    np.testing.assert_allclose(a1["Y64"] - a0["Y64"], np.broadcast_to(b, (5, N)).astype(np.float64),
+                               rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(a1["Y"], a1["Y64"].astype(np.float16))
+    _, y = O.int8_linear_entries(X, Wq[[2, 7]], sw[[2, 7]], W, 6.0, [1, 4], [2, 7], bias=b)
+    np.testing.assert_allclose(y, a1["Y64"][[1, 4], [2, 7]], rtol=1e-13, atol=1e-13)
