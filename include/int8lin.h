@@ -127,6 +127,18 @@ i8l_status int8_linear(const uint16_t *X, int64_t M, int64_t K,
                        uint16_t *Y, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/* int8_linear with a bias, for a linear layer that has one ([blog, "Usage"]:
+ * the 8-bit layer takes nn.Linear's bias argument).
+ *   bias   fp16 [N], 2-byte aligned, or NULL (then identical to int8_linear);
+ *          Y = fp16(acc*sx[i]*sw[n]/127^2 + outlier product + bias[n]), the sum
+ *          formed in fp32 and rounded once.
+ * Every other argument, and every error, as for int8_linear. */
+i8l_status int8_linear_bias(const uint16_t *X, int64_t M, int64_t K,
+                            const int8_t *Wq, const float *sw, int64_t N,
+                            const uint16_t *W_outlier_rows, const uint16_t *bias,
+                            float threshold, uint16_t *Y, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
 /* Activation stage on its own ([blog, "A gentle summary of LLM.int8()"],
  * step 1, and the row-wise quantization of [blog, "A closer look at the
  * MatMul"]); the same kernels int8_linear runs for M > 16.

@@ -77,12 +77,13 @@ def new_workspace(M, K, N, device):
     return torch.empty((max(workspace_bytes(M, K, N), 1),), dtype=torch.uint8, device=device)
 
 
-def linear(X, Wq, sw, W=None, threshold=6.0, workspace=None, out=None):
+def linear(X, Wq, sw, W=None, threshold=6.0, workspace=None, out=None, bias=None):
     """LLM.int8() linear layer: X fp16 [M][K] -> Y fp16 [M][N].
 
     W (fp16 [K][N]) supplies the weight rows of the outlier columns.  With
     W None no fp16 weight is kept: those rows are rebuilt from the codes as
-    fp16(Wq[n][k] * sw[n] / 127).
+    fp16(Wq[n][k] * sw[n] / 127).  ``bias`` (fp16 [N]) is added before the
+    final rounding.
     """
     torch = _torch()
     _require(X, torch.float16, "X")
@@ -96,14 +97,19 @@ def linear(X, Wq, sw, W=None, threshold=6.0, workspace=None, out=None):
         _require(W, torch.float16, "W")
         if tuple(W.shape) != (K, N):
             raise ValueError(f"W must be [K][N] = [{K}][{N}], got {tuple(W.shape)}")
+    if bias is not None:
+        _require(bias, torch.float16, "bias")
+        if tuple(bias.shape) != (N,):
+            raise ValueError(f"bias must be [{N}], got {tuple(bias.shape)}")
     if workspace is None:
         workspace = new_workspace(M, K, N, X.device)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=X.device)
     with torch.cuda.device(X.device):
-        check(lib().int8_linear(
+        check(lib().int8_linear_bias(
             X.data_ptr(), M, K, Wq.data_ptr(), sw.data_ptr(), N,
-            W.data_ptr() if W is not None else None, float(threshold),
+            W.data_ptr() if W is not None else None,
+            bias.data_ptr() if bias is not None else None, float(threshold),
             out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(X)))
     return out
 

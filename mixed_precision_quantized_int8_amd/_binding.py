@@ -28,6 +28,7 @@ EXPORTS = (
     "i8l_linear_workspace_bytes",
     "int8_quantize_weight",
     "int8_linear",
+    "int8_linear_bias",
     "int8_quantize_activation",
     "int8_gemm_i32",
     "i8l_last_error",
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.int8_quantize_weight.restype = ctypes.c_int
     L.int8_linear.argtypes = [vp, i64, i64, vp, vp, i64, vp, f32, vp, vp, sz, vp]
     L.int8_linear.restype = ctypes.c_int
+    L.int8_linear_bias.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp, f32, vp, vp, sz, vp]
+    L.int8_linear_bias.restype = ctypes.c_int
     L.int8_quantize_activation.argtypes = [vp, i64, i64, f32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.int8_quantize_activation.restype = ctypes.c_int
     L.int8_gemm_i32.argtypes = [vp, vp, i64, i64, i64, vp, vp]

@@ -55,6 +55,7 @@ struct DecodeArgs {
   const int8_t* Wq;
   const float* sw;
   const uint16_t* W_rows;
+  const uint16_t* bias;   // fp16 [N] or NULL
   uint32_t thr;        // smallest fp16 magnitude pattern that is an outlier
                        // (0x10000 when the decomposition is off: never reached)
   uint16_t* Y;
@@ -143,6 +144,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   }
   const int ne = n0 + (wave & (kDecP - 1)) * 16 + lr;   // epilogue feature of this lane
   const float swv = d.sw[ne < N ? ne : N - 1];
+  // bias (zero-sized resource when there is none: the load reads nothing)
+  const uint16_t bvb = buf_load_u16(make_rsrc(d.bias, d.bias ? (uint32_t)N * 2u : 0u),
+                                    (uint32_t)(ne < N ? ne : N - 1) * 2u);
 
   const int nrows = N - n0 < kDecCols ? N - n0 : kDecCols;
   const buf_rsrc rw = make_rsrc(d.Wq + (size_t)n0 * K, (uint32_t)(nrows * K));
@@ -405,7 +409,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = mb + r;
-    if (m < M) d.Y[(size_t)m * N + n] = f2h((float)tot[r] * (sSx[m] * swn) + yo4[r]);
+    if (m < M) d.Y[(size_t)m * N + n] = f2h((float)tot[r] * (sSx[m] * swn) + yo4[r] + h2f(bvb));
   }
 }
 
@@ -490,6 +494,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
   const int mb = (lane >> 4) * 4;
   if (n >= N || mb >= M) return;
   const float swn = swn_raw * (1.0f / 16129.0f);
+  const float bv = d.bias ? h2f(d.bias[n]) : 0.0f;
   float y[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -514,7 +519,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = mb + r;
-    if (m < M) d.Y[(size_t)m * N + n] = f2h(y[r]);
+    if (m < M) d.Y[(size_t)m * N + n] = f2h(y[r] + bv);
   }
 }
 
@@ -542,10 +547,10 @@ uint32_t threshold_bits(float t) {
 typedef void (*kfn)(DecodeArgs);
 
 hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
-                         int N, const uint16_t* W_rows, float threshold, bool enabled,
-                         uint16_t* Y, const Workspace& ws, hipStream_t stream) {
+                         int N, const uint16_t* W_rows, const uint16_t* bias, float threshold,
+                         bool enabled, uint16_t* Y, const Workspace& ws, hipStream_t stream) {
   const uint32_t thr = enabled ? threshold_bits(threshold) : 0x10000u;
-  DecodeArgs d{X, M, K, N, Wq, sw, W_rows, thr, Y, ws.n_out, ws.idx, ws.sx, ws.Xq, ws.X_O};
+  DecodeArgs d{X, M, K, N, Wq, sw, W_rows, bias, thr, Y, ws.n_out, ws.idx, ws.sx, ws.Xq, ws.X_O};
   const dim3 grid((N + kDecCols - 1) / kDecCols), block(kDecThreads);
   if (decode_fits(M, K)) {
     const int steps = ((K + 63) / 64 + kDecWaves - 1) / kDecWaves;   // k-steps per wave

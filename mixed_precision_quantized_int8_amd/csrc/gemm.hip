@@ -332,11 +332,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     uint16_t* sBo = sAo + kBM * kOutG;                             // [256 cols][96 halves]
     float* sSx = reinterpret_cast<float*>(sBo + kBN * kOutG);      // [256]
     float* sSw = sSx + kBM;                                        // [256], includes 1/127^2
+    float* sBias = sSw + kBN;                                      // [256] (0 without bias)
     // 16-byte chunk c of staged row r sits at c ^ ((r >> 2) & 3): conflict-free
     // fragment reads with the 192-byte row stride
     auto och = [](int r, int c) { return (c ^ ((r >> 2) & 3)) << 3; };
     sSx[t] = m0 + t < M ? a.sx[m0 + t] : 0.0f;
     sSw[t] = n0 + t < N ? a.sw[n0 + t] * (1.0f / 16129.0f) : 0.0f;
+    sBias[t] = a.bias && n0 + t < N ? h2f(a.bias[n0 + t]) : 0.0f;
 
     // fp16 bits of the outlier weight W[k][n]: the caller's fp16 row, or, with
     // W_rows NULL, rebuilt from the code Wq[n][k] and sw[n]
@@ -442,10 +444,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
           }
         }
         if (n < N) {
+          const float bv = sBias[wn + j * 32 + l32];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int m = m0 + wm + i * 32 + d_row(r, lane);
-            if (m < M) a.Y[(size_t)m * N + n] = f2h(y[r]);
+            if (m < M) a.Y[(size_t)m * N + n] = f2h(y[r] + bv);
           }
         }
         __builtin_amdgcn_sched_barrier(0);   // one block at a time: bounded live ranges

@@ -135,11 +135,11 @@ I8L_API i8l_status int8_quantize_weight(const uint16_t* W, int64_t K, int64_t N,
                                                     static_cast<hipStream_t>(stream)));
 }
 
-I8L_API i8l_status int8_linear(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
-                               const float* sw, int64_t N, const uint16_t* W_outlier_rows,
-                               float threshold, uint16_t* Y, void* workspace,
-                               size_t workspace_bytes, void* stream) {
-  const char* fn = "int8_linear";
+namespace {
+i8l_status linear_impl(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
+                       const float* sw, int64_t N, const uint16_t* W_outlier_rows,
+                       const uint16_t* bias, float threshold, uint16_t* Y, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   i8l_status s = check_shape(fn, M, K, N);
   if (s != I8L_OK) return s;
   if (isnan(threshold)) return fail(I8L_ERR_INVALID_ARG, "%s: threshold is NaN", fn);
@@ -153,6 +153,8 @@ I8L_API i8l_status int8_linear(const uint16_t* X, int64_t M, int64_t K, const in
   // NULL W_outlier_rows: the outlier rows are rebuilt from Wq and sw
   if (W_outlier_rows && !aligned(W_outlier_rows, 2))
     return fail(I8L_ERR_INVALID_ARG, "%s: W_outlier_rows must be 2-byte aligned", fn);
+  if (bias && !aligned(bias, 2))
+    return fail(I8L_ERR_INVALID_ARG, "%s: bias must be 2-byte aligned", fn);
   const i8l_workspace_layout L = layout_of(M, K, N);
   if (workspace_bytes < L.total)
     return fail(I8L_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn,
@@ -162,14 +164,31 @@ I8L_API i8l_status int8_linear(const uint16_t* X, int64_t M, int64_t K, const in
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int m = (int)M, k = (int)K, n = (int)N;
   if (m <= 16) {
-    return hip_status(fn, i8l::launch_decode(X, m, k, Wq, sw, n, W_outlier_rows, threshold,
+    return hip_status(fn, i8l::launch_decode(X, m, k, Wq, sw, n, W_outlier_rows, bias, threshold,
                                              enabled, Y, w, st));
   }
   hipError_t e = i8l::launch_quantize_activation(X, m, k, threshold, enabled, w, st);
   if (e != hipSuccess) return hip_status(fn, e);
   i8l::GemmArgs g{w.Xq, Wq, m, n, k, w.sx, sw, w.n_out, w.idx, w.X_O, W_outlier_rows, Y, nullptr,
-                  w.gemm_cnt, w.gemm_part, w.gemm_slices, 0, 1};
+                  bias, w.gemm_cnt, w.gemm_part, w.gemm_slices, 0, 1};
   return hip_status(fn, i8l::launch_gemm(g, st));
+}
+}  // namespace
+
+I8L_API i8l_status int8_linear(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
+                               const float* sw, int64_t N, const uint16_t* W_outlier_rows,
+                               float threshold, uint16_t* Y, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return linear_impl("int8_linear", X, M, K, Wq, sw, N, W_outlier_rows, nullptr, threshold, Y,
+                     workspace, workspace_bytes, stream);
+}
+
+I8L_API i8l_status int8_linear_bias(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
+                                    const float* sw, int64_t N, const uint16_t* W_outlier_rows,
+                                    const uint16_t* bias, float threshold, uint16_t* Y,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_impl("int8_linear_bias", X, M, K, Wq, sw, N, W_outlier_rows, bias, threshold, Y,
+                     workspace, workspace_bytes, stream);
 }
 
 I8L_API i8l_status int8_quantize_activation(const uint16_t* X, int64_t M, int64_t K,
@@ -222,7 +241,7 @@ I8L_API i8l_status int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, 
   REQUIRE_PTR(fn, acc, 16);
   (void)hipGetLastError();
   i8l::GemmArgs g{Xq, Wq, (int)M, (int)N, (int)K, nullptr, nullptr, nullptr, nullptr,
-                  nullptr, nullptr, nullptr, acc, nullptr, nullptr, 0, 0, 1};
+                  nullptr, nullptr, nullptr, acc, nullptr, nullptr, nullptr, 0, 0, 1};
   return hip_status(fn, i8l::launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 

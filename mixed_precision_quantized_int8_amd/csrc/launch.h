@@ -58,6 +58,7 @@ struct GemmArgs {
   const uint16_t* W_rows;   // [K][N]
   uint16_t* Y;
   int32_t* acc;
+  const uint16_t* bias;   // fp16 [N] added before the final rounding, or NULL
   int32_t* cnt;      // split-K tail (Y output only): workspace counters / partials
   int32_t* part;
   int part_slices;   // 0: never split
@@ -72,8 +73,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // does the rest.
 bool decode_fits(int M, int K);
 hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
-                         int N, const uint16_t* W_rows, float threshold, bool enabled,
-                         uint16_t* Y, const Workspace& ws, hipStream_t stream);
+                         int N, const uint16_t* W_rows, const uint16_t* bias, float threshold,
+                         bool enabled, uint16_t* Y, const Workspace& ws, hipStream_t stream);
 
 const char* gemm_tile_info();
 
