@@ -139,6 +139,9 @@ def main():
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: auto, >512 MB)")
+    ap.add_argument("--rebuilt-rows", action="store_true",
+                    help="keep no fp16 weight: outlier rows rebuilt from the codes")
+    ap.add_argument("--bias", action="store_true", help="add an fp16 bias [N]")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every step from Python instead of replaying a captured graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -185,9 +188,12 @@ def main():
         Y = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
         sets.append((*s, ws, Y))
 
+    bias_t = (torch.randn(w.N, device=dev) * 0.1).half() if args.bias else None
+
     def step(i):
         x, q, s, wf, ws, y = sets[i % R]
-        pkg.linear(x, q, s, wf, w.threshold, workspace=ws, out=y)
+        pkg.linear(x, q, s, None if args.rebuilt_rows else wf, w.threshold, workspace=ws, out=y,
+                   bias=bias_t)
 
     for i in range(args.warmup):
         step(i)
@@ -288,6 +294,8 @@ def main():
         "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N,
                    "outlier_columns": w.n_out, "threshold": w.threshold,
                    "buffer_sets": R, "x_dtype": "fp16", "y_dtype": "fp16",
+                   "outlier_rows": "rebuilt from codes" if args.rebuilt_rows else "fp16 weight",
+                   "bias": bool(args.bias),
                    "launch": "eager" if args.no_graph else "hip_graph"},
         "roofline": roof,
     }
@@ -295,6 +303,9 @@ def main():
         result["eager_ms_per_step"] = round(eager_ms, 5)
 
     if not args.no_cpu_baseline:
+        if args.rebuilt_rows or args.bias:
+            raise SystemExit("the CPU baseline and parity check cover the default layer only "
+                             "(run with --no-cpu-baseline)")
         cb, ref, Wq_o, sw_o = cpu_baseline(w, X, W)
         result["cpu_baseline"] = cb
         y = sets[0][5].cpu().numpy().astype(np.float64)
