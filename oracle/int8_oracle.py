@@ -46,6 +46,15 @@ its reason in the design notes of the repository):
   r10 when no fp16 weight is kept, the outlier rows are rebuilt from the codes
       as the Usage section does, on fp32 values (code x scale, then / 127),
       and rounded to fp16 for the fp16 outlier product.
+  r11 zero-point variant (the unsigned int8 scheme of "Introduction to model
+      quantization": subtract the minimum, scale by the range, zero exact):
+      per row of X over the regular columns lo = min(0, min x), hi = max(0,
+      max x); inv = fl32(255 / fl32(hi - lo)); zp = RHAZ(fl32(-lo * inv));
+      q = clamp(RHAZ(fl32(x * inv)) + zp, 0, 255); outlier columns take q = zp;
+      the row's dequantization factor is xscale = fl32(fl32(hi - lo) / 255).
+      Codes are kept as q - 128 (int8) and the weight stays absmax per
+      column, so sum_k (q - zp) w = sum_k (q - 128) w + (128 - zp) S[n] with
+      S[n] = sum_k Wq[n][k]; K <= 66304 keeps every such sum inside int32.
 
 Layouts (row-major numpy arrays):
   X  fp16 [M][K]        W  fp16 [K][N]  (math layout, Y = X @ W)
@@ -76,6 +85,10 @@ __all__ = [
     "int8_linear_entries",
     "dequantize_weight",
     "decomposition_enabled",
+    "zero_point_codes",
+    "quantize_activation_zp",
+    "weight_code_sums",
+    "int8_linear_zp",
 ]
 
 
@@ -302,3 +315,80 @@ def dequantize_weight(Wq, sw) -> np.ndarray:
     s = np.asarray(sw, dtype=np.float32)
     prod = q * s[:, None]                       # exact: 8-bit integer x fp16 value
     return (prod / np.float32(INT8_MAX)).T.astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# Zero-point (unsigned) variant of the activation quantizer (r11)
+# ---------------------------------------------------------------------------
+UINT8_MAX = 255
+ZP_MAX_K = 66304          # 255 * 127 * K < 2^31
+
+
+def zero_point_codes(values_f32, lo_f32, hi_f32):
+    """Unsigned 8-bit codes with a zero point (r11).
+
+    [blog, "Introduction to model quantization"]: for unsigned int8 the minimum
+    is subtracted and the values scaled to the range; with the range widened
+    to contain 0, the value 0 maps to an integer (the zero point) exactly.
+    Returns (q int32 in [0, 255], zp int32, xscale fp32); broadcasts like
+    ``absmax_codes``.
+    """
+    x = np.asarray(values_f32, dtype=np.float32)
+    lo = np.minimum(np.asarray(lo_f32, dtype=np.float32), np.float32(0))
+    hi = np.maximum(np.asarray(hi_f32, dtype=np.float32), np.float32(0))
+    rng = (hi - lo).astype(np.float32)                                   # fl32
+    safe = np.where(rng > 0, rng, np.float32(1.0)).astype(np.float32)
+    inv = np.where(rng > 0, (np.float32(UINT8_MAX) / safe).astype(np.float32),
+                   np.float32(0.0)).astype(np.float32)
+    zp = rhaz((-lo * inv).astype(np.float32))
+    q = np.clip(rhaz((x * inv).astype(np.float32)) + zp, 0, UINT8_MAX)
+    xscale = (rng / np.float32(UINT8_MAX)).astype(np.float32)
+    return q.astype(np.int32), zp.astype(np.int32), xscale
+
+
+def quantize_activation_zp(X16: np.ndarray, threshold: float):
+    """Decomposition as in ``quantize_activation``, then zero-point codes per row
+    over the regular columns (r11).
+
+    Returns (Xq int8 [M][K] = q - 128 (zp - 128 in outlier columns), zp int32 [M],
+    xscale fp32 [M], idx int32 [n_out], X_O fp16 [M][n_out]).
+    """
+    X = np.asarray(X16, dtype=np.float16)
+    M, K = X.shape
+    idx = outlier_columns(X, threshold)
+    regular = np.ones(K, dtype=bool)
+    regular[idx] = False
+    Xf = X.astype(np.float32)
+    big = np.float32(np.inf)
+    lo = np.where(regular[None, :], Xf, big).min(axis=1) if K else np.zeros(M, np.float32)
+    hi = np.where(regular[None, :], Xf, -big).max(axis=1) if K else np.zeros(M, np.float32)
+    lo = np.where(np.isfinite(lo), lo, 0).astype(np.float32)       # no regular column: 0
+    hi = np.where(np.isfinite(hi), hi, 0).astype(np.float32)
+    q, zp, xscale = zero_point_codes(Xf, lo[:, None], hi[:, None])
+    zp = zp[:, 0]
+    xscale = xscale[:, 0]
+    q = np.where(regular[None, :], q, zp[:, None])
+    return (q - 128).astype(np.int8), zp.astype(np.int32), xscale, idx, X[:, idx].copy()
+
+
+def weight_code_sums(Wq) -> np.ndarray:
+    """S[n] = sum_k Wq[n, k] as int32 (r11: the zero-point correction)."""
+    return np.asarray(Wq, dtype=np.int8).astype(np.int64).sum(axis=1).astype(np.int32)
+
+
+def int8_linear_zp(X16, Wq, sw, W16, threshold, bias=None):
+    """The LLM.int8() layer with zero-point activation codes (r11):
+    Y64 = sum_k (q - zp) w * xscale[i] * sw[n] / 127 + outlier product (+ bias)."""
+    Xq, zp, xscale, idx, X_O = quantize_activation_zp(X16, threshold)
+    qd = Xq.astype(np.float64) + 128.0 - zp.astype(np.float64)[:, None]    # q - zp, exact
+    acc = qd @ np.asarray(Wq, np.int8).astype(np.float64).T                 # exact integers
+    M, N = acc.shape
+    Yo = outlier_matmul(X_O, W16, idx) if len(idx) else np.zeros((M, N))
+    Y64 = acc * np.multiply.outer(xscale.astype(np.float64),
+                                  np.asarray(sw, np.float64)) / float(INT8_MAX) + Yo
+    if bias is not None:
+        Y64 = Y64 + np.asarray(bias, dtype=np.float16).astype(np.float64)[None, :]
+    with np.errstate(over="ignore"):
+        Y = Y64.astype(np.float16)
+    return dict(Xq=Xq, zp=zp, xscale=xscale, idx=idx, X_O=X_O, acc=acc.astype(np.int64),
+                Y64=Y64, Y=Y)

@@ -472,3 +472,67 @@ def test_bias_added_before_the_single_rounding():
     np.testing.assert_array_equal(a1["Y"], a1["Y64"].astype(np.float16))
     _, y = O.int8_linear_entries(X, Wq[[2, 7]], sw[[2, 7]], W, 6.0, [1, 4], [2, 7], bias=b)
     np.testing.assert_allclose(y, a1["Y64"][[1, 4], [2, 7]], rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Zero-point variant (unsigned codes with a zero point)
+# --------------------------------------------------------------------------
+def test_zero_point_codes_closed_forms():
+    # range [-1, 1]: inv = 127.5, zp = RHAZ(127.5) = 128; 0 maps to the zero point
+    X = np.array([[-1.0, 0.5, 0.25, 1.0, 0.0]], np.float16)
+    Xq, zp, xs, idx, _ = O.quantize_activation_zp(X, 6.0)
+    q = Xq.astype(np.int32) + 128
+    assert len(idx) == 0 and zp[0] == 128
+    np.testing.assert_array_equal(q[0], [0, 192, 160, 255, 128])      # 1.0 -> 256 -> 255
+    assert xs[0] == np.float32(2.0) / np.float32(255)
+    # all-positive row: the range is widened to 0, so zp = 0
+    Xq, zp, xs, _, _ = O.quantize_activation_zp(np.array([[0.5, 2.0]], np.float16), 6.0)
+    assert zp[0] == 0
+    np.testing.assert_array_equal(Xq[0].astype(np.int32) + 128, [64, 255])
+    # zero row: every code is the zero point 0
+    Xq, zp, xs, _, _ = O.quantize_activation_zp(np.zeros((1, 4), np.float16), 6.0)
+    assert zp[0] == 0 and xs[0] == 0 and np.all(Xq == -128)
+    # outlier column: excluded from the range, its code is the zero point
+    X = np.array([[-0.5, 7.0, 1.5], [0.25, -8.0, 0.75]], np.float16)
+    Xq, zp, xs, idx, X_O = O.quantize_activation_zp(X, 6.0)
+    np.testing.assert_array_equal(idx, [1])
+    np.testing.assert_array_equal(Xq[:, 1].astype(np.int32) + 128, zp)
+    np.testing.assert_array_equal(X_O[:, 0], X[:, 1])
+    assert xs[0] == np.float32(2.0) / np.float32(255)                 # [-0.5, 1.5]
+    assert xs[1] == np.float32(0.75) / np.float32(255)                # [0, 0.75]
+
+
+def test_zero_point_round_trip_and_layer_identity():
+    rng = np.random.default_rng(17)
+    M, K, N = 6, 96, 20
+    X = (rng.standard_normal((M, K)) * 1.5 + 0.7).astype(np.float16)    # off-centre rows
+    X[:, 9] = 9.0
+    W = (rng.standard_normal((K, N)) * 0.05).astype(np.float16)
+    b = (rng.standard_normal(N)).astype(np.float16)
+    Wq, sw = O.quantize_weight(W)
+    Xq, zp, xs, idx, X_O = O.quantize_activation_zp(X, 6.0)
+    reg = np.ones(K, bool)
+    reg[idx] = False
+    deq = (Xq.astype(np.float64) + 128 - zp[:, None]) * xs.astype(np.float64)[:, None]
+    err = np.abs(deq - X.astype(np.float64))[:, reg]
+    step = np.broadcast_to(xs.astype(np.float64)[:, None], (M, K))[:, reg]
+    # q - zp is RHAZ(fl(x * inv)): half a step, plus the three fp32 roundings in
+    # inv = fl(255 / range), fl(x * inv) and xscale = fl(range / 255), each at
+    # most 2^-24 relative to |x|; where the clamp to [0, 255] bites at the ends of
+    # the range, one step more
+    ax = np.abs(X.astype(np.float64))[:, reg]
+    fp = 4 * 2.0 ** -24 * ax
+    q = Xq.astype(np.int32)[:, reg] + 128
+    inner = (q > 0) & (q < 255)
+    assert inner.sum() > 0.9 * inner.size
+    assert np.all(err[inner] <= (0.5 * step + fp)[inner])
+    assert np.all(err <= 1.5 * step + fp)
+    # signed storage: sum (q-128) w + (128 - zp) S = sum (q - zp) w, exactly
+    S = O.weight_code_sums(Wq)
+    lhs = Xq.astype(np.int64) @ Wq.astype(np.int64).T + (128 - zp.astype(np.int64))[:, None] * S
+    r = O.int8_linear_zp(X, Wq, sw, W, 6.0, bias=b)
+    np.testing.assert_array_equal(lhs, r["acc"])
+    # the layer equals the product of the dequantized operands (plus outliers, bias)
+    Wd = Wq.astype(np.float64).T * sw.astype(np.float64)[None, :] / 127
+    ref = deq[:, reg] @ Wd[reg] + X[:, idx].astype(np.float64) @ W[idx].astype(np.float64) + b
+    np.testing.assert_allclose(r["Y64"], ref, rtol=1e-12, atol=1e-12)
