@@ -59,6 +59,10 @@ typedef enum {
 /* Largest supported K (K * 127 * 127 < 2^31, rounded down to a multiple of 16). */
 #define I8L_MAX_K 133136
 
+/* Largest K of the zero-point entry points (K * 255 * 127 < 2^31, a multiple
+ * of 16): every sum_k (q - zp) * w then fits in int32. */
+#define I8L_MAX_K_ZP 66304
+
 /* Byte offsets, inside the int8_linear / int8_quantize_activation workspace, of
  * the intermediates that the call leaves there.  After an int8_linear call
  * (once the stream has reached it) the workspace holds, for that call:
@@ -69,6 +73,9 @@ typedef enum {
  *   X_outliers   fp16  [M][K] cap outlier values, element (i, j) at i*K + j,
  *                                 j < n_out, j-th outlier column in ascending order
  *   flags        uint32 [ceil(K/32)] internal: outlier column bitmask
+ *   zero_points  int32 [M]        int8_linear_zp only: the row zero points;
+ *                                 sx then holds range / 255 and Xq the codes
+ *                                 minus 128 (see int8_quantize_activation_zp)
  *   gemm_counters, gemm_partials   internal (M > 16): arrival counters and
  *                                 int32 partial tiles of the GEMM's split-K
  *                                 tail; gemm_slices partial tiles of 256x256
@@ -84,6 +91,7 @@ typedef struct {
   size_t gemm_counters;
   size_t gemm_partials;
   size_t gemm_slices;
+  size_t zero_points;
 } i8l_workspace_layout;
 
 /* Fills *layout for an int8_linear call of this shape.
@@ -161,6 +169,59 @@ i8l_status int8_quantize_activation(const uint16_t *X, int64_t M, int64_t K, flo
  *   acc  int32 [M][N]  out: acc[i][n] = sum_k Xq[i][k] * Wq[n][k] */
 i8l_status int8_gemm_i32(const int8_t *Xq, const int8_t *Wq, int64_t M, int64_t N, int64_t K,
                          int32_t *acc, void *stream);
+
+/* ---- Zero-point variant ----------------------------------------------------
+ * [blog, "Introduction to model quantization"] describes, next to absmax, the
+ * unsigned int8 scheme: subtract the minimum, scale the range onto [0, 255],
+ * and round the image of 0 to an integer, the zero point.  Here X is quantized
+ * that way per row (over the regular columns; the outlier decomposition is the
+ * same as in int8_linear) and the weight keeps its absmax codes per output
+ * feature:
+ *   lo = min(0, min_k x), hi = max(0, max_k x) over the row's regular columns,
+ *   inv = fl32(255 / fl32(hi - lo))  (0 when hi == lo),
+ *   zp = round_half_away(fl32(-lo * inv)),
+ *   q = clamp(round_half_away(fl32(x * inv)) + zp, 0, 255),
+ *   xscale = fl32(fl32(hi - lo) / 255);
+ * outlier columns take q = zp (the code of 0).  Codes are stored as q - 128
+ * (int8) so the int8 matrix cores multiply them; the layer uses
+ *   sum_k (q - zp) w = sum_k (q - 128) w + (128 - zp) S[n],  S[n] = sum_k Wq[n][k],
+ * exact in int32 for K <= I8L_MAX_K_ZP, and
+ *   Y = fp16(acc * xscale[i] * sw[n] / 127 + outlier product + bias[n]).
+ * X must be finite in its regular columns (a non-finite value there makes the
+ * codes of that row unspecified; with the decomposition on, +-inf is always an
+ * outlier). */
+
+/* S[n] = sum_k Wq[n][k] (int32), the per-output correction term of the
+ * zero-point variant; computed once per layer, like the weight codes.
+ *   Wq  int8 [N][K]  16-byte aligned, read only
+ *   S   int32 [N]    out, 4-byte aligned
+ * Shape rules as for int8_quantize_weight. */
+i8l_status int8_weight_code_sums(const int8_t *Wq, int64_t N, int64_t K, int32_t *S,
+                                 void *stream);
+
+/* The layer with zero-point activation codes (see above).
+ *   wsum   int32 [N] from int8_weight_code_sums for this Wq, 4-byte aligned
+ * Every other argument, the workspace size and the errors as for
+ * int8_linear_bias; in addition K > I8L_MAX_K_ZP gives I8L_ERR_K_TOO_LARGE.
+ * Afterwards the workspace holds Xq (q - 128), sx (xscale), zero_points, the
+ * outlier list and X_outliers of this call. */
+i8l_status int8_linear_zp(const uint16_t *X, int64_t M, int64_t K,
+                          const int8_t *Wq, const float *sw, const int32_t *wsum, int64_t N,
+                          const uint16_t *W_outlier_rows, const uint16_t *bias,
+                          float threshold, uint16_t *Y, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* Activation stage of the zero-point variant on its own.
+ *   Xq      int8 [M][K]  out: q - 128, zp - 128 in outlier columns
+ *   zp      int32 [M]    out: zero points in [0, 255]
+ *   xscale  fp32 [M]     out: fl32(range / 255)
+ * Other arguments, alignment, workspace and errors as for
+ * int8_quantize_activation; K > I8L_MAX_K_ZP gives I8L_ERR_K_TOO_LARGE. */
+i8l_status int8_quantize_activation_zp(const uint16_t *X, int64_t M, int64_t K, float threshold,
+                                       int8_t *Xq, int32_t *zp, float *xscale,
+                                       int32_t *outlier_idx, int32_t *n_outliers,
+                                       uint16_t *X_outliers, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *i8l_last_error(void);

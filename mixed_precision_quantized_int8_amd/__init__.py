@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     Int8LinError,
     MAX_K,
+    MAX_K_ZP,
     build_info,
     check,
     last_error,
@@ -26,6 +27,9 @@ __all__ = [
     "linear",
     "quantize_activation",
     "gemm_i32",
+    "weight_code_sums",
+    "linear_zp",
+    "quantize_activation_zp",
     "workspace_layout",
     "workspace_bytes",
     "workspace_views",
@@ -77,14 +81,7 @@ def new_workspace(M, K, N, device):
     return torch.empty((max(workspace_bytes(M, K, N), 1),), dtype=torch.uint8, device=device)
 
 
-def linear(X, Wq, sw, W=None, threshold=6.0, workspace=None, out=None, bias=None):
-    """LLM.int8() linear layer: X fp16 [M][K] -> Y fp16 [M][N].
-
-    W (fp16 [K][N]) supplies the weight rows of the outlier columns.  With
-    W None no fp16 weight is kept: those rows are rebuilt from the codes as
-    fp16(Wq[n][k] * sw[n] / 127).  ``bias`` (fp16 [N]) is added before the
-    final rounding.
-    """
+def _linear_args(X, Wq, sw, W, bias, workspace, out):
     torch = _torch()
     _require(X, torch.float16, "X")
     _require(Wq, torch.int8, "Wq")
@@ -105,9 +102,52 @@ def linear(X, Wq, sw, W=None, threshold=6.0, workspace=None, out=None, bias=None
         workspace = new_workspace(M, K, N, X.device)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    return M, K, N, workspace, out
+
+
+def linear(X, Wq, sw, W=None, threshold=6.0, workspace=None, out=None, bias=None):
+    """LLM.int8() linear layer: X fp16 [M][K] -> Y fp16 [M][N].
+
+    W (fp16 [K][N]) supplies the weight rows of the outlier columns.  With
+    W None no fp16 weight is kept: those rows are rebuilt from the codes as
+    fp16(Wq[n][k] * sw[n] / 127).  ``bias`` (fp16 [N]) is added before the
+    final rounding.
+    """
+    torch = _torch()
+    M, K, N, workspace, out = _linear_args(X, Wq, sw, W, bias, workspace, out)
     with torch.cuda.device(X.device):
         check(lib().int8_linear_bias(
             X.data_ptr(), M, K, Wq.data_ptr(), sw.data_ptr(), N,
+            W.data_ptr() if W is not None else None,
+            bias.data_ptr() if bias is not None else None, float(threshold),
+            out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(X)))
+    return out
+
+
+def weight_code_sums(Wq, out=None):
+    """Wq int8 [N][K] -> S int32 [N], S[n] = sum_k Wq[n][k] (zero-point variant)."""
+    torch = _torch()
+    _require(Wq, torch.int8, "Wq")
+    N, K = Wq.shape
+    if out is None:
+        out = torch.empty((N,), dtype=torch.int32, device=Wq.device)
+    with torch.cuda.device(Wq.device):
+        check(lib().int8_weight_code_sums(Wq.data_ptr(), N, K, out.data_ptr(), _stream(Wq)))
+    return out
+
+
+def linear_zp(X, Wq, sw, wsum, W=None, threshold=6.0, workspace=None, out=None, bias=None):
+    """The layer with zero-point (unsigned) activation codes per row of X; the
+    weight keeps its absmax codes.  ``wsum`` comes from ``weight_code_sums(Wq)``;
+    the other arguments as for ``linear``."""
+    torch = _torch()
+    M, K, N, workspace, out = _linear_args(X, Wq, sw, W, bias, workspace, out)
+    _require(wsum, torch.int32, "wsum")
+    if tuple(wsum.shape) != (N,):
+        raise ValueError(f"wsum must be [{N}], got {tuple(wsum.shape)}")
+    with torch.cuda.device(X.device):
+        check(lib().int8_linear_zp(
+            X.data_ptr(), M, K, Wq.data_ptr(), sw.data_ptr(), wsum.data_ptr(), N,
             W.data_ptr() if W is not None else None,
             bias.data_ptr() if bias is not None else None, float(threshold),
             out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(X)))
@@ -124,6 +164,7 @@ def workspace_views(workspace, M, K):
         return b[off:off + nbytes].view(dtype).view(shape)
 
     return {
+        "zp": view(L["zero_points"], 4 * M, torch.int32, (M,)),
         "n_out": view(L["n_outliers"], 4, torch.int32, (1,)),
         "idx": view(L["outlier_idx"], 4 * K, torch.int32, (K,)),
         "sx": view(L["sx"], 4 * M, torch.float32, (M,)),
@@ -151,6 +192,29 @@ def quantize_activation(X, threshold=6.0, workspace=None):
             X.data_ptr(), M, K, float(threshold), Xq.data_ptr(), sx.data_ptr(), idx.data_ptr(),
             n_out.data_ptr(), X_O.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(X)))
     return {"Xq": Xq, "sx": sx, "idx": idx, "n_out": n_out, "X_O": X_O}
+
+
+def quantize_activation_zp(X, threshold=6.0, workspace=None):
+    """Zero-point activation stage alone: dict of Xq [M][K] (codes - 128), zp [M],
+    xscale [M], idx [K] (first n_out valid), n_out [1], X_O [M][K]."""
+    torch = _torch()
+    _require(X, torch.float16, "X")
+    M, K = X.shape
+    dev = X.device
+    Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    zp = torch.empty((M,), dtype=torch.int32, device=dev)
+    xscale = torch.empty((M,), dtype=torch.float32, device=dev)
+    idx = torch.empty((K,), dtype=torch.int32, device=dev)
+    n_out = torch.empty((1,), dtype=torch.int32, device=dev)
+    X_O = torch.empty((M, K), dtype=torch.float16, device=dev)
+    if workspace is None:
+        workspace = new_workspace(M, K, 0, dev)
+    with torch.cuda.device(dev):
+        check(lib().int8_quantize_activation_zp(
+            X.data_ptr(), M, K, float(threshold), Xq.data_ptr(), zp.data_ptr(), xscale.data_ptr(),
+            idx.data_ptr(), n_out.data_ptr(), X_O.data_ptr(), workspace.data_ptr(),
+            workspace.numel(), _stream(X)))
+    return {"Xq": Xq, "zp": zp, "xscale": xscale, "idx": idx, "n_out": n_out, "X_O": X_O}
 
 
 def gemm_i32(Xq, Wq):

@@ -21,6 +21,7 @@ STATUS_NAMES = {
     4: "I8L_ERR_HIP",
 }
 MAX_K = 133136
+MAX_K_ZP = 66304
 
 # Every symbol include/int8lin.h declares.
 EXPORTS = (
@@ -31,6 +32,9 @@ EXPORTS = (
     "int8_linear_bias",
     "int8_quantize_activation",
     "int8_gemm_i32",
+    "int8_weight_code_sums",
+    "int8_linear_zp",
+    "int8_quantize_activation_zp",
     "i8l_last_error",
     "i8l_build_info",
 )
@@ -54,6 +58,7 @@ class WorkspaceLayout(ctypes.Structure):
         ("gemm_counters", ctypes.c_size_t),
         ("gemm_partials", ctypes.c_size_t),
         ("gemm_slices", ctypes.c_size_t),
+        ("zero_points", ctypes.c_size_t),
     ]
 
 
@@ -86,6 +91,13 @@ def lib() -> ctypes.CDLL:
     L.int8_quantize_activation.restype = ctypes.c_int
     L.int8_gemm_i32.argtypes = [vp, vp, i64, i64, i64, vp, vp]
     L.int8_gemm_i32.restype = ctypes.c_int
+    L.int8_weight_code_sums.argtypes = [vp, i64, i64, vp, vp]
+    L.int8_weight_code_sums.restype = ctypes.c_int
+    L.int8_linear_zp.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, vp, f32, vp, vp, sz, vp]
+    L.int8_linear_zp.restype = ctypes.c_int
+    L.int8_quantize_activation_zp.argtypes = [vp, i64, i64, f32, vp, vp, vp, vp, vp, vp, vp, sz,
+                                              vp]
+    L.int8_quantize_activation_zp.restype = ctypes.c_int
     L.i8l_last_error.argtypes = []
     L.i8l_last_error.restype = ctypes.c_char_p
     L.i8l_build_info.argtypes = []

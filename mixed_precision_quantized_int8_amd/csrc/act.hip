@@ -17,6 +17,13 @@
 //             regular columns is reduced, then codes are written (8 bytes per
 //             thread, coalesced) and outlier values are scattered to X_O at
 //             their rank; workgroup 0 also writes the ascending index list.
+// Zero-point mode of rowquant ([blog, "Introduction to model quantization"],
+// the unsigned scheme): the row's minimum and maximum over the regular columns,
+// widened to contain 0, give inv = fl32(255 / range) and the zero point
+// zp = round_half_away(-min * inv); codes are clamp(round_half_away(x * inv) +
+// zp, 0, 255), stored as code - 128 so the int8 matrix cores can take them;
+// outlier columns store zp - 128 (the code of 0).  The row writes
+// fl32(range / 255) to sx and zp to the zero-point array.
 // The column dependency (every row must be seen before any row scale) is why
 // X is read twice; the second read is one coalesced pass per row.
 #include "common.h"
@@ -111,11 +118,18 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
 
 constexpr int kMaxFlagWords = (I8L_MAX_K_DEV + 31) / 32;
 
+__device__ __forceinline__ float wave_min(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = __builtin_fminf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
 // One workgroup per row of X.  NCH 16-byte chunks per thread: K <= BS * 8 * NCH.
-template <int BS, int NCH>
+// ZP: zero-point codes (zp != nullptr) instead of absmax codes.
+template <int BS, int NCH, bool ZP>
 __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                      const uint32_t* __restrict__ flags,
                                                      int8_t* __restrict__ Xq, float* __restrict__ sx,
+                                                     int32_t* __restrict__ zp,
                                                      int32_t* __restrict__ idx,
                                                      int32_t* __restrict__ n_out,
                                                      uint16_t* __restrict__ X_O) {
@@ -123,6 +137,7 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
   __shared__ int s_rank[kMaxFlagWords];
   __shared__ int s_tmp[BS / 64 + 1];
   __shared__ uint32_t s_max[BS / 64];
+  __shared__ float s_lo[ZP ? BS / 64 : 1], s_hi[ZP ? BS / 64 : 1];
 
   const int t = threadIdx.x;
   const int row = blockIdx.x;
@@ -156,6 +171,7 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
     else raw[j] = v4i{0, 0, 0, 0};
   }
   uint32_t mx = 0;
+  float lo = 0.0f, hi = 0.0f;   // zero-point mode: the range always contains 0
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int q = t + j * BS;
@@ -163,19 +179,49 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
       const uint32_t ob = (s_flags[q >> 2] >> ((q & 3) * 8)) & 0xffu;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t h = ((uint32_t)raw[j][e >> 1] >> ((e & 1) * 16)) & 0x7fffu;
-        if (!((ob >> e) & 1u)) mx = h > mx ? h : mx;
+        const uint32_t hb = ((uint32_t)raw[j][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        if (!((ob >> e) & 1u)) {
+          if constexpr (ZP) {
+            const float x = h2f((uint16_t)hb);
+            lo = __builtin_fminf(lo, x);
+            hi = __builtin_fmaxf(hi, x);
+          } else {
+            const uint32_t h = hb & 0x7fffu;
+            mx = h > mx ? h : mx;
+          }
+        }
       }
     }
   }
-  mx = wave_max_u32(mx);
-  if ((t & 63) == 0) s_max[t >> 6] = mx;
-  __syncthreads();
-  mx = 0;
+  float inv, scale;
+  int zpv = 0;
+  if constexpr (ZP) {
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if ((t & 63) == 0) {
+      s_lo[t >> 6] = lo;
+      s_hi[t >> 6] = hi;
+    }
+    __syncthreads();
 #pragma unroll
-  for (int w = 0; w < BS / 64; ++w) mx = s_max[w] > mx ? s_max[w] : mx;
-  const float amax = h2f((uint16_t)mx);
-  const float inv = quant_scale(amax);
+    for (int w = 0; w < BS / 64; ++w) {
+      lo = __builtin_fminf(lo, s_lo[w]);
+      hi = __builtin_fmaxf(hi, s_hi[w]);
+    }
+    const float range = hi - lo;
+    inv = range > 0.0f ? 255.0f / range : 0.0f;
+    zpv = (int)__builtin_roundf(-lo * inv);
+    scale = range / 255.0f;
+  } else {
+    mx = wave_max_u32(mx);
+    if ((t & 63) == 0) s_max[t >> 6] = mx;
+    __syncthreads();
+    mx = 0;
+#pragma unroll
+    for (int w = 0; w < BS / 64; ++w) mx = s_max[w] > mx ? s_max[w] : mx;
+    scale = h2f((uint16_t)mx);
+    inv = quant_scale(scale);
+  }
 
   int8_t* qr = Xq + (size_t)row * K;
   uint16_t* orow = X_O + (size_t)row * K;
@@ -190,7 +236,13 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint16_t hb = (uint16_t)(((uint32_t)raw[j][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-        code[e] = ((ob >> e) & 1u) ? 0 : quant_code(h2f(hb), inv);
+        if constexpr (ZP) {
+          int c = ((ob >> e) & 1u) ? zpv : (int)__builtin_roundf(h2f(hb) * inv) + zpv;
+          c = c < 0 ? 0 : (c > 255 ? 255 : c);
+          code[e] = c - 128;
+        } else {
+          code[e] = ((ob >> e) & 1u) ? 0 : quant_code(h2f(hb), inv);
+        }
       }
       v2i packed = {(int)pack4_i8(code[0], code[1], code[2], code[3]),
                     (int)pack4_i8(code[4], code[5], code[6], code[7])};
@@ -209,7 +261,10 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
       }
     }
   }
-  if (t == 0) sx[row] = amax;
+  if (t == 0) {
+    sx[row] = scale;
+    if constexpr (ZP) zp[row] = zpv;
+  }
 
   if (row == 0) {
     for (int w = t; w < nw; w += BS) {
@@ -226,14 +281,20 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
 }
 
 template <int BS, int NCH>
-static void launch_rowquant(const uint16_t* X, int M, int K, const Workspace& ws,
+static void launch_rowquant(const uint16_t* X, int M, int K, bool zp, const Workspace& ws,
                             hipStream_t stream) {
-  hipLaunchKernelGGL((rowquant_kernel<BS, NCH>), dim3(M), dim3(BS), 0, stream, X, M, K,
-                     (const uint32_t*)ws.flags, ws.Xq, ws.sx, ws.idx, ws.n_out, ws.X_O);
+  if (zp)
+    hipLaunchKernelGGL((rowquant_kernel<BS, NCH, true>), dim3(M), dim3(BS), 0, stream, X, M, K,
+                       (const uint32_t*)ws.flags, ws.Xq, ws.sx, ws.zp, ws.idx, ws.n_out, ws.X_O);
+  else
+    hipLaunchKernelGGL((rowquant_kernel<BS, NCH, false>), dim3(M), dim3(BS), 0, stream, X, M, K,
+                       (const uint32_t*)ws.flags, ws.Xq, ws.sx, nullptr, ws.idx, ws.n_out,
+                       ws.X_O);
 }
 
 hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float threshold,
-                                      bool enabled, const Workspace& ws, hipStream_t stream) {
+                                      bool enabled, const Workspace& ws, hipStream_t stream,
+                                      bool zp) {
   const int nw = (K + 31) / 32;
   launch_fill_u32(ws.flags, nw, 0u, stream);
   if (enabled && M > 0) {
@@ -247,13 +308,13 @@ hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float thr
   }
   if (M > 0) {
     const int nch256 = (K / 8 + 255) / 256;
-    if (nch256 <= 1) launch_rowquant<256, 1>(X, M, K, ws, stream);
-    else if (nch256 <= 2) launch_rowquant<256, 2>(X, M, K, ws, stream);
-    else if (nch256 <= 4) launch_rowquant<256, 4>(X, M, K, ws, stream);
-    else if (nch256 <= 8) launch_rowquant<256, 8>(X, M, K, ws, stream);
-    else if (nch256 <= 16) launch_rowquant<256, 16>(X, M, K, ws, stream);
-    else if (nch256 <= 32) launch_rowquant<256, 32>(X, M, K, ws, stream);
-    else launch_rowquant<1024, 17>(X, M, K, ws, stream);
+    if (nch256 <= 1) launch_rowquant<256, 1>(X, M, K, zp, ws, stream);
+    else if (nch256 <= 2) launch_rowquant<256, 2>(X, M, K, zp, ws, stream);
+    else if (nch256 <= 4) launch_rowquant<256, 4>(X, M, K, zp, ws, stream);
+    else if (nch256 <= 8) launch_rowquant<256, 8>(X, M, K, zp, ws, stream);
+    else if (nch256 <= 16) launch_rowquant<256, 16>(X, M, K, zp, ws, stream);
+    else if (nch256 <= 32) launch_rowquant<256, 32>(X, M, K, zp, ws, stream);
+    else launch_rowquant<1024, 17>(X, M, K, zp, ws, stream);
   }
   return hipGetLastError();
 }

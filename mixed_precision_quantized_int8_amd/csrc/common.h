@@ -66,6 +66,9 @@ template <int AUX = 0>
 __device__ __forceinline__ v4i buf_load16(buf_rsrc r, uint32_t off) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
 }
+__device__ __forceinline__ uint32_t buf_load_u32(buf_rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
 __device__ __forceinline__ uint16_t buf_load_u16(buf_rsrc r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }

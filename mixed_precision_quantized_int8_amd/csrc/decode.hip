@@ -27,8 +27,10 @@
 // Workgroup 0 also writes the intermediates (Xq, sx, outlier list, X_O) to the
 // workspace.
 //
-// Stream kernel (larger K): reads the intermediates written by the activation
-// kernels and does the product and epilogue the same way.
+// Stream kernel (larger K, and the zero-point mode): reads the intermediates
+// written by the activation kernels and does the product and epilogue the same
+// way; in zero-point mode the accumulator is corrected by (128 - zp[m]) * wsum[n]
+// and dequantized with sx * sw / 127.
 #include <cmath>
 
 #include "common.h"
@@ -64,6 +66,8 @@ struct DecodeArgs {
   float* sx;
   int8_t* Xq;
   uint16_t* X_O;
+  const int32_t* zp = nullptr;     // zero-point mode (stream kernel only)
+  const int32_t* wsum = nullptr;
 };
 
 bool decode_fits(int M, int K) { return M >= 1 && M <= 16 && K <= kDecWaves * kDecMaxKS * 64; }
@@ -493,8 +497,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
   }
   const int mb = (lane >> 4) * 4;
   if (n >= N || mb >= M) return;
-  const float swn = swn_raw * (1.0f / 16129.0f);
+  const float swn = swn_raw * (d.zp ? 1.0f / 127.0f : 1.0f / 16129.0f);
   const float bv = d.bias ? h2f(d.bias[n]) : 0.0f;
+  if (d.zp) {   // sum (q - zp) w = sum (q - 128) w + (128 - zp) S[n], mod 2^32
+    const uint32_t wsv = (uint32_t)d.wsum[n];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (mb + r < M) tot[r] = (int)((uint32_t)tot[r] + (uint32_t)(128 - d.zp[mb + r]) * wsv);
+  }
   float y[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -568,6 +578,20 @@ hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, cons
   hipError_t e = launch_quantize_activation(X, M, K, threshold, enabled, ws, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_stream_kernel, grid, block, 0, stream, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_zp(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
+                            const int32_t* wsum, int N, const uint16_t* W_rows,
+                            const uint16_t* bias, float threshold, bool enabled, uint16_t* Y,
+                            const Workspace& ws, hipStream_t stream) {
+  const uint32_t thr = enabled ? threshold_bits(threshold) : 0x10000u;
+  DecodeArgs d{X, M, K, N, Wq, sw, W_rows, bias, thr, Y, ws.n_out, ws.idx, ws.sx, ws.Xq, ws.X_O,
+               ws.zp, wsum};
+  hipError_t e = launch_quantize_activation(X, M, K, threshold, enabled, ws, stream, true);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_stream_kernel, dim3((N + kDecCols - 1) / kDecCols), dim3(kDecThreads),
+                     0, stream, d);
   return hipGetLastError();
 }
 

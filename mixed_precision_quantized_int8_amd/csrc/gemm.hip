@@ -42,6 +42,10 @@
 // With at most 32 outlier columns the staging happens once per tile.  The
 // outlier count is read from device memory, so no host synchronization is
 // needed.
+// Zero-point mode (ZP): Xq holds unsigned codes minus 128 and sx the row's
+// range / 255; the int32 block gets (128 - zp[m]) * wsum[n] added (exact in
+// int32 arithmetic, wrap-around included, for K within the zero-point limit)
+// before the dequantization by sx * sw / 127.
 #include <algorithm>
 
 #include "common.h"
@@ -105,8 +109,8 @@ __device__ __forceinline__ int d_row(int r, int lane) {
 
 // SPLIT: the workgroups are the split tiles of the tail (S per tile), each on
 // its own range of k-steps; a separate instantiation, so that the whole-tile
-// kernel carries none of the split bookkeeping.
-template <bool OUT_I32, bool SPLIT>
+// kernel carries none of the split bookkeeping.  ZP: zero-point epilogue.
+template <bool OUT_I32, bool SPLIT, bool ZP>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   // kStages ring buffers of [A 256 x 64 | B 256 x 64] bytes
   __shared__ __attribute__((aligned(1024))) int8_t smem[kStages][2][kBM * kBK];
@@ -198,6 +202,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
+  if constexpr (ZP && !SPLIT) {
+    // Zero-point correction as the accumulators' starting value: the MFMAs then
+    // add sum_k (q - 128) w on top.  Every prefix sum stays within
+    // 255 * 127 * K < 2^31 in magnitude, so nothing wraps.  Rows past M read 0
+    // from the buffer resource (never stored).
+    const buf_rsrc rz = make_rsrc(a.zp, (uint32_t)M * 4u);
+    uint32_t wsv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + j * 32 + l32;
+      wsv[j] = n < N ? (uint32_t)a.wsum[n] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {   // one dword per row: each load wholly in or out
+        const uint32_t z = buf_load_u32(rz, (uint32_t)(m0 + wm + i * 32 + d_row(r, lane)) * 4u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j][r] = (int)((128u - z) * wsv[j]);
+      }
+  }
   auto mfma_one = [&](const v4i (&fa)[4], const v4i (&fb)[4], int q) {
     const int i = q & 3, j = q >> 2;
     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
@@ -333,12 +358,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     float* sSx = reinterpret_cast<float*>(sBo + kBN * kOutG);      // [256]
     float* sSw = sSx + kBM;                                        // [256], includes 1/127^2
     float* sBias = sSw + kBN;                                      // [256] (0 without bias)
+    int* sZc = reinterpret_cast<int*>(sBias + kBN);                // [256] 128 - zp (ZP)
+    int* sWs = sZc + kBM;                                          // [256] wsum (ZP)
     // 16-byte chunk c of staged row r sits at c ^ ((r >> 2) & 3): conflict-free
     // fragment reads with the 192-byte row stride
     auto och = [](int r, int c) { return (c ^ ((r >> 2) & 3)) << 3; };
     sSx[t] = m0 + t < M ? a.sx[m0 + t] : 0.0f;
-    sSw[t] = n0 + t < N ? a.sw[n0 + t] * (1.0f / 16129.0f) : 0.0f;
+    sSw[t] = n0 + t < N ? a.sw[n0 + t] * (ZP ? 1.0f / 127.0f : 1.0f / 16129.0f) : 0.0f;
     sBias[t] = a.bias && n0 + t < N ? h2f(a.bias[n0 + t]) : 0.0f;
+    if constexpr (ZP) {
+      sZc[t] = m0 + t < M ? 128 - a.zp[m0 + t] : 0;
+      sWs[t] = n0 + t < N ? a.wsum[n0 + t] : 0;
+    }
 
     // fp16 bits of the outlier weight W[k][n]: the caller's fp16 row, or, with
     // W_rows NULL, rebuilt from the code Wq[n][k] and sw[n]
@@ -411,6 +442,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) tot[r] = acc[i][j][r];
+        }
+        if constexpr (ZP && SPLIT) {   // sum (q - zp) w = sum (q - 128) w + (128 - zp) S[n], mod 2^32
+          const uint32_t wsv = (uint32_t)sWs[wn + j * 32 + l32];
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            tot[r] = (int)((uint32_t)tot[r] + (uint32_t)sZc[wm + i * 32 + d_row(r, lane)] * wsv);
         }
         v16f y;
 #pragma unroll
@@ -503,17 +540,28 @@ hipError_t launch_gemm(const GemmArgs& in, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (a.acc) {
-    hipLaunchKernelGGL((gemm_i8_kernel<true, false>), dim3(p.full_tiles), dim3(kGemmThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((gemm_i8_kernel<true, false, false>), dim3(p.full_tiles),
+                       dim3(kGemmThreads), 0, stream, a);
     return hipGetLastError();
   }
   // whole tiles, then the split tail (both launches fill the chip)
-  if (p.full_tiles > 0)
-    hipLaunchKernelGGL((gemm_i8_kernel<false, false>), dim3(p.full_tiles), dim3(kGemmThreads), 0,
-                       stream, a);
-  if (p.split_tiles > 0)
-    hipLaunchKernelGGL((gemm_i8_kernel<false, true>), dim3(p.split_tiles * p.S),
-                       dim3(kGemmThreads), 0, stream, a);
+  const bool zp = a.zp != nullptr;
+  if (p.full_tiles > 0) {
+    if (zp)
+      hipLaunchKernelGGL((gemm_i8_kernel<false, false, true>), dim3(p.full_tiles),
+                         dim3(kGemmThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_i8_kernel<false, false, false>), dim3(p.full_tiles),
+                         dim3(kGemmThreads), 0, stream, a);
+  }
+  if (p.split_tiles > 0) {
+    if (zp)
+      hipLaunchKernelGGL((gemm_i8_kernel<false, true, true>), dim3(p.split_tiles * p.S),
+                         dim3(kGemmThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_i8_kernel<false, true, false>), dim3(p.split_tiles * p.S),
+                         dim3(kGemmThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -55,6 +55,14 @@ i8l_status check_shape(const char* fn, int64_t M, int64_t K, int64_t N) {
   return I8L_OK;
 }
 
+i8l_status check_zp_k(const char* fn, int64_t K) {
+  if (K > I8L_MAX_K_ZP)
+    return fail(I8L_ERR_K_TOO_LARGE,
+                "%s: K=%lld exceeds %d for zero-point codes (K*255*127 must fit in int32)", fn,
+                (long long)K, I8L_MAX_K_ZP);
+  return I8L_OK;
+}
+
 // The GEMM's split-K tail (M > 16) needs arrival counters and int32 partial
 // tiles; they are sized for a device with up to kGemmMaxSlices compute units.
 i8l_workspace_layout layout_of(int64_t M, int64_t K, int64_t N) {
@@ -66,6 +74,8 @@ i8l_workspace_layout layout_of(int64_t M, int64_t K, int64_t N) {
   L.flags = off; off += up((size_t)((K + 31) / 32) * sizeof(uint32_t));
   L.Xq = off; off += up((size_t)M * (size_t)K);
   L.X_outliers = off; off += up((size_t)M * (size_t)K * sizeof(uint16_t));
+  // before the GEMM's part, so that its offset does not depend on N
+  L.zero_points = off; off += up((size_t)M * sizeof(int32_t));
   int slices = 0;
   if (M > 16 && N > 0) {
     const i8l::GemmSplit p = i8l::gemm_split_plan((int)M, (int)N, (int)K, i8l::kGemmMaxSlices);
@@ -90,6 +100,7 @@ i8l::Workspace carve(void* ws, const i8l_workspace_layout& L) {
   w.gemm_cnt = reinterpret_cast<int32_t*>(b + L.gemm_counters);
   w.gemm_part = reinterpret_cast<int32_t*>(b + L.gemm_partials);
   w.gemm_slices = (int)L.gemm_slices;
+  w.zp = reinterpret_cast<int32_t*>(b + L.zero_points);
   return w;
 }
 
@@ -135,19 +146,36 @@ I8L_API i8l_status int8_quantize_weight(const uint16_t* W, int64_t K, int64_t N,
                                                     static_cast<hipStream_t>(stream)));
 }
 
+I8L_API i8l_status int8_weight_code_sums(const int8_t* Wq, int64_t N, int64_t K, int32_t* S,
+                                        void* stream) {
+  const char* fn = "int8_weight_code_sums";
+  i8l_status s = check_shape(fn, 0, K, N);
+  if (s != I8L_OK) return s;
+  if (N == 0) return ok();
+  REQUIRE_PTR(fn, Wq, 16);
+  REQUIRE_PTR(fn, S, 4);
+  (void)hipGetLastError();
+  return hip_status(fn, i8l::launch_weight_code_sums(Wq, (int)N, (int)K, S,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 namespace {
+// zp: zero-point codes for X and the corrected epilogue (wsum required).
 i8l_status linear_impl(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
-                       const float* sw, int64_t N, const uint16_t* W_outlier_rows,
-                       const uint16_t* bias, float threshold, uint16_t* Y, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       const float* sw, const int32_t* wsum, int64_t N,
+                       const uint16_t* W_outlier_rows, const uint16_t* bias, float threshold,
+                       uint16_t* Y, void* workspace, size_t workspace_bytes, void* stream,
+                       bool zp) {
   i8l_status s = check_shape(fn, M, K, N);
   if (s != I8L_OK) return s;
+  if (zp && (s = check_zp_k(fn, K)) != I8L_OK) return s;
   if (isnan(threshold)) return fail(I8L_ERR_INVALID_ARG, "%s: threshold is NaN", fn);
   const bool enabled = threshold > 0.0f && isfinite(threshold);
   if (M == 0 || N == 0) return ok();   // nothing to read or write
   REQUIRE_PTR(fn, X, 16);
   REQUIRE_PTR(fn, Wq, 16);
   REQUIRE_PTR(fn, sw, 4);
+  if (zp) REQUIRE_PTR(fn, wsum, 4);
   REQUIRE_PTR(fn, Y, 16);
   REQUIRE_PTR(fn, workspace, 16);
   // NULL W_outlier_rows: the outlier rows are rebuilt from Wq and sw
@@ -164,13 +192,17 @@ i8l_status linear_impl(const char* fn, const uint16_t* X, int64_t M, int64_t K, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int m = (int)M, k = (int)K, n = (int)N;
   if (m <= 16) {
+    if (zp)
+      return hip_status(fn, i8l::launch_decode_zp(X, m, k, Wq, sw, wsum, n, W_outlier_rows, bias,
+                                                  threshold, enabled, Y, w, st));
     return hip_status(fn, i8l::launch_decode(X, m, k, Wq, sw, n, W_outlier_rows, bias, threshold,
                                              enabled, Y, w, st));
   }
-  hipError_t e = i8l::launch_quantize_activation(X, m, k, threshold, enabled, w, st);
+  hipError_t e = i8l::launch_quantize_activation(X, m, k, threshold, enabled, w, st, zp);
   if (e != hipSuccess) return hip_status(fn, e);
   i8l::GemmArgs g{w.Xq, Wq, m, n, k, w.sx, sw, w.n_out, w.idx, w.X_O, W_outlier_rows, Y, nullptr,
-                  bias, w.gemm_cnt, w.gemm_part, w.gemm_slices, 0, 1};
+                  bias, zp ? w.zp : nullptr, zp ? wsum : nullptr, w.gemm_cnt, w.gemm_part,
+                  w.gemm_slices, 0, 1};
   return hip_status(fn, i8l::launch_gemm(g, st));
 }
 }  // namespace
@@ -179,26 +211,37 @@ I8L_API i8l_status int8_linear(const uint16_t* X, int64_t M, int64_t K, const in
                                const float* sw, int64_t N, const uint16_t* W_outlier_rows,
                                float threshold, uint16_t* Y, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  return linear_impl("int8_linear", X, M, K, Wq, sw, N, W_outlier_rows, nullptr, threshold, Y,
-                     workspace, workspace_bytes, stream);
+  return linear_impl("int8_linear", X, M, K, Wq, sw, nullptr, N, W_outlier_rows, nullptr,
+                     threshold, Y, workspace, workspace_bytes, stream, false);
 }
 
 I8L_API i8l_status int8_linear_bias(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
                                     const float* sw, int64_t N, const uint16_t* W_outlier_rows,
                                     const uint16_t* bias, float threshold, uint16_t* Y,
                                     void* workspace, size_t workspace_bytes, void* stream) {
-  return linear_impl("int8_linear_bias", X, M, K, Wq, sw, N, W_outlier_rows, bias, threshold, Y,
-                     workspace, workspace_bytes, stream);
+  return linear_impl("int8_linear_bias", X, M, K, Wq, sw, nullptr, N, W_outlier_rows, bias,
+                     threshold, Y, workspace, workspace_bytes, stream, false);
 }
 
-I8L_API i8l_status int8_quantize_activation(const uint16_t* X, int64_t M, int64_t K,
-                                            float threshold, int8_t* Xq, float* sx,
-                                            int32_t* outlier_idx, int32_t* n_outliers,
-                                            uint16_t* X_outliers, void* workspace,
-                                            size_t workspace_bytes, void* stream) {
-  const char* fn = "int8_quantize_activation";
+I8L_API i8l_status int8_linear_zp(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
+                                  const float* sw, const int32_t* wsum, int64_t N,
+                                  const uint16_t* W_outlier_rows, const uint16_t* bias,
+                                  float threshold, uint16_t* Y, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return linear_impl("int8_linear_zp", X, M, K, Wq, sw, wsum, N, W_outlier_rows, bias, threshold,
+                     Y, workspace, workspace_bytes, stream, true);
+}
+
+namespace {
+// use_zp: zero-point codes (sx then receives range / 255, zp the zero points).
+i8l_status quantize_activation_impl(const char* fn, const uint16_t* X, int64_t M, int64_t K,
+                                    float threshold, int8_t* Xq, float* sx, int32_t* zp,
+                                    int32_t* outlier_idx, int32_t* n_outliers,
+                                    uint16_t* X_outliers, void* workspace,
+                                    size_t workspace_bytes, void* stream, bool use_zp) {
   i8l_status s = check_shape(fn, M, K, 0);
   if (s != I8L_OK) return s;
+  if (use_zp && (s = check_zp_k(fn, K)) != I8L_OK) return s;
   if (isnan(threshold)) return fail(I8L_ERR_INVALID_ARG, "%s: threshold is NaN", fn);
   const bool enabled = threshold > 0.0f && isfinite(threshold);
   if (M == 0) {
@@ -211,6 +254,7 @@ I8L_API i8l_status int8_quantize_activation(const uint16_t* X, int64_t M, int64_
   REQUIRE_PTR(fn, X, 16);
   REQUIRE_PTR(fn, Xq, 16);
   REQUIRE_PTR(fn, sx, 4);
+  if (use_zp) REQUIRE_PTR(fn, zp, 4);
   REQUIRE_PTR(fn, outlier_idx, 4);
   REQUIRE_PTR(fn, n_outliers, 4);
   REQUIRE_PTR(fn, X_outliers, 16);
@@ -226,8 +270,32 @@ I8L_API i8l_status int8_quantize_activation(const uint16_t* X, int64_t M, int64_
   w.sx = sx;
   w.Xq = Xq;
   w.X_O = X_outliers;
+  if (use_zp) w.zp = zp;
   return hip_status(fn, i8l::launch_quantize_activation(X, (int)M, (int)K, threshold, enabled, w,
-                                                        static_cast<hipStream_t>(stream)));
+                                                        static_cast<hipStream_t>(stream),
+                                                        use_zp));
+}
+}  // namespace
+
+I8L_API i8l_status int8_quantize_activation(const uint16_t* X, int64_t M, int64_t K,
+                                            float threshold, int8_t* Xq, float* sx,
+                                            int32_t* outlier_idx, int32_t* n_outliers,
+                                            uint16_t* X_outliers, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  return quantize_activation_impl("int8_quantize_activation", X, M, K, threshold, Xq, sx, nullptr,
+                                  outlier_idx, n_outliers, X_outliers, workspace,
+                                  workspace_bytes, stream, false);
+}
+
+I8L_API i8l_status int8_quantize_activation_zp(const uint16_t* X, int64_t M, int64_t K,
+                                               float threshold, int8_t* Xq, int32_t* zp,
+                                               float* xscale, int32_t* outlier_idx,
+                                               int32_t* n_outliers, uint16_t* X_outliers,
+                                               void* workspace, size_t workspace_bytes,
+                                               void* stream) {
+  return quantize_activation_impl("int8_quantize_activation_zp", X, M, K, threshold, Xq, xscale,
+                                  zp, outlier_idx, n_outliers, X_outliers, workspace,
+                                  workspace_bytes, stream, true);
 }
 
 I8L_API i8l_status int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N,
@@ -240,8 +308,8 @@ I8L_API i8l_status int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, 
   REQUIRE_PTR(fn, Wq, 16);
   REQUIRE_PTR(fn, acc, 16);
   (void)hipGetLastError();
-  i8l::GemmArgs g{Xq, Wq, (int)M, (int)N, (int)K, nullptr, nullptr, nullptr, nullptr,
-                  nullptr, nullptr, nullptr, acc, nullptr, nullptr, nullptr, 0, 0, 1};
+  i8l::GemmArgs g{Xq, Wq, (int)M, (int)N, (int)K, nullptr, nullptr, nullptr, nullptr, nullptr,
+                  nullptr, nullptr, acc, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 1};
   return hip_status(fn, i8l::launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 

@@ -12,7 +12,8 @@ namespace i8l {
 struct Workspace {
   int32_t* n_out;      // [1]
   int32_t* idx;        // [K]
-  float* sx;           // [M]
+  float* sx;           // [M] absmax, or range / 255 in zero-point mode
+  int32_t* zp;         // [M] zero points (zero-point mode only)
   int8_t* Xq;          // [M][K]
   uint16_t* X_O;       // [M][K] capacity, row stride K
   uint32_t* flags;     // [ceil(K/32)]
@@ -39,9 +40,15 @@ hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, f
                                   hipStream_t stream);
 
 // Outlier column scan + row quantization (two kernels after a flag clear).
-// `enabled` false skips the scan: no column is an outlier.
+// `enabled` false skips the scan: no column is an outlier.  `zp`: zero-point
+// codes (stored minus 128), range / 255 in ws.sx and the zero points in ws.zp.
 hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float threshold,
-                                      bool enabled, const Workspace& ws, hipStream_t stream);
+                                      bool enabled, const Workspace& ws, hipStream_t stream,
+                                      bool zp = false);
+
+// S[n] = sum_k Wq[n][k] (the zero-point correction of the int8 product).
+hipError_t launch_weight_code_sums(const int8_t* Wq, int N, int K, int32_t* S,
+                                   hipStream_t stream);
 
 // int8 GEMM on the matrix cores.  With Y != nullptr: dequantize with sx/sw, add
 // the fp16 outlier product (X_O against rows idx of W_rows) and store fp16 Y.
@@ -59,6 +66,11 @@ struct GemmArgs {
   uint16_t* Y;
   int32_t* acc;
   const uint16_t* bias;   // fp16 [N] added before the final rounding, or NULL
+  // zero-point mode (zp != NULL): Xq holds q - 128 and sx the row's range / 255;
+  // the accumulator becomes acc + (128 - zp[m]) * wsum[n] (exact in int32) and
+  // is dequantized with sx * sw / 127
+  const int32_t* zp;
+  const int32_t* wsum;
   int32_t* cnt;      // split-K tail (Y output only): workspace counters / partials
   int32_t* part;
   int part_slices;   // 0: never split
@@ -75,6 +87,12 @@ bool decode_fits(int M, int K);
 hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
                          int N, const uint16_t* W_rows, const uint16_t* bias, float threshold,
                          bool enabled, uint16_t* Y, const Workspace& ws, hipStream_t stream);
+// Zero-point mode for M <= 16: the activation kernels (zero-point codes), then
+// the streaming kernel with the corrected epilogue.
+hipError_t launch_decode_zp(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
+                            const int32_t* wsum, int N, const uint16_t* W_rows,
+                            const uint16_t* bias, float threshold, bool enabled, uint16_t* Y,
+                            const Workspace& ws, hipStream_t stream);
 
 const char* gemm_tile_info();
 

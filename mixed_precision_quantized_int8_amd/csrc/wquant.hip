@@ -119,4 +119,37 @@ hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, f
   return hipGetLastError();
 }
 
+// Code sums S[n] = sum_k Wq[n][k] for the zero-point mode: with activation
+// codes q stored as q - 128, sum_k (q - zp) w = sum_k (q - 128) w + (128 - zp) S[n]
+// ([blog, "Introduction to model quantization"], the unsigned scheme).
+// One wave per row of Wq, 16-byte loads along K (K % 16 == 0).  Runs once per
+// layer, next to the weight quantization.
+constexpr int kWsThreads = 256;
+__global__ __launch_bounds__(kWsThreads) void wsum_kernel(const int8_t* __restrict__ Wq, int N,
+                                                         int K, int32_t* __restrict__ S) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * (kWsThreads / 64) + (threadIdx.x >> 6);
+  if (n >= N) return;   // whole wave
+  const int8_t* row = Wq + (size_t)n * K;
+  int sum = 0;
+  for (int k = lane * 16; k < K; k += 64 * 16) {
+    const v4i v = *reinterpret_cast<const v4i*>(row + k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int x = v[e];
+      sum += (int)(int8_t)x + (int)(int8_t)(x >> 8) + (int)(int8_t)(x >> 16) + (x >> 24);
+    }
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) S[n] = sum;
+}
+
+hipError_t launch_weight_code_sums(const int8_t* Wq, int N, int K, int32_t* S,
+                                   hipStream_t stream) {
+  const int per = kWsThreads / 64;
+  hipLaunchKernelGGL(wsum_kernel, dim3((N + per - 1) / per), dim3(kWsThreads), 0, stream, Wq, N,
+                     K, S);
+  return hipGetLastError();
+}
+
 }  // namespace i8l

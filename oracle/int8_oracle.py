@@ -392,3 +392,23 @@ def int8_linear_zp(X16, Wq, sw, W16, threshold, bias=None):
         Y = Y64.astype(np.float16)
     return dict(Xq=Xq, zp=zp, xscale=xscale, idx=idx, X_O=X_O, acc=acc.astype(np.int64),
                 Y64=Y64, Y=Y)
+
+
+def int8_linear_zp_entries(act_zp, Wq_rows, sw_rows, W16, rows, cols, bias=None):
+    """Y64 of ``int8_linear_zp`` at sampled (rows[j], cols[j]) pairs (r11), each
+    computed on its own from a ``quantize_activation_zp`` result; ``Wq_rows`` /
+    ``sw_rows`` hold the weight rows for ``cols`` in the same order.
+    Returns (acc int64 = sum_k (q - zp) w, Y64)."""
+    Xq, zp, xscale, idx, X_O = act_zp
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    qd = Xq[rows].astype(np.float64) + 128.0 - zp[rows].astype(np.float64)[:, None]
+    acc = np.einsum("jk,jk->j", qd, np.asarray(Wq_rows, np.int8).astype(np.float64))
+    Y64 = acc * xscale[rows].astype(np.float64) * np.asarray(sw_rows, np.float64) / float(INT8_MAX)
+    if len(idx):
+        W = np.asarray(W16, dtype=np.float16)
+        WO = W[idx.astype(np.int64)][:, cols].astype(np.float64)
+        Y64 = Y64 + np.einsum("jo,oj->j", X_O[rows].astype(np.float64), WO)
+    if bias is not None:
+        Y64 = Y64 + np.asarray(bias, dtype=np.float16).astype(np.float64)[cols]
+    return acc.astype(np.int64), Y64

@@ -107,6 +107,46 @@ def test_other_entry_points_validate(i8l):
     assert L.int8_quantize_activation(*bad) == WORKSPACE
 
 
+def test_zero_point_entry_points_validate(i8l):
+    L = i8l.lib()
+
+    def lin(X=P16, M=32, K=64, Wq=P16, sw=P16, S=P16, N=32, W=P16, b=None, t=6.0, Y=P16,
+            ws=P16, wsb=1 << 40):
+        return L.int8_linear_zp(X, M, K, Wq, sw, S, N, W, b, t, Y, ws, wsb, None)
+
+    assert lin(S=None) == INVALID and "wsum is NULL" in i8l.last_error()
+    assert lin(S=P16 + 2) == INVALID and "aligned" in i8l.last_error()
+    assert lin(X=None) == INVALID
+    assert lin(b=P16 + 1) == INVALID and "bias" in i8l.last_error()
+    assert lin(t=math.nan) == INVALID
+    assert lin(K=72) == INVALID
+    # zero-point codes: 255 * 127 * K must fit in int32
+    assert lin(K=66320) == K_TOO_LARGE and "66304" in i8l.last_error()
+    assert lin(K=66304, M=0) == OK
+    assert lin(M=0) == OK and lin(N=0) == OK
+    need = i8l.workspace_bytes(32, 64, 32)
+    assert lin(wsb=need - 1) == WORKSPACE
+
+    args = [P16, 8, 64, 6.0, P16, P16, P16, P16, P16, P16, P16, 1 << 40, None]
+    for i in (0, 4, 5, 6, 7, 8, 9, 10):
+        bad = list(args)
+        bad[i] = None
+        assert L.int8_quantize_activation_zp(*bad) == INVALID, i
+    bad = list(args)
+    bad[2] = 66320
+    assert L.int8_quantize_activation_zp(*bad) == K_TOO_LARGE
+    bad = list(args)
+    bad[11] = 16
+    assert L.int8_quantize_activation_zp(*bad) == WORKSPACE
+
+    assert L.int8_weight_code_sums(None, 8, 64, P16, None) == INVALID
+    assert L.int8_weight_code_sums(P16, 8, 64, None, None) == INVALID
+    assert L.int8_weight_code_sums(P16 + 4, 8, 64, P16, None) == INVALID
+    assert L.int8_weight_code_sums(P16, 8, 70, P16, None) == INVALID
+    assert L.int8_weight_code_sums(P16, 0, 64, P16, None) == OK
+    assert i8l.MAX_K_ZP == 66304
+
+
 def test_workspace_layout(i8l):
     for (M, K) in [(1, 16), (16, 1024), (2048, 14336), (4096, 57344), (300, 272)]:
         L = i8l.workspace_layout(M, K, 123)
@@ -118,7 +158,10 @@ def test_workspace_layout(i8l):
         assert L["flags"] - L["sx"] >= 4 * M
         assert L["Xq"] - L["flags"] >= 4 * ((K + 31) // 32)
         assert L["X_outliers"] - L["Xq"] >= M * K
-        assert L["gemm_counters"] - L["X_outliers"] >= 2 * M * K
+        assert L["zero_points"] - L["X_outliers"] >= 2 * M * K
+        assert L["gemm_counters"] - L["zero_points"] >= 4 * M
+        assert L["zero_points"] % 256 == 0
+        assert L["zero_points"] == i8l.workspace_layout(M, K, 0)["zero_points"]
         assert L["gemm_partials"] >= L["gemm_counters"]
         assert L["total"] - L["gemm_partials"] >= L["gemm_slices"] * 256 * 256 * 4
         if L["gemm_slices"]:

@@ -536,3 +536,20 @@ def test_zero_point_round_trip_and_layer_identity():
     Wd = Wq.astype(np.float64).T * sw.astype(np.float64)[None, :] / 127
     ref = deq[:, reg] @ Wd[reg] + X[:, idx].astype(np.float64) @ W[idx].astype(np.float64) + b
     np.testing.assert_allclose(r["Y64"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_point_sampled_entries_match_full():
+    rng = np.random.default_rng(23)
+    M, K, N = 9, 160, 24
+    X = (rng.standard_normal((M, K)) + 0.8).astype(np.float16)
+    X[:, [3, 77]] = np.float16(7.5)
+    W = (rng.standard_normal((K, N)) * 0.04).astype(np.float16)
+    b = rng.standard_normal(N).astype(np.float16)
+    Wq, sw = O.quantize_weight(W)
+    full = O.int8_linear_zp(X, Wq, sw, W, 6.0, bias=b)
+    rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    rows, cols = rows.ravel(), cols.ravel()
+    act = O.quantize_activation_zp(X, 6.0)
+    acc, y = O.int8_linear_zp_entries(act, Wq[cols], sw[cols], W, rows, cols, bias=b)
+    np.testing.assert_array_equal(acc, full["acc"][rows, cols])
+    np.testing.assert_allclose(y, full["Y64"][rows, cols], rtol=1e-13, atol=1e-13)
