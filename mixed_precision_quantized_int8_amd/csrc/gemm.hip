@@ -12,25 +12,32 @@
 // Layout: Xq [M][K] and Wq [N][K] are both K-contiguous ("NT"), which is what
 // the matrix-core operands want: each lane feeds 16 consecutive k of one row.
 //
-// Tiling (256 threads = 4 waves of 64, one workgroup per CU):
-//   * workgroup tile 256 x 256, K step 64 bytes;
-//   * a 4-stage LDS ring (4 x 32 KB) fed by direct global->LDS loads
-//     (global_load_lds_dwordx4), issued three stages ahead of use, with
-//     explicit vmcnt waits and a fence-free barrier so they stay in flight;
-//     every iteration issues exactly one stage (past the last stage it
-//     re-reads valid memory into a consumed buffer), so the loop body has no
-//     branches and the loads can be interleaved with the MFMAs;
-//   * each wave owns a 128 x 128 sub-tile = 4 x 4 blocks of
-//     v_mfma_i32_32x32x32_i8 (256 int32 accumulators per lane, held in the
-//     accumulation registers).  On gfx950 this shape sustains ~93% of the int8
-//     peak in a bare loop, against ~79% for v_mfma_i32_16x16x64_i8;
-//   * software pipeline at half-step granularity: while the 16 MFMAs of one
-//     32-byte k half run, the 8 fragments of the next half are read from LDS
-//     into the other of two fixed register sets; reads and loads are placed
-//     one per MFMA with sched_group_barrier;
-//   * LDS rows are 64 bytes = four 16-byte chunks; chunk c of row r is stored
-//     at c ^ (((r >> 1) ^ (r >> 3)) & 3), so the 16-byte fragment reads of 8
-//     or 16 consecutive rows fall into distinct banks;
+// Tiling (512 threads = 8 waves of 64, one workgroup per CU, two waves per
+// SIMD so that one can issue matrix instructions while the other waits on a
+// load or the LDS):
+//   * workgroup tile 256 x 256, K step 128 bytes: every load instruction moves
+//     8 rows x 128 bytes, whole cache lines (measured: feeding the tile's
+//     panels this way is ~30 % faster than with 64-byte rows);
+//   * the LDS holds 5 slots of 32 KB, each one operand panel (256 rows x 128
+//     bytes) of one K step: while step kt is multiplied, B of step kt+1 and A
+//     of step kt+2 are in flight (A of kt+1 was issued one step earlier), so
+//     2.5 steps live in the 160 KB; loads go global -> LDS directly
+//     (global_load_lds_dwordx4) with explicit vmcnt waits and a fence-free
+//     barrier, so they stay in flight across it; past the last step they
+//     re-read valid memory into a consumed slot, so the loop body has no
+//     branches and the wait counts are fixed;
+//   * each wave owns a 128 x 64 sub-tile = 4 x 2 blocks of
+//     v_mfma_i32_32x32x32_i8 (128 int32 accumulators per lane); on gfx950 this
+//     shape sustains ~93% of the int8 peak in a bare loop, against ~79% for
+//     v_mfma_i32_16x16x64_i8;
+//   * software pipeline at quarter-step granularity: while the 8 MFMAs of one
+//     32-byte k quarter run, the 6 fragments of the next quarter are read from
+//     LDS into the other of two fixed register sets; reads and loads are
+//     placed between the MFMAs with sched_group_barrier;
+//   * LDS rows are 128 bytes = eight 16-byte chunks; chunk c of row r is
+//     stored at c ^ (((r >> 1) & 3) | (((r >> 4) & 1) << 2)): the bank-conflict
+//     counter reads 0 for the fragment reads (one chunk of 32 consecutive rows
+//     per half-wave);
 //   * tiles are handed out XCD by XCD: workgroup b runs on XCD b % 8, and each
 //     XCD takes a contiguous range of tiles ordered in groups of 8 tile-rows so
 //     that concurrently running tiles share operand panels in that XCD's L2.
@@ -56,11 +63,12 @@ namespace i8l {
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kStages = 4;   // LDS ring depth (32 KB per stage)
-constexpr int kGemmThreads = 256;
+constexpr int kBM = 256, kBN = 256, kBK = 128;
+constexpr int kSlots = 5;                  // LDS slots of one operand panel of one K step
+constexpr int kSlot = kBM * kBK;           // 32 KB
+constexpr int kGemmThreads = 512;
 constexpr int kGroupM = 8;
-__device__ __forceinline__ int lds_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int lds_swz(int row) { return ((row >> 1) & 3) | (((row >> 4) & 1) << 2); }
 
 // Tile order: linear tile index -> (tile row, tile column), in groups of
 // kGroupM tile rows so that concurrently running tiles share operand panels.
@@ -112,13 +120,13 @@ __device__ __forceinline__ int d_row(int r, int lane) {
 // kernel carries none of the split bookkeeping.  ZP: zero-point epilogue.
 template <bool OUT_I32, bool SPLIT, bool ZP>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
-  // kStages ring buffers of [A 256 x 64 | B 256 x 64] bytes
-  __shared__ __attribute__((aligned(1024))) int8_t smem[kStages][2][kBM * kBK];
-
-  __shared__ int sLast;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kSlots * kSlot];
+  // split tiles' arrival flag, after the main loop only: the last word of the
+  // LDS, past the region the epilogue stages into
+  int& sLast = *reinterpret_cast<int*>(&smem[kSlots * kSlot - 4]);
 
   const int M = a.M, N = a.N, K = a.K;
-  const int nkt = (K + kBK - 1) / kBK;   // k-steps of 64 bytes
+  const int nkt = (K + kBK - 1) / kBK;   // k-steps of 128 bytes
   const int nTm = (M + kBM - 1) / kBM, nTn = (N + kBN - 1) / kBN;
   // Whole tiles first; then the split tiles of the tail, S workgroups each,
   // every one on its own range of k-steps [kb, kb + nk).
@@ -138,13 +146,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
   const int l32 = lane & 31, lh = lane >> 5;
 
   // Direct global -> LDS loads.  One instruction moves 64 lanes x 16 bytes into
-  // 1 KB of LDS (16 rows of 64 bytes); lane l lands at row 16*blk + l/4,
-  // physical chunk l%4, so it fetches the logical chunk (l%4) ^ swz(row).
-  // Wave w fills blocks 4w .. 4w+3 of A and of B: 8 loads per stage.
+  // 1 KB of a slot (8 rows of 128 bytes); lane l lands at row 8*blk + l/8,
+  // physical chunk l%8, so it fetches the logical chunk (l%8) ^ swz(row).
+  // Wave w fills blocks 4w .. 4w+3 of a slot: 4 loads per operand and step.
   // Rows past M (or N) are clamped to the last row: they only feed outputs
   // that are never stored.  K-tail chunks read zeros from a device zero page.
   // Every address stays inside the operands.
@@ -153,64 +161,55 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   const int lastA = min(M - m0, kBM) - 1, lastB = min(N - n0, kBN) - 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = (wave * 4 + i) * 16 + (lane >> 2);
-    cofs[i] = ((lane & 3) ^ lds_swz(row)) * 16;
+    const int row = (wave * 4 + i) * 8 + (lane >> 3);
+    cofs[i] = ((lane & 7) ^ lds_swz(row)) * 16;
     rowA[i] = (uint32_t)(min(row, lastA) * K);
     rowB[i] = (uint32_t)(min(row, lastB) * K);
   }
   const int8_t* tileA = a.Xq + (size_t)m0 * K;
   const int8_t* tileB = a.Wq + (size_t)n0 * K;
-  // Loads of stage kt into ring buffer `stage`, in two groups of 4 (blocks
-  // 4w, 4w+1 of A and B; blocks 4w+2, 4w+3) that go out in different halves of
-  // an iteration; branch-free so that they can be interleaved with the MFMAs
-  // (K-tail chunks select the zero page per lane).
-  auto issue_group = [&](int stage, int kt, int grp) {   // kt: step inside [kb, kb + nk)
-    const int k0 = (kb + kt) * kBK;
-#pragma unroll
-    for (int i = 2 * grp; i < 2 * grp + 2; ++i) {
-      const int kk = k0 + cofs[i];
-      const bool in = kk < K;
-      const int8_t* ga = in ? tileA + rowA[i] + kk : g_zero_page;
-      const int8_t* gb = in ? tileB + rowB[i] + kk : g_zero_page;
-      __builtin_amdgcn_global_load_lds((const void*)ga,
-                                       I8L_LDS(&smem[stage][0][(wave * 4 + i) * 1024]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)gb,
-                                       I8L_LDS(&smem[stage][1][(wave * 4 + i) * 1024]), 16, 0, 0);
-    }
+  // Load i (0..3) of one operand of step kt into slot `sl`; branch-free so that
+  // it can be placed between the MFMAs (K-tail chunks select the zero page).
+  auto load = [&](int sl, int kt, bool isB, int i) {   // kt: step inside [kb, kb + nk)
+    const int kk = (kb + kt) * kBK + cofs[i];
+    const bool in = kk < K;
+    const int8_t* g = in ? (isB ? tileB + rowB[i] : tileA + rowA[i]) + kk : g_zero_page;
+    __builtin_amdgcn_global_load_lds((const void*)g, I8L_LDS(&smem[sl * kSlot + (wave * 4 + i) * 1024]),
+                                     16, 0, 0);
   };
-
-  // Fragments of one 32-byte k half `h` of stage kt: 4 A blocks and 4 B blocks
-  // of 32 rows; lane l reads row l % 32, logical chunk 2h + l / 32.
-  auto read_half = [&](int kt, int h, v4i (&fa)[4], v4i (&fb)[4]) {
-    const int8_t* sA = smem[kt % kStages][0];
-    const int8_t* sB = smem[kt % kStages][1];
-    const int c = 2 * h + lh;
+  // Step kt's A panel sits in slot (2 kt) % 5 and its B panel in (2 kt + 1) % 5.
+  // Fragments of the 32-byte k quarter q: 4 A blocks and 2 B blocks of 32
+  // rows; lane l reads row l % 32, logical chunk 2q + l / 32.
+  auto read_q = [&](int kt, int q, v4i (&fa)[4], v4i (&fb)[2]) {
+    const int8_t* sA = &smem[((2 * kt) % kSlots) * kSlot];
+    const int8_t* sB = &smem[((2 * kt + 1) % kSlots) * kSlot];
+    const int c = 2 * q + lh;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wm + i * 32 + l32;
       fa[i] = *reinterpret_cast<const v4i*>(&sA[row * kBK + ((c ^ lds_swz(row)) << 4)]);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int row = wn + j * 32 + l32;
       fb[j] = *reinterpret_cast<const v4i*>(&sB[row * kBK + ((c ^ lds_swz(row)) << 4)]);
     }
   };
 
-  v16i acc[4][4];
+  v16i acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16i{};
   if constexpr (ZP && !SPLIT) {
     // Zero-point correction as the accumulators' starting value: the MFMAs then
     // add sum_k (q - 128) w on top.  Every prefix sum stays within
     // 255 * 127 * K < 2^31 in magnitude, so nothing wraps.  Rows past M read 0
     // from the buffer resource (never stored).
     const buf_rsrc rz = make_rsrc(a.zp, (uint32_t)M * 4u);
-    uint32_t wsv[4];
+    uint32_t wsv[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int n = n0 + wn + j * 32 + l32;
       wsv[j] = n < N ? (uint32_t)a.wsum[n] : 0u;
     }
@@ -220,83 +219,105 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
       for (int r = 0; r < 16; ++r) {   // one dword per row: each load wholly in or out
         const uint32_t z = buf_load_u32(rz, (uint32_t)(m0 + wm + i * 32 + d_row(r, lane)) * 4u);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j][r] = (int)((128u - z) * wsv[j]);
+        for (int j = 0; j < 2; ++j) acc[i][j][r] = (int)((128u - z) * wsv[j]);
       }
   }
-  auto mfma_one = [&](const v4i (&fa)[4], const v4i (&fb)[4], int q) {
+  auto mfma_one = [&](const v4i (&fa)[4], const v4i (&fb)[2], int q) {
     const int i = q & 3, j = q >> 2;
     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
   // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
   constexpr int kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100;
-
-  // Ring schedule.  The buffer of stage kt is free once every wave has read
-  // its half-1 fragments, i.e. after the barrier in the middle of iteration kt,
-  // so stage kt+4 can go there.  Each stage's 8 loads per wave go out in two
-  // groups: group 0 of stage kt+4 in the second half of iteration kt, group 1
-  // in the first half of iteration kt+1, one load per ~4 MFMAs, so that the
-  // four waves do not flood the load pipeline at the same moment.  Every
-  // iteration issues exactly 8 loads (past the last stage they re-read stage
-  // nk-1 into a consumed buffer), so when stage kt+1 is waited for, the 16
-  // loads of stages kt+2 and kt+3 may stay in flight.
-  issue_group(0, 0, 0);
-  issue_group(0, 0, 1);
+  // One quarter: 8 MFMAs with the 6 fragment reads of the next quarter and 2
+  // loads between them.
+  auto pattern_quarter = [&]() {
 #pragma unroll
-  for (int s = 1; s < kStages - 1; ++s) {
-    issue_group(s, min(s, nk - 1), 0);
-    issue_group(s, min(s, nk - 1), 1);
+    for (int r = 0; r < 2; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Slot schedule (5 slots, steps of two panels).  During iteration kt: step
+  // kt is read from slots 2kt, 2kt+1; A of kt+1 (slot 2kt+2) was issued during
+  // iteration kt-1; B of kt+1 goes to slot 2kt+3 (quarters 0-1) and A of kt+2
+  // to slot 2kt+4 (quarters 2-3), all mod 5.  Slots 2kt+3 and 2kt+4 held step
+  // kt-1, which every wave finished reading before the previous barrier.  The
+  // barrier at the end of iteration kt needs step kt+1 complete: issued after
+  // its last load are only the first two A loads of kt+2, so vmcnt(2).
+  load(0, 0, false, 0); load(0, 0, false, 1); load(0, 0, false, 2); load(0, 0, false, 3);
+  load(1, 0, true, 0); load(1, 0, true, 1); load(1, 0, true, 2); load(1, 0, true, 3);
+  {
+    const int k1 = min(1, nk - 1);
+    load(2, k1, false, 0); load(2, k1, false, 1); load(2, k1, false, 2); load(2, k1, false, 3);
   }
-  issue_group(kStages - 1, min(kStages - 1, nk - 1), 0);
-  static_assert(kStages == 4, "wait counts below assume a 4-stage ring");
-  wait_vmcnt<20>();   // stage 0 landed
+  wait_vmcnt<4>();   // step 0 landed; A of step 1 may be in flight
   lds_barrier();
 
-  v4i f0a[4], f0b[4], f1a[4], f1b[4];
-  read_half(0, 0, f0a, f0b);
+  v4i f0a[4], f0b[2], f1a[4], f1b[2];
+  read_q(0, 0, f0a, f0b);
   for (int kt = 0; kt < nk; ++kt) {
-    // ---- half 0 of stage kt: MFMAs on f0; the 8 reads of half 1 of stage kt
-    // and group 1 of stage kt+3 (its buffer held stage kt-1, consumed before
-    // the previous iteration's barrier) interleaved.  The only outstanding LDS
-    // reads here are those of f0, so draining lgkmcnt first costs little.
+    const int slB = (2 * kt + 3) % kSlots, slA = (2 * kt + 4) % kSlots;
+    const int kB = min(kt + 1, nk - 1), kA = min(kt + 2, nk - 1);
+    // ---- quarter 0: MFMAs on f0, reads of quarter 1 into f1, B loads 0-1.
+    // The only outstanding LDS reads are those of f0, so draining lgkmcnt
+    // first costs little.
     wait_lgkmcnt0();
-    read_half(kt, 1, f1a, f1b);
-    issue_group((kt + 3) % kStages, min(kt + 3, nk - 1), 1);
+    read_q(kt, 1, f1a, f1b);
+    load(slB, kB, true, 0);
+    load(slB, kB, true, 1);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) mfma_one(f0a, f0b, q);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < 8; ++q) mfma_one(f0a, f0b, q);
+    pattern_quarter();
+    // ---- quarter 1: B loads 2-3
     wait_lgkmcnt0();
-    // ---- half 1: the first MFMA goes out before the stage wait and the
-    // barrier, so the matrix pipe is busy while the waves synchronize.
+    read_q(kt, 2, f0a, f0b);
+    load(slB, kB, true, 2);
+    load(slB, kB, true, 3);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) mfma_one(f1a, f1b, q);
+    pattern_quarter();
+    // ---- quarter 2: A loads 0-1 of step kt+2
+    wait_lgkmcnt0();
+    read_q(kt, 3, f1a, f1b);
+    load(slA, kA, false, 0);
+    load(slA, kA, false, 1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) mfma_one(f0a, f0b, q);
+    pattern_quarter();
+    // ---- quarter 3: the first MFMA goes out before the wait and the barrier,
+    // so the matrix pipe is busy while the waves synchronize.
+    wait_lgkmcnt0();
     mfma_one(f1a, f1b, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // Stage kt+1 must have landed in every wave's view.
-    wait_vmcnt<16>();
+    wait_vmcnt<2>();
     lds_barrier();
-    // Stage kt is fully read: its buffer takes group 0 of stage kt+4.  On the
-    // last step the fragment reads re-read stage kt (landed, unused), so that
+    // Step kt+1 is in every wave's view and step kt's slots are free.  On the
+    // last step the fragment reads re-read step kt (landed, unused), so that
     // the registers keep fixed roles.
-    read_half(kt + 1 < nk ? kt + 1 : kt, 0, f0a, f0b);
-    issue_group(kt % kStages, min(kt + 4, nk - 1), 0);
+    read_q(kt + 1 < nk ? kt + 1 : kt, 0, f0a, f0b);
+    load(slA, kA, false, 2);
+    load(slA, kA, false, 3);
 #pragma unroll
-    for (int q = 1; q < 16; ++q) mfma_one(f1a, f1b, q);
+    for (int q = 1; q < 8; ++q) mfma_one(f1a, f1b, q);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int r = 0; r < 2; ++r) {
       __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   wait_vmcnt<0>();
@@ -312,7 +333,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           mine[(wm + i * 32 + d_row(r, lane)) * kBN + wn + j * 32 + l32] = acc[i][j][r];
@@ -330,7 +351,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         const int n = n0 + wn + j * 32 + l32;
         if (n >= N) continue;
 #pragma unroll
@@ -353,22 +374,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     constexpr int kOutC = kOutG / 8;           // 16-byte chunks per staged row
     const int n_out = *a.n_out;
     const int ngroups = (n_out + kOutG - 1) / kOutG;
-    uint16_t* sAo = reinterpret_cast<uint16_t*>(&smem[0][0][0]);   // [256 rows][96 halves]
+    uint16_t* sAo = reinterpret_cast<uint16_t*>(&smem[0]);         // [256 rows][96 halves]
     uint16_t* sBo = sAo + kBM * kOutG;                             // [256 cols][96 halves]
     float* sSx = reinterpret_cast<float*>(sBo + kBN * kOutG);      // [256]
     float* sSw = sSx + kBM;                                        // [256], includes 1/127^2
     float* sBias = sSw + kBN;                                      // [256] (0 without bias)
     int* sZc = reinterpret_cast<int*>(sBias + kBN);                // [256] 128 - zp (ZP)
     int* sWs = sZc + kBM;                                          // [256] wsum (ZP)
+    static_assert(2 * kBM * kOutG * 2 + 5 * 256 * 4 <= (int)sizeof(smem) - 4,
+                  "epilogue staging must stay clear of the arrival flag");
     // 16-byte chunk c of staged row r sits at c ^ ((r >> 2) & 3): conflict-free
     // fragment reads with the 192-byte row stride
     auto och = [](int r, int c) { return (c ^ ((r >> 2) & 3)) << 3; };
-    sSx[t] = m0 + t < M ? a.sx[m0 + t] : 0.0f;
-    sSw[t] = n0 + t < N ? a.sw[n0 + t] * (ZP ? 1.0f / 127.0f : 1.0f / 16129.0f) : 0.0f;
-    sBias[t] = a.bias && n0 + t < N ? h2f(a.bias[n0 + t]) : 0.0f;
-    if constexpr (ZP) {
-      sZc[t] = m0 + t < M ? 128 - a.zp[m0 + t] : 0;
-      sWs[t] = n0 + t < N ? a.wsum[n0 + t] : 0;
+    if (t < kBM) {   // 512 threads: the first half fills the row/column tables
+      sSx[t] = m0 + t < M ? a.sx[m0 + t] : 0.0f;
+      sSw[t] = n0 + t < N ? a.sw[n0 + t] * (ZP ? 1.0f / 127.0f : 1.0f / 16129.0f) : 0.0f;
+      sBias[t] = a.bias && n0 + t < N ? h2f(a.bias[n0 + t]) : 0.0f;
+    } else if constexpr (ZP) {
+      const int u = t - kBM;
+      sZc[u] = m0 + u < M ? 128 - a.zp[m0 + u] : 0;
+      sWs[u] = n0 + u < N ? a.wsum[n0 + u] : 0;
     }
 
     // fp16 bits of the outlier weight W[k][n]: the caller's fp16 row, or, with
@@ -397,9 +422,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
         }
         *reinterpret_cast<v4i*>(&sAo[row * kOutG + och(row, c)]) = v;
       }
-      const int col = t;   // 256 threads = 256 columns
+      const int col = t & (kBN - 1);   // 512 threads: two per column, half the chunks each
       const int gn = n0 + col;
-      for (int c = 0; c < kOutC; ++c) {
+      for (int c = (t >> 8) * (kOutC / 2); c < ((t >> 8) + 1) * (kOutC / 2); ++c) {
         uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -424,7 +449,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
         for (int e = 0; e < 4; ++e) sxv[4 * q + e] = v[e];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         const int n = n0 + wn + j * 32 + l32;
         const float swv = sSw[wn + j * 32 + l32];
         int tot[16];
@@ -505,8 +530,9 @@ GemmSplit gemm_split_plan(int M, int N, int K, int cus) {
   // round that is at least half full (or a problem smaller than one round) is
   // split.
   if (rem == 0 || (T > cus && 2 * rem < cus)) return p;
-  // each split keeps at least 16 k-steps, so the fix-up stays a small part
-  const int S = std::min(cus / rem, nk / 16);
+  // each split keeps at least 1024 bytes of K (8 k-steps), so the fix-up
+  // stays a small part
+  const int S = std::min(cus / rem, nk / 8);
   if (S < 2) return p;
   return GemmSplit{T - rem, rem, S};
 }
@@ -566,7 +592,7 @@ hipError_t launch_gemm(const GemmArgs& in, hipStream_t stream) {
 }
 
 const char* gemm_tile_info() {
-  return "gemm: 256x256x64 tile, 4-stage LDS-DMA ring, 4 waves of 128x128, "
+  return "gemm: 256x256x128 tile, 5-slot LDS-DMA ring, 8 waves of 128x64, "
          "v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_f16 outlier tail";
 }
 
