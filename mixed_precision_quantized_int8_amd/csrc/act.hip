@@ -102,17 +102,17 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = wave_incl_scan(v);
   if (lane == 63) s_tmp[wave] = incl;
-  __syncthreads();
+  lds_sync();
   if (wave == 0) {
     int w = lane < BS / 64 ? s_tmp[lane] : 0;
     int wi = wave_incl_scan(w);
     if (lane < BS / 64) s_tmp[lane] = wi - w;
     if (lane == 63) s_tmp[BS / 64] = wi;
   }
-  __syncthreads();
+  lds_sync();
   int r = s_tmp[wave] + incl - v;
   *total = s_tmp[BS / 64];
-  __syncthreads();
+  lds_sync();
   return r;
 }
 
@@ -143,33 +143,37 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
   const int row = blockIdx.x;
   const int nw = (K + 31) >> 5;
 
-  // flags -> LDS, exclusive prefix popcount per word
+  // Loads first, all branch-free buffer loads (past the end they read 0): the
+  // flag words w = t + i*BS, then the row; writing the flags to LDS waits only
+  // for the flag loads, and the row stays in flight while the flags are
+  // scanned (the barriers below order LDS only).
+  constexpr int FW = (NCH + 3) / 4;   // BS*NCH*8 >= K, so FW*BS >= ceil(K/32)
+  const buf_rsrc rf = make_rsrc(flags, (uint32_t)nw * 4u);
+  uint32_t fl[FW];
+#pragma unroll
+  for (int i = 0; i < FW; ++i) fl[i] = buf_load_u32(rf, (uint32_t)(t + i * BS) * 4u);
+  const buf_rsrc rx = make_rsrc(X + (size_t)row * K, (uint32_t)K * 2u);
+  const int nchunks = K >> 3;
+  v4i raw[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) raw[j] = buf_load16(rx, (uint32_t)(t + j * BS) * 16u);
+#pragma unroll
+  for (int i = 0; i < FW; ++i)
+    if (t + i * BS < nw) s_flags[t + i * BS] = fl[i];
+  lds_sync();
+
+  // exclusive prefix popcount per flag word, over contiguous word ranges
   const int w0 = t * ((nw + BS - 1) / BS);
   const int w1 = min(nw, w0 + (nw + BS - 1) / BS);
   int cnt = 0;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t f = flags[w];
-    s_flags[w] = f;
-    cnt += __builtin_popcount(f);
-  }
+  for (int w = w0; w < w1; ++w) cnt += __builtin_popcount(s_flags[w]);
   int total;
   int base = block_excl_scan<BS>(cnt, s_tmp, &total);
   for (int w = w0; w < w1; ++w) {
     s_rank[w] = base;
     base += __builtin_popcount(s_flags[w]);
   }
-  __syncthreads();
-
-  // the row, in registers
-  const uint16_t* xr = X + (size_t)row * K;
-  const int nchunks = K >> 3;
-  v4i raw[NCH];
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int q = t + j * BS;
-    if (q < nchunks) raw[j] = *reinterpret_cast<const v4i*>(xr + q * 8);
-    else raw[j] = v4i{0, 0, 0, 0};
-  }
+  lds_sync();
   uint32_t mx = 0;
   float lo = 0.0f, hi = 0.0f;   // zero-point mode: the range always contains 0
 #pragma unroll
@@ -307,13 +311,19 @@ hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float thr
                        threshold, ws.flags);
   }
   if (M > 0) {
-    const int nch256 = (K / 8 + 255) / 256;
-    if (nch256 <= 1) launch_rowquant<256, 1>(X, M, K, zp, ws, stream);
-    else if (nch256 <= 2) launch_rowquant<256, 2>(X, M, K, zp, ws, stream);
-    else if (nch256 <= 4) launch_rowquant<256, 4>(X, M, K, zp, ws, stream);
-    else if (nch256 <= 8) launch_rowquant<256, 8>(X, M, K, zp, ws, stream);
-    else if (nch256 <= 16) launch_rowquant<256, 16>(X, M, K, zp, ws, stream);
-    else if (nch256 <= 32) launch_rowquant<256, 32>(X, M, K, zp, ws, stream);
+    // Few 16-byte chunks per thread and wide workgroups: the row's loads are
+    // spread over many waves (measured on MI355X: 2048 x 14336 in 24.6 us with
+    // 512 threads x 4 chunks against 43 us with 256 x 32; 4096 x 57344 in
+    // 164 us with 1024 x 7 against 232 us with 256 x 32).
+    const int nch = K / 8;
+    if (nch <= 256) launch_rowquant<256, 1>(X, M, K, zp, ws, stream);
+    else if (nch <= 512) launch_rowquant<256, 2>(X, M, K, zp, ws, stream);
+    else if (nch <= 1024) launch_rowquant<256, 4>(X, M, K, zp, ws, stream);
+    else if (nch <= 2048) launch_rowquant<512, 4>(X, M, K, zp, ws, stream);
+    else if (nch <= 4096) launch_rowquant<1024, 4>(X, M, K, zp, ws, stream);
+    else if (nch <= 7168) launch_rowquant<1024, 7>(X, M, K, zp, ws, stream);
+    else if (nch <= 8192) launch_rowquant<1024, 8>(X, M, K, zp, ws, stream);
+    else if (nch <= 16384) launch_rowquant<1024, 16>(X, M, K, zp, ws, stream);
     else launch_rowquant<1024, 17>(X, M, K, zp, ws, stream);
   }
   return hipGetLastError();

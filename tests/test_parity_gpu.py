@@ -111,6 +111,10 @@ def _act_cases():
     yield "one_row", *wl.make_x(1, 16, 1.0, 0, 8, 20, 4), 6.0
     yield "k_mod32_16", *wl.make_x(17, 1040, 1.0, 3, 8, 20, 5), 6.0
     yield "many_outliers", *wl.make_x(40, 512, 1.0, 45, 8, 20, 6), 6.0
+    # one case per row-quantizer launch shape (chunks of 8 columns per thread)
+    yield "k_24576", *wl.make_x(5, 24576, 1.0, 3, 8, 20, 11), 6.0
+    yield "k_60000", *wl.make_x(3, 60000, 1.0, 4, 8, 20, 12), 6.0
+    yield "k_max", *wl.make_x(2, 133136, 1.0, 5, 8, 20, 13), 6.0
     X, c = wl.make_x(33, 256, 1.0, 0, 8, 20, 7)
     yield "all_outliers", X, c, 2.0 ** -24
     yield "disabled_inf", X, c, math.inf
