@@ -42,9 +42,9 @@ PEAK_INT8_TOPS = 5000.0
 # (profiles/traffic-decode.md: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB, the
 # factors a 512 MiB device copy gives).
 TRAFFIC = {
-    ("decode_kernel", "decode"): {"bytes": 68624496, "src": "cb5bcc7a282cc020"},
-    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2314256549, "src": "75d3f4421d0b4027"},
-    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 2802323812, "src": "75d3f4421d0b4027"},
+    ("decode_kernel", "decode"): {"bytes": 68681526, "src": "0c2b4e6bcd263a94"},
+    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2221329466, "src": "ce1d711bf3a6b42f"},
+    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5551346321, "src": "ce1d711bf3a6b42f"},
 }
 
 
@@ -62,7 +62,9 @@ def algorithmic_bytes(w):
             + 4 * w.N + 4 * w.M + 4 * w.n_out)
 
 
-def dominant_kernel(w):
+def dominant_kernel(w, zero_point=False):
+    if zero_point and w.M <= 16:   # activation kernels, then the streaming kernel
+        return "decode_stream_kernel", "hbm", ["decode.hip", "common.h"]
     if w.M <= 16 and w.K <= 8192 and w.M * ((w.K + 63) // 64 * 64) <= 65536 and (w.M <= 8 or w.K <= 4096):
         return "decode_kernel", "hbm", ["decode.hip", "common.h"]
     return "gemm_i8_kernel", "mfma", ["gemm.hip", "common.h"]
@@ -142,6 +144,8 @@ def main():
     ap.add_argument("--rebuilt-rows", action="store_true",
                     help="keep no fp16 weight: outlier rows rebuilt from the codes")
     ap.add_argument("--bias", action="store_true", help="add an fp16 bias [N]")
+    ap.add_argument("--zero-point", action="store_true",
+                    help="zero-point (unsigned) activation codes: int8_linear_zp")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every step from Python instead of replaying a captured graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -186,14 +190,18 @@ def main():
             s = (Xd.clone(), Wq.clone(), sw.clone(), Wd.clone())
         ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
         Y = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
-        sets.append((*s, ws, Y))
+        S = pkg.weight_code_sums(s[1]) if args.zero_point else None   # once per layer
+        sets.append((*s, ws, Y, S))
 
     bias_t = (torch.randn(w.N, device=dev) * 0.1).half() if args.bias else None
 
     def step(i):
-        x, q, s, wf, ws, y = sets[i % R]
-        pkg.linear(x, q, s, None if args.rebuilt_rows else wf, w.threshold, workspace=ws, out=y,
-                   bias=bias_t)
+        x, q, s, wf, ws, y, S = sets[i % R]
+        rows = None if args.rebuilt_rows else wf
+        if args.zero_point:
+            pkg.linear_zp(x, q, s, S, rows, w.threshold, workspace=ws, out=y, bias=bias_t)
+        else:
+            pkg.linear(x, q, s, rows, w.threshold, workspace=ws, out=y, bias=bias_t)
 
     for i in range(args.warmup):
         step(i)
@@ -257,7 +265,7 @@ def main():
         ms_launch = float(per_launch.mean())
 
     value = w.int_ops / (ms_per_step * 1e-3) / 1e12
-    kname, bound, files = dominant_kernel(w)
+    kname, bound, files = dominant_kernel(w, args.zero_point)
     src_hash = kernel_source_hash(files)
     if bound == "hbm":
         alg = algorithmic_bytes(w)
@@ -268,7 +276,8 @@ def main():
         achieved = w.int_ops / (ms_launch * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
                 "unit": "TOPS", "frac": round(achieved / PEAK_INT8_TOPS, 4)}
-    tr = TRAFFIC.get((kname, w.name))
+    # counter figures were taken on the default layer (fp16 outlier rows, absmax codes)
+    tr = None if (args.zero_point or args.rebuilt_rows) else TRAFFIC.get((kname, w.name))
     roof["traffic"] = tr["bytes"] if tr and tr["src"] == src_hash else None
     roof["kernel"] = kname
     roof["kernel_ms"] = round(ms_launch, 5)
@@ -296,6 +305,7 @@ def main():
                    "buffer_sets": R, "x_dtype": "fp16", "y_dtype": "fp16",
                    "outlier_rows": "rebuilt from codes" if args.rebuilt_rows else "fp16 weight",
                    "bias": bool(args.bias),
+                   "activation_codes": "zero-point" if args.zero_point else "absmax",
                    "launch": "eager" if args.no_graph else "hip_graph"},
         "roofline": roof,
     }
@@ -303,7 +313,7 @@ def main():
         result["eager_ms_per_step"] = round(eager_ms, 5)
 
     if not args.no_cpu_baseline:
-        if args.rebuilt_rows or args.bias:
+        if args.rebuilt_rows or args.bias or args.zero_point:
             raise SystemExit("the CPU baseline and parity check cover the default layer only "
                              "(run with --no-cpu-baseline)")
         cb, ref, Wq_o, sw_o = cpu_baseline(w, X, W)
