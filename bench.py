@@ -62,11 +62,12 @@ def algorithmic_bytes(w):
             + 4 * w.N + 4 * w.M + 4 * w.n_out)
 
 
-def dominant_kernel(w, zero_point=False):
-    if zero_point and w.M <= 16:   # activation kernels, then the streaming kernel
-        return "decode_stream_kernel", "hbm", ["decode.hip", "common.h"]
-    if w.M <= 16 and w.K <= 8192 and w.M * ((w.K + 63) // 64 * 64) <= 65536 and (w.M <= 8 or w.K <= 4096):
-        return "decode_kernel", "hbm", ["decode.hip", "common.h"]
+def dominant_kernel(w):
+    """The kernel that carries the call: the fused small-M kernel (M <= 16,
+    K <= 4096), the streaming small-M kernel (M <= 16, larger K) or the GEMM."""
+    if w.M <= 16:
+        name = "decode_kernel" if w.K <= 4096 else "decode_stream_kernel"
+        return name, "hbm", ["decode.hip", "common.h"]
     return "gemm_i8_kernel", "mfma", ["gemm.hip", "common.h"]
 
 
@@ -265,7 +266,7 @@ def main():
         ms_launch = float(per_launch.mean())
 
     value = w.int_ops / (ms_per_step * 1e-3) / 1e12
-    kname, bound, files = dominant_kernel(w, args.zero_point)
+    kname, bound, files = dominant_kernel(w)
     src_hash = kernel_source_hash(files)
     if bound == "hbm":
         alg = algorithmic_bytes(w)

@@ -66,7 +66,7 @@ struct DecodeArgs {
   float* sx;
   int8_t* Xq;
   uint16_t* X_O;
-  const int32_t* zp = nullptr;     // zero-point mode (stream kernel only)
+  int32_t* zp = nullptr;           // zero-point mode: zero points (read, or written by the fused kernel)
   const int32_t* wsum = nullptr;
 };
 
@@ -103,19 +103,53 @@ __device__ __forceinline__ v4i codes16(const v4i (&x)[2], float inv65) {
   return a;
 }
 
+// Zero-point codes of 16 values: clamp(round_half_away(x * inv) + zp, 0, 255)
+// - 128 per byte, with inv65 = inv * 2^16 as above; |x * inv| <= 255, so the
+// fixed-point rounding is exact.  Zeroed outlier values give zp - 128.
+__device__ __forceinline__ v4i codes16_zp(const v4i (&x)[2], float inv65, int zp) {
+  v4i a;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = (int)rhaz_sum(h2f((uint16_t)half_at(x, 4 * i + e)) * inv65) >> 16;
+      int q = r + zp;
+      q = q < 0 ? 0 : (q > 255 ? 255 : q);
+      b[e] = (uint32_t)(q - 128) & 0xffu;
+    }
+    a[i] = (int)(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24));
+  }
+  return a;
+}
+
+// Order-preserving u16 key of an fp16 value (finite values): positive values
+// get the top bit set, negative ones are bit-inverted; applied to both halves.
+__device__ __forceinline__ uint32_t f16x2_keys(uint32_t x) {
+  const uint32_t neg = ((x >> 15) & 0x00010001u) * 0xffffu;
+  return x ^ (0x80008000u | (neg & 0x7fff7fffu));
+}
+__device__ __forceinline__ float f16_of_key(uint32_t k) {
+  return h2f((uint16_t)(k & 0x8000u ? k ^ 0x8000u : ~k & 0xffffu));
+}
+
 // KS: k-steps of 64 per wave (>= ceil(K / 64 / 8));
 // R: k-steps packed into one register set (M <= 16 / R): lane row lr holds X
 //    row lr % (16/R) of k-step (lr / (16/R)) of the set, so padding rows >= M
 //    carry real data instead of zeros; the codes are moved to the MFMA operand
 //    rows by lane shuffles;
 // PRE: weight k-steps issued before the activation stage.
-template <int KS, int R, int PRE>
+// ZP: zero-point codes (row minimum and maximum instead of the absmax, codes
+//    minus 128, accumulators corrected by (128 - zp) * wsum, scale range / 255).
+template <int KS, int R, int PRE, bool ZP>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   constexpr int MR = 16 / R;         // X rows per slot
   constexpr int NSET = KS / R;       // register sets
   __shared__ v4i sRed[kDecWaves][kDecP][64];        // int32 partials, D layout
   __shared__ float sYo[kDecWaves][16][kDecCols];    // fp32 outlier partials [m][col]
   __shared__ uint32_t sRowMax[kDecWaves][16];       // per chunk, per row
+  __shared__ uint32_t sRowMin[ZP ? kDecWaves : 1][16];   // zero-point mode: minimum key
+  __shared__ int sZp[16];
   __shared__ int sCnt[kDecWaves];                   // outliers per K chunk
   __shared__ int sHasOut[kDecWaves];
   __shared__ float sSx[16];
@@ -148,6 +182,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   }
   const int ne = n0 + (wave & (kDecP - 1)) * 16 + lr;   // epilogue feature of this lane
   const float swv = d.sw[ne < N ? ne : N - 1];
+  const int wsn = ZP ? d.wsum[ne < N ? ne : N - 1] : 0;
   // bias (zero-sized resource when there is none: the load reads nothing)
   const uint16_t bvb = buf_load_u16(make_rsrc(d.bias, d.bias ? (uint32_t)N * 2u : 0u),
                                     (uint32_t)(ne < N ? ne : N - 1) * 2u);
@@ -174,6 +209,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   // zeroed in registers (so the row max and the codes need no masking).
   const uint32_t T = d.thr;
   u16x2 rmv = {0, 0};
+  u16x2 kmax = {0, 0}, kmin = {0xffff, 0xffff};   // zero-point mode: value keys
   uint32_t hm[NSET];         // this lane's 16 columns: outlier bits (0 if the set has none)
   uint32_t hitsets = 0;      // uniform: sets with an outlier column
 #pragma unroll
@@ -204,6 +240,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
       hitsets |= 1u << j;
     }
     rmv = __builtin_elementwise_max(rmv, smax);
+    if constexpr (ZP) {   // outlier values are zeroed by now: they count as 0
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const u16x2 k2 = __builtin_bit_cast(u16x2, f16x2_keys((uint32_t)xr[j][i >> 2][i & 3]));
+        kmax = __builtin_elementwise_max(kmax, k2);
+        kmin = __builtin_elementwise_min(kmin, k2);
+      }
+    }
   }
   // outlier columns of chunk step t as a wave-wide mask: bit l <-> column
   // (s0+t)*64 + l, so ascending column order is (t, bit)
@@ -253,13 +297,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     return rebuild ? h2f(dequant_w16((int)(int8_t)wc[j], swl)) : h2f(wo[j]);
   };
 
-  uint32_t rm = rmv[0] > rmv[1] ? rmv[0] : rmv[1];
+  uint32_t rm, rn = 0;
+  if constexpr (ZP) {
+    rm = kmax[0] > kmax[1] ? kmax[0] : kmax[1];
+    rn = kmin[0] < kmin[1] ? kmin[0] : kmin[1];
+  } else {
+    rm = rmv[0] > rmv[1] ? rmv[0] : rmv[1];
+  }
 #pragma unroll
   for (int off = MR; off < 64; off <<= 1) {   // over the slots, then the column groups
     const uint32_t o = __shfl_xor(rm, off, 64);
     rm = o > rm ? o : rm;
+    if constexpr (ZP) {
+      const uint32_t o2 = __shfl_xor(rn, off, 64);
+      rn = o2 < rn ? o2 : rn;
+    }
   }
   if (lane < MR) sRowMax[kc][lane] = rm;
+  if (ZP && lane < MR) sRowMin[ZP ? kc : 0][lane] = rn;
   if (lane == 0) sCnt[kc] = wcount;
   lds_sync();
 
@@ -269,8 +324,29 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   uint32_t mx = 0;
 #pragma unroll
   for (int w = 0; w < kDecWaves; ++w) mx = sRowMax[w][rr] > mx ? sRowMax[w][rr] : mx;
-  const float inv65 = quant_scale(h2f((uint16_t)mx)) * 65536.0f;
-  if (wave == 0 && lane < 16) sSx[lane] = lane < MR ? h2f((uint16_t)mx) : 0.0f;
+  float inv65, rowscale;
+  int zpv = 0;
+  if constexpr (ZP) {
+    // [blog, "Introduction to model quantization"], the unsigned scheme: the
+    // row's range, widened to contain 0, maps onto [0, 255]
+    uint32_t mn = 0xffffu;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) mn = sRowMin[w][rr] < mn ? sRowMin[w][rr] : mn;
+    const float hi = __builtin_fmaxf(f16_of_key(mx), 0.0f);
+    const float lo = __builtin_fminf(f16_of_key(mn), 0.0f);
+    const float range = hi - lo;
+    const float inv = range > 0.0f ? 255.0f / range : 0.0f;
+    zpv = (int)__builtin_roundf(-lo * inv);
+    inv65 = inv * 65536.0f;
+    rowscale = range / 255.0f;
+  } else {
+    rowscale = h2f((uint16_t)mx);
+    inv65 = quant_scale(rowscale) * 65536.0f;
+  }
+  if (wave == 0 && lane < 16) {
+    sSx[lane] = lane < MR ? rowscale : 0.0f;
+    sZp[lane] = lane < MR ? zpv : 0;
+  }
   v4i acc[kDecP];
 #pragma unroll
   for (int c = 0; c < kDecP; ++c) acc[c] = v4i{0, 0, 0, 0};
@@ -281,7 +357,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   v4i a[KS];
 #pragma unroll
   for (int j = 0; j < NSET; ++j) {
-    const v4i cj = codes16(xr[j], inv65);
+    v4i cj;
+    if constexpr (ZP) {
+      // positions past K or past this wave's chunk must contribute nothing:
+      // their code is 0 (the zero point's code is not)
+      const int tq = s0 + j * R + q;
+      cj = tq < s1 && tq * 64 + 16 * g < K ? codes16_zp(xr[j], inv65, zpv) : v4i{0, 0, 0, 0};
+    } else {
+      cj = codes16(xr[j], inv65);
+    }
 #pragma unroll
     for (int qq = 0; qq < R; ++qq) {
       const int t = j * R + qq;
@@ -383,6 +467,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     }
     if (wave == 0) {
       if (lane < M) d.sx[lane] = sSx[lane];
+      if (ZP && lane < M) d.zp[lane] = sZp[lane];
       if (lane == 0) {
         int tot = 0;
         for (int w = 0; w < kDecWaves; ++w) tot += sCnt[w];
@@ -409,7 +494,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   // ---- epilogue ----------------------------------------------------------------------
   const int n = ne;
   if (n >= N || mb >= M) return;
-  const float swn = swv * (1.0f / 16129.0f);
+  const float swn = swv * (ZP ? 1.0f / 127.0f : 1.0f / 16129.0f);
+  if constexpr (ZP) {   // sum (q - zp) w = sum (q - 128) w + (128 - zp) S[n], mod 2^32
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (mb + r < M) tot[r] = (int)((uint32_t)tot[r] + (uint32_t)(128 - sZp[mb + r]) * (uint32_t)wsn);
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = mb + r;
@@ -556,6 +646,23 @@ uint32_t threshold_bits(float t) {
 
 typedef void (*kfn)(DecodeArgs);
 
+namespace {
+// Fused kernel instantiation for M <= 16, K <= 4096.
+template <bool ZP>
+kfn fused_decode_kernel(int M, int K) {
+  const int steps = ((K + 63) / 64 + kDecWaves - 1) / kDecWaves;   // k-steps per wave
+  const int ks = steps <= 1 ? 1 : steps <= 2 ? 2 : steps <= 4 ? 4 : 8;
+  int r = 1;   // k-steps packed per register set: M <= 16 / r, r <= ks
+  while (r < ks && M <= 16 / (2 * r)) r *= 2;
+  kfn f = nullptr;
+#define I8L_DEC(KS_, R_) if (ks == KS_ && r == R_) f = decode_kernel<KS_, R_, 2, ZP>;
+  I8L_DEC(1, 1) I8L_DEC(2, 1) I8L_DEC(2, 2) I8L_DEC(4, 1) I8L_DEC(4, 2) I8L_DEC(4, 4)
+  I8L_DEC(8, 1) I8L_DEC(8, 2) I8L_DEC(8, 4) I8L_DEC(8, 8)
+#undef I8L_DEC
+  return f;
+}
+}  // namespace
+
 hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
                          int N, const uint16_t* W_rows, const uint16_t* bias, float threshold,
                          bool enabled, uint16_t* Y, const Workspace& ws, hipStream_t stream) {
@@ -563,16 +670,7 @@ hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, cons
   DecodeArgs d{X, M, K, N, Wq, sw, W_rows, bias, thr, Y, ws.n_out, ws.idx, ws.sx, ws.Xq, ws.X_O};
   const dim3 grid((N + kDecCols - 1) / kDecCols), block(kDecThreads);
   if (decode_fits(M, K)) {
-    const int steps = ((K + 63) / 64 + kDecWaves - 1) / kDecWaves;   // k-steps per wave
-    const int ks = steps <= 1 ? 1 : steps <= 2 ? 2 : steps <= 4 ? 4 : 8;
-    int r = 1;   // k-steps packed per register set: M <= 16 / r, r <= ks
-    while (r < ks && M <= 16 / (2 * r)) r *= 2;
-    kfn f = nullptr;
-#define I8L_DEC(KS_, R_) if (ks == KS_ && r == R_) f = decode_kernel<KS_, R_, 2>;
-    I8L_DEC(1, 1) I8L_DEC(2, 1) I8L_DEC(2, 2) I8L_DEC(4, 1) I8L_DEC(4, 2) I8L_DEC(4, 4)
-    I8L_DEC(8, 1) I8L_DEC(8, 2) I8L_DEC(8, 4) I8L_DEC(8, 8)
-#undef I8L_DEC
-    hipLaunchKernelGGL(f, grid, block, 0, stream, d);
+    hipLaunchKernelGGL(fused_decode_kernel<false>(M, K), grid, block, 0, stream, d);
     return hipGetLastError();
   }
   hipError_t e = launch_quantize_activation(X, M, K, threshold, enabled, ws, stream);
@@ -588,10 +686,14 @@ hipError_t launch_decode_zp(const uint16_t* X, int M, int K, const int8_t* Wq, c
   const uint32_t thr = enabled ? threshold_bits(threshold) : 0x10000u;
   DecodeArgs d{X, M, K, N, Wq, sw, W_rows, bias, thr, Y, ws.n_out, ws.idx, ws.sx, ws.Xq, ws.X_O,
                ws.zp, wsum};
+  const dim3 grid((N + kDecCols - 1) / kDecCols), block(kDecThreads);
+  if (decode_fits(M, K)) {
+    hipLaunchKernelGGL(fused_decode_kernel<true>(M, K), grid, block, 0, stream, d);
+    return hipGetLastError();
+  }
   hipError_t e = launch_quantize_activation(X, M, K, threshold, enabled, ws, stream, true);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_stream_kernel, dim3((N + kDecCols - 1) / kDecCols), dim3(kDecThreads),
-                     0, stream, d);
+  hipLaunchKernelGGL(decode_stream_kernel, grid, block, 0, stream, d);
   return hipGetLastError();
 }
 

@@ -87,8 +87,9 @@ bool decode_fits(int M, int K);
 hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
                          int N, const uint16_t* W_rows, const uint16_t* bias, float threshold,
                          bool enabled, uint16_t* Y, const Workspace& ws, hipStream_t stream);
-// Zero-point mode for M <= 16: the activation kernels (zero-point codes), then
-// the streaming kernel with the corrected epilogue.
+// Zero-point mode for M <= 16: the fused kernel when decode_fits(M, K), else the
+// activation kernels (zero-point codes), then the streaming kernel with the
+// corrected epilogue.
 hipError_t launch_decode_zp(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
                             const int32_t* wsum, int N, const uint16_t* W_rows,
                             const uint16_t* bias, float threshold, bool enabled, uint16_t* Y,

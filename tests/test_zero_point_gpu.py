@@ -147,6 +147,11 @@ def _linear_cases():
     yield "decode_m16", 16, 4096, 512, 3, 6.0, "offset", True, False
     yield "decode_k8192", 8, 8192, 256, 5, 6.0, "negative", False, True
     yield "decode_k_mod64", 5, 1040, 200, 2, 6.0, "offset", False, False
+    yield "decode_m3_k272", 3, 272, 130, 1, 6.0, "negative", True, True
+    yield "decode_m12_k2048", 12, 2048, 300, 2, 6.0, "positive", False, True
+    yield "decode_m4_k4096", 4, 4096, 520, 3, 6.0, "offset", True, False
+    yield "decode_m1_k16", 1, 16, 64, 0, 6.0, "offset", False, True
+    yield "decode_m2_k3088", 2, 3088, 70, 1, 6.0, "offset", True, True
     yield "prefill_m17", 17, 1024, 600, 2, 6.0, "positive", True, True
     yield "prefill_ragged", 300, 272, 520, 5, 6.0, "offset", True, True
     yield "prefill_tiles", 513, 1040, 769, 8, 6.0, "offset", False, False
