@@ -16,11 +16,12 @@
 //     dependency: one LDS exchange and one barrier;
 //   * the codes are computed in registers, already in MFMA operand layout;
 //   * each wave adds the fp16 product of its own outlier columns (weight rows
-//     loaded as soon as the columns are known, long before they are needed);
+//     of up to four columns loaded as soon as the columns are known, long
+//     before they are needed; a fifth and later ones are read at the end);
 //   * a second barrier sums the 8 waves' int32 partials (exact) and fp32
 //     outlier partials, then the epilogue dequantizes and stores fp16.
 // The weight is streamed with 16-byte buffer loads (default cache policy:
-// measured faster here than the nontemporal hint); the first PRE
+// measured faster here than the nontemporal hint); the first PRE (3)
 // k-steps of a wave are issued before the activation stage and the rest right
 // after its barrier.  The K chunk a wave streams is rotated by the workgroup
 // index (measured ~15% more HBM bandwidth than all starting at chunk 0).
@@ -43,7 +44,7 @@ constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kDecP = 4;                      // 16-feature blocks per workgroup
 constexpr int kDecCols = 16 * kDecP;
 constexpr int kDecMaxKS = 8;                  // fused kernel: k-steps per wave
-constexpr int kDecOutPre = 2;                 // outlier columns per wave preloaded
+constexpr int kDecOutPre = 4;                 // outlier columns per wave preloaded
 constexpr int kDecMaxOutLds = 64;             // stream kernel: outlier values in LDS
 constexpr int kDecOutReg = 8;                 // stream kernel: outlier weights per lane
 
@@ -655,7 +656,7 @@ kfn fused_decode_kernel(int M, int K) {
   int r = 1;   // k-steps packed per register set: M <= 16 / r, r <= ks
   while (r < ks && M <= 16 / (2 * r)) r *= 2;
   kfn f = nullptr;
-#define I8L_DEC(KS_, R_) if (ks == KS_ && r == R_) f = decode_kernel<KS_, R_, 2, ZP>;
+#define I8L_DEC(KS_, R_) if (ks == KS_ && r == R_) f = decode_kernel<KS_, R_, 3, ZP>;
   I8L_DEC(1, 1) I8L_DEC(2, 1) I8L_DEC(2, 2) I8L_DEC(4, 1) I8L_DEC(4, 2) I8L_DEC(4, 4)
   I8L_DEC(8, 1) I8L_DEC(8, 2) I8L_DEC(8, 4) I8L_DEC(8, 8)
 #undef I8L_DEC
