@@ -42,7 +42,7 @@ PEAK_INT8_TOPS = 5000.0
 # (profiles/traffic-decode.md: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB, the
 # factors a 512 MiB device copy gives).
 TRAFFIC = {
-    ("decode_kernel", "decode"): {"bytes": 68681526, "src": "0c2b4e6bcd263a94"},
+    ("decode_kernel", "decode"): {"bytes": 73882049, "src": "cab274b25c8fb318"},
     ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2221329466, "src": "ce1d711bf3a6b42f"},
     ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5551346321, "src": "ce1d711bf3a6b42f"},
 }
