@@ -403,41 +403,74 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
       return a.W_rows ? (uint32_t)a.W_rows[(size_t)k * N + n]
                       : (uint32_t)dequant_w16(a.Wq[(size_t)n * K + k], a.sw[n]);
     };
-    // X_O[., j0 ..] and rows idx[j0 ..] of W (transposed to [column][outlier]);
-    // zero past n_out and outside the matrix
-    auto stage_outliers = [&](int j0) {
-      for (int q = t; q < kBM * kOutC; q += kGemmThreads) {
-        const int row = q / kOutC, c = q % kOutC;
-        const int gm = m0 + row;
-        const int jj = j0 + c * 8;
-        v4i v = {0, 0, 0, 0};
-        if (gm < M && jj < n_out) {
-          const uint16_t* src = a.X_O + (size_t)gm * K + jj;
-          if (jj + 8 <= n_out) {
-            v = *reinterpret_cast<const v4i*>(src);
-          } else {
-            uint32_t w[4] = {0, 0, 0, 0};
-            for (int e = 0; jj + e < n_out; ++e) w[e >> 1] |= (uint32_t)src[e] << ((e & 1) * 16);
-            v = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-          }
-        }
-        *reinterpret_cast<v4i*>(&sAo[row * kOutG + och(row, c)]) = v;
+    // X_O[., 0 .. 96) and rows idx[0 .. 96) of W (transposed to
+    // [column][outlier]); zero past n_out and outside the matrix.  All loads
+    // go out before any store and none sits behind a branch (X_O rows past
+    // the tile read 0 from the buffer resource; indices past n_out read entry
+    // 0 and are masked), so the staging costs about one memory round trip.
+    auto stage_outliers = [&]() {
+      constexpr int kPerT = kBM * kOutC / kGemmThreads;   // X_O chunks per thread
+      const int rows = min(M - m0, kBM);
+      const buf_rsrc rxo = make_rsrc(a.X_O + (size_t)m0 * K, (uint32_t)rows * (uint32_t)K * 2u);
+      v4i xv[kPerT];
+#pragma unroll
+      for (int i = 0; i < kPerT; ++i) {
+        const int q = t + i * kGemmThreads, row = q / kOutC, c = q % kOutC;
+        xv[i] = buf_load16(rxo, (uint32_t)(row * K + c * 8) * 2u);
       }
       const int col = t & (kBN - 1);   // 512 threads: two per column, half the chunks each
-      const int gn = n0 + col;
-      for (int c = (t >> 8) * (kOutC / 2); c < ((t >> 8) + 1) * (kOutC / 2); ++c) {
-        uint32_t w[4] = {0, 0, 0, 0};
+      const int gn = n0 + col, gnc = gn < N ? gn : N - 1;
+      const float sn = a.W_rows ? 0.0f : a.sw[gnc];
+      // the thread's 6 chunks of 8 outlier rows in two passes of 3 (bounded
+      // registers; the X_O loads above are still in flight during the first)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = j0 + c * 8 + e;
-          const uint32_t h = (j < n_out && gn < N) ? wbits(a.idx[j], gn) : 0u;
-          w[e >> 1] |= h << ((e & 1) * 16);
+      for (int pass = 0; pass < 2; ++pass) {
+        const int cb = (t >> 8) * (kOutC / 2) + pass * (kOutC / 4);
+        uint32_t hv[kOutC / 4][8];
+        if (a.W_rows) {   // uniform
+#pragma unroll
+          for (int ci = 0; ci < kOutC / 4; ++ci)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int j = (cb + ci) * 8 + e;
+              hv[ci][e] = a.W_rows[(size_t)a.idx[j < n_out ? j : 0] * N + gnc];
+            }
+        } else {
+#pragma unroll
+          for (int ci = 0; ci < kOutC / 4; ++ci)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int j = (cb + ci) * 8 + e;
+              hv[ci][e] = dequant_w16(a.Wq[(size_t)gnc * K + a.idx[j < n_out ? j : 0]], sn);
+            }
         }
-        *reinterpret_cast<v4i*>(&sBo[col * kOutG + och(col, c)]) =
-            v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+        if (pass == 0) {
+#pragma unroll
+          for (int i = 0; i < kPerT; ++i) {
+            const int q = t + i * kGemmThreads, row = q / kOutC, c = q % kOutC;
+            const int nv = n_out - c * 8;   // valid halves of this chunk
+            v4i v = xv[i];
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+              v[d] &= (int)((2 * d < nv ? 0xffffu : 0u) | (2 * d + 1 < nv ? 0xffff0000u : 0u));
+            *reinterpret_cast<v4i*>(&sAo[row * kOutG + och(row, c)]) = v;
+          }
+        }
+#pragma unroll
+        for (int ci = 0; ci < kOutC / 4; ++ci) {
+          uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = (cb + ci) * 8 + e;
+            const uint32_t h = (j < n_out && gn < N) ? (hv[ci][e] & 0xffffu) : 0u;
+            w[e >> 1] |= h << ((e & 1) * 16);
+          }
+          *reinterpret_cast<v4i*>(&sBo[col * kOutG + och(col, cb + ci)]) =
+              v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+        }
       }
     };
-    if (ngroups == 1) stage_outliers(0);
+    if (ngroups == 1) stage_outliers();
     __syncthreads();
 
 #pragma unroll
