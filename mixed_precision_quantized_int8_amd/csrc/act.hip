@@ -52,10 +52,12 @@ __global__ __launch_bounds__(kColThreads) void colflags_kernel(const uint16_t* _
                                                               uint32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  __shared__ uint32_t s_bits[kColThreads / 64][kColStrip / 32];
   const int c = blockIdx.x * kColStrip + lane * 8;
-  if (c >= K) return;   // K % 16 == 0, so c < K means all 8 columns are in range
+  // K % 16 == 0, so c < K means all 8 columns are in range; lanes past K scan
+  // no rows (they stay in for the block-wide combine below)
   const int r0 = blockIdx.y * rows_per_block;
-  const int r1 = min(M, r0 + rows_per_block);
+  const int r1 = c < K ? min(M, r0 + rows_per_block) : r0;
   const uint16_t* base = X + c;
   uint32_t mx[4] = {0, 0, 0, 0};   // packed pairs of |fp16| bit patterns
   int r = r0 + wave;
@@ -93,7 +95,20 @@ __global__ __launch_bounds__(kColThreads) void colflags_kernel(const uint16_t* _
     const uint32_t h = (mx[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
     if (h2f((uint16_t)h) >= threshold) bits |= 1u << e;
   }
-  if (bits) atomicOr(flags + (c >> 5), bits << (c & 31));
+  // one atomic per flag word and block: the 4 lanes of a word, then the 4
+  // waves (which scanned other rows of the same columns), are combined first
+  uint32_t wbits = bits << (c & 31);
+  wbits |= __shfl_xor(wbits, 1, 64);
+  wbits |= __shfl_xor(wbits, 2, 64);
+  if ((lane & 3) == 0) s_bits[wave][lane >> 2] = wbits;
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < kColStrip / 32) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int w = 0; w < kColThreads / 64; ++w) v |= s_bits[w][t];
+    if (v) atomicOr(flags + blockIdx.x * (kColStrip / 32) + t, v);
+  }
 }
 
 // Exclusive block-wide prefix sum (blockDim.x threads, multiple of 64).
