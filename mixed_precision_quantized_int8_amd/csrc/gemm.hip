@@ -41,18 +41,18 @@
 //   * tiles are handed out XCD by XCD: workgroup b runs on XCD b % 8, and each
 //     XCD takes a contiguous range of tiles ordered in groups of 8 tile-rows so
 //     that concurrently running tiles share operand panels in that XCD's L2.
-// Epilogue, one 32-column block of the wave tile at a time: the int32
+// Epilogue, one 32x32 block of the wave tile at a time: the int32
 // accumulators of the block are dequantized to fp32 (acc * sx * sw / 127^2),
 // then the outlier product is accumulated onto them with
-// v_mfma_f32_32x32x16_f16 from X_O[256 x 32] and the matching 32 weight rows
-// (transposed to [256 x 32]) staged in LDS, and the block is stored as fp16.
-// With at most 32 outlier columns the staging happens once per tile.  The
-// outlier count is read from device memory, so no host synchronization is
-// needed.
+// v_mfma_f32_32x32x16_f16 from X_O [256 x 96] and the matching weight rows
+// (transposed to [256 x 96]) staged in LDS once per tile (up to 96 outlier
+// columns; beyond that the fragments are read from memory per block), the
+// bias is added, and the block is stored as fp16.  The outlier count is read
+// from device memory, so no host synchronization is needed.
 // Zero-point mode (ZP): Xq holds unsigned codes minus 128 and sx the row's
-// range / 255; the int32 block gets (128 - zp[m]) * wsum[n] added (exact in
-// int32 arithmetic, wrap-around included, for K within the zero-point limit)
-// before the dequantization by sx * sw / 127.
+// range / 255; the accumulators start at (128 - zp[m]) * wsum[n] (the split
+// tail adds it to the summed partials), exact in int32 for K within the
+// zero-point limit, and are dequantized by sx * sw / 127.
 #include <algorithm>
 
 #include "common.h"
