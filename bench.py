@@ -43,8 +43,8 @@ PEAK_INT8_TOPS = 5000.0
 # factors a 512 MiB device copy gives).
 TRAFFIC = {
     ("decode_kernel", "decode"): {"bytes": 73882049, "src": "cab274b25c8fb318"},
-    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2221329466, "src": "ce1d711bf3a6b42f"},
-    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5551346321, "src": "ce1d711bf3a6b42f"},
+    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2234511970, "src": "67c44cb98a422e57"},
+    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5558268378, "src": "67c44cb98a422e57"},
 }
 
 
