@@ -407,3 +407,40 @@ def test_linear_rebuilt_outlier_rows(lib, name, M, K, N, n_out):
     # rebuilt weight values (a sanity check that the rebuilt path is used)
     r16 = O.int8_linear(X, Wq_o, sw_o, W, 6.0)
     assert not np.array_equal(r16["Y64"], r["Y64"])
+
+
+# ---------------------------------------------------------------------------------
+# a sweep of seeded random shapes through both activation codes
+# ---------------------------------------------------------------------------------
+def _random_cases(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        M = int(rng.choice([1, 2, 3, 5, 8, 11, 16, 17, 33, 100, 257, 300]))
+        K = int(16 * rng.integers(1, 160))            # 16 .. 2544, ragged against 64 and 128
+        N = int(rng.integers(1, 700))
+        n_out = int(min(K, rng.choice([0, 1, 2, 5, 20])))
+        yield (f"r{i}_{M}x{K}x{N}_o{n_out}", M, K, N, n_out, bool(rng.integers(0, 2)),
+               bool(rng.integers(0, 2)), bool(rng.integers(0, 2)), int(rng.integers(0, 1000)))
+
+
+@pytest.mark.parametrize("case", list(_random_cases()), ids=lambda c: c[0])
+def test_linear_random_shapes(lib, case):
+    name, M, K, N, n_out, with_bias, pass_w, zp, seed = case
+    say(f"random {name} bias={with_bias} W={'fp16' if pass_w else 'rebuilt'} zp={zp}")
+    X, W, _ = wl.make_small(M, K, N, seed=seed, n_out=n_out)
+    b = (np.random.default_rng(seed).standard_normal(N) * 0.5).astype(np.float16) \
+        if with_bias else None
+    Xd, Wd = dev(X), dev(W)
+    Wq, sw = lib.quantize_weight(Wd)
+    bd = dev(b) if b is not None else None
+    Wq_o, sw_o = O.quantize_weight(W)
+    np.testing.assert_array_equal(host(Wq), Wq_o)
+    W_rows = W if pass_w else O.dequantize_weight(Wq_o, sw_o)
+    if zp:
+        S = lib.weight_code_sums(Wq)
+        Y = lib.linear_zp(Xd, Wq, sw, S, Wd if pass_w else None, 6.0, bias=bd)
+        r = O.int8_linear_zp(X, Wq_o, sw_o, W_rows, 6.0, bias=b)
+    else:
+        Y = lib.linear(Xd, Wq, sw, Wd if pass_w else None, 6.0, bias=bd)
+        r = O.int8_linear(X, Wq_o, sw_o, W_rows, 6.0, bias=b)
+    assert_y(host(Y), r["Y64"], what=name)
