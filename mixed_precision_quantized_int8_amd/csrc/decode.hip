@@ -21,10 +21,11 @@
 //   * a second barrier sums the 8 waves' int32 partials (exact) and fp32
 //     outlier partials, then the epilogue dequantizes and stores fp16.
 // The weight is streamed with 16-byte buffer loads (default cache policy:
-// measured faster here than the nontemporal hint); the first PRE (3)
-// k-steps of a wave are issued before the activation stage and the rest right
-// after its barrier.  The K chunk a wave streams is rotated by the workgroup
-// index (measured ~15% more HBM bandwidth than all starting at chunk 0).
+// measured faster here than the nontemporal hint); the first PRE (2)
+// k-steps of a wave are issued before the activation stage and the rest as
+// soon as the wave's own row reduction is done, before the workgroup barrier.
+// The K chunk a wave streams is rotated by the workgroup index (measured ~15%
+// more HBM bandwidth than all starting at chunk 0).
 // Workgroup 0 also writes the intermediates (Xq, sx, outlier list, X_O) to the
 // workspace.
 //
@@ -314,12 +315,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
       rn = o2 < rn ? o2 : rn;
     }
   }
+  // the rest of the weight stream goes out before the barrier: a wave waiting
+  // there for the slowest wave of its workgroup keeps its loads in flight
+  load_b(kPre, KS);
   if (lane < MR) sRowMax[kc][lane] = rm;
   if (ZP && lane < MR) sRowMin[ZP ? kc : 0][lane] = rn;
   if (lane == 0) sCnt[kc] = wcount;
   lds_sync();
-
-  load_b(kPre, KS);
 
   // ---- codes and the int8 product, one register set at a time ---------------------
   uint32_t mx = 0;
@@ -656,7 +658,7 @@ kfn fused_decode_kernel(int M, int K) {
   int r = 1;   // k-steps packed per register set: M <= 16 / r, r <= ks
   while (r < ks && M <= 16 / (2 * r)) r *= 2;
   kfn f = nullptr;
-#define I8L_DEC(KS_, R_) if (ks == KS_ && r == R_) f = decode_kernel<KS_, R_, 3, ZP>;
+#define I8L_DEC(KS_, R_) if (ks == KS_ && r == R_) f = decode_kernel<KS_, R_, 2, ZP>;
   I8L_DEC(1, 1) I8L_DEC(2, 1) I8L_DEC(2, 2) I8L_DEC(4, 1) I8L_DEC(4, 2) I8L_DEC(4, 4)
   I8L_DEC(8, 1) I8L_DEC(8, 2) I8L_DEC(8, 4) I8L_DEC(8, 8)
 #undef I8L_DEC
