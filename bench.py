@@ -131,6 +131,28 @@ def copy_ceiling(torch, dev, mib=1024, reps=10):
     return 2 * (mib << 20) / (best * 1e-3) / 1e9
 
 
+def fp16_context(torch, w, sets, int8_ms, reps):
+    """Context only, not part of the library: the plain fp16 product X.W at the
+    same shape through torch.matmul (the vendor BLAS), over the same rotated
+    buffer sets, timed with events around `reps` back-to-back calls."""
+    out = torch.empty((w.M, w.N), dtype=torch.float16, device=sets[0][0].device)
+    R = len(sets)
+    for i in range(3):
+        torch.matmul(sets[i % R][0], sets[i % R][3], out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        torch.matmul(sets[i % R][0], sets[i % R][3], out=out)
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    return {"op": "torch.matmul fp16 X.W (vendor BLAS), eager launches, same buffer sets",
+            "ms_per_call": round(ms, 5),
+            "tflops": round(2.0 * w.M * w.N * w.K / (ms * 1e-3) / 1e12, 2),
+            "int8_layer_speedup": round(ms / int8_ms, 3)}
+
+
 def copy_calibration(mib):
     import torch
     dev = torch.device("cuda:0")
@@ -157,6 +179,8 @@ def main():
     ap.add_argument("--bias", action="store_true", help="add an fp16 bias [N]")
     ap.add_argument("--zero-point", action="store_true",
                     help="zero-point (unsigned) activation codes: int8_linear_zp")
+    ap.add_argument("--no-fp16-context", action="store_true",
+                    help="skip timing torch.matmul in fp16 at the same shape")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every step from Python instead of replaying a captured graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -323,6 +347,9 @@ def main():
     }
     if eager_ms is not None:
         result["eager_ms_per_step"] = round(eager_ms, 5)
+
+    if not args.no_fp16_context:
+        result["fp16_context"] = fp16_context(torch, w, sets, ms_per_step, min(K, 50))
 
     if not args.no_cpu_baseline:
         if args.rebuilt_rows or args.bias or args.zero_point:
