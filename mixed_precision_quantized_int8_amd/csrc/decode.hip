@@ -21,18 +21,21 @@
 //   * a second barrier sums the 8 waves' int32 partials (exact) and fp32
 //     outlier partials, then the epilogue dequantizes and stores fp16.
 // The weight is streamed with 16-byte buffer loads (default cache policy:
-// measured faster here than the nontemporal hint); the first PRE (2)
-// k-steps of a wave are issued before the activation stage and the rest as
-// soon as the wave's own row reduction is done, before the workgroup barrier.
+// measured faster here than the nontemporal hint), one 16-feature block after
+// the other, all k-steps of a block back to back (~8 % more bandwidth than
+// k-step by k-step across the blocks); the first PRE (4) loads of a wave are
+// issued before the activation stage and the rest as soon as the wave's own
+// row reduction is done, before the workgroup barrier.
 // The K chunk a wave streams is rotated by the workgroup index (measured ~15%
 // more HBM bandwidth than all starting at chunk 0).
 // Workgroup 0 also writes the intermediates (Xq, sx, outlier list, X_O) to the
 // workspace.
 //
-// Stream kernel (larger K, and the zero-point mode): reads the intermediates
-// written by the activation kernels and does the product and epilogue the same
-// way; in zero-point mode the accumulator is corrected by (128 - zp[m]) * wsum[n]
-// and dequantized with sx * sw / 127.
+// Stream kernel (K > 4096): reads the intermediates written by the activation
+// kernels and does the product and epilogue the same way, with the weight
+// registers double-buffered across the wave's K chunk; in zero-point mode the
+// accumulator is corrected by (128 - zp[m]) * wsum[n] and dequantized with
+// sx * sw / 127.
 #include <cmath>
 
 #include "common.h"
@@ -140,7 +143,8 @@ __device__ __forceinline__ float f16_of_key(uint32_t k) {
 //    row lr % (16/R) of k-step (lr / (16/R)) of the set, so padding rows >= M
 //    carry real data instead of zeros; the codes are moved to the MFMA operand
 //    rows by lane shuffles;
-// PRE: weight k-steps issued before the activation stage.
+// PRE: weight loads (of KS * kDecP, block by block) issued before the
+//    activation stage.
 // ZP: zero-point codes (row minimum and maximum instead of the absmax, codes
 //    minus 128, accumulators corrected by (128 - zp) * wsum, scale range / 255).
 template <int KS, int R, int PRE, bool ZP>
@@ -193,14 +197,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   const buf_rsrc rw = make_rsrc(d.Wq + (size_t)n0 * K, (uint32_t)(nrows * K));
   const uint32_t wb = (uint32_t)(lr * K + s0 * 64 + 16 * g);
   v4i fb[KS][kDecP];
-  auto load_b = [&](int u0, int u1) {
+  // load i of the wave's KS * kDecP: feature block i / KS, k-step i % KS, so
+  // the chunk's bytes of each weight row are requested back to back
+  auto load_b = [&](int i0, int i1) {
 #pragma unroll
-    for (int u = u0; u < u1; ++u)
-#pragma unroll
-      for (int c = 0; c < kDecP; ++c)
-        fb[u][c] = buf_load16(rw, wb + (uint32_t)(c * 16 * K + u * 64));
+    for (int i = i0; i < i1; ++i) {
+      const int c = i / KS, u = i % KS;
+      fb[u][c] = buf_load16(rw, wb + (uint32_t)(c * 16 * K + u * 64));
+    }
   };
-  constexpr int kPre = PRE < KS ? PRE : KS;
+  constexpr int kLoads = KS * kDecP;
+  constexpr int kPre = PRE < kLoads ? PRE : kLoads;
   load_b(0, kPre);
   __builtin_amdgcn_sched_barrier(0);   // the stream goes out before the stage below
 
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   }
   // the rest of the weight stream goes out before the barrier: a wave waiting
   // there for the slowest wave of its workgroup keeps its loads in flight
-  load_b(kPre, KS);
+  load_b(kPre, kLoads);
   if (lane < MR) sRowMax[kc][lane] = rm;
   if (ZP && lane < MR) sRowMin[ZP ? kc : 0][lane] = rn;
   if (lane == 0) sCnt[kc] = wcount;
@@ -389,9 +396,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int t = 0; t < KS; ++t)
+  for (int c = 0; c < kDecP; ++c)
 #pragma unroll
-    for (int c = 0; c < kDecP; ++c)
+    for (int t = 0; t < KS; ++t)
       acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], fb[t][c], acc[c], 0, 0, 0);
 
   // ---- outlier product of this chunk's columns (lane = feature n0 + lane) ----------
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
 // Stream kernel for small M with larger K: the activation kernels have written
 // the codes, the row scales and the outlier list to the workspace.
 __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d) {
-  constexpr int kU = 8;
+  constexpr int kU = 4;
   __shared__ v4i sRed[kDecWaves][kDecP][64];
   __shared__ float sXO[16][kDecMaxOutLds];
 
@@ -525,26 +532,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
   const int kc = (wave + blockIdx.x) % kDecWaves;
   const int s0 = kc * nsteps / kDecWaves, s1 = (kc + 1) * nsteps / kDecWaves;
 
-  v4i fb[kU][kDecP];
-  auto load_b = [&](int s) {
+  // weight registers double-buffered: the loads of the next kU k-steps are in
+  // flight while the current ones are multiplied; each buffer is filled one
+  // 16-feature block after the other, the k-steps of a block back to back.
+  // Steps past s1 read the zero page, so the loop needs no tail.
+  v4i fb[2][kU][kDecP];
+  auto load_b = [&](int b, int s) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int k = (s + u) * 64 + kl;
+    for (int c = 0; c < kDecP; ++c) {
 #pragma unroll
-      for (int c = 0; c < kDecP; ++c) {
+      for (int u = 0; u < kU; ++u) {
+        const int k = (s + u) * 64 + kl;
         const int n = n0 + c * 16 + lr;
         const bool in = s + u < s1 && n < N && k < K;
         const int8_t* p = in ? d.Wq + (size_t)n * K + k : g_dec_zero;
-        fb[u][c] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+        fb[b][u][c] = *reinterpret_cast<const v4i*>(p);
       }
     }
   };
-  load_b(s0);
-  v4i acc[kDecP];
-#pragma unroll
-  for (int c = 0; c < kDecP; ++c) acc[c] = v4i{0, 0, 0, 0};
-  for (int s = s0; s < s1; s += kU) {
-    v4i fa[kU];
+  auto load_a = [&](int s, v4i (&fa)[kU]) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int k = (s + u) * 64 + kl;
@@ -552,12 +558,32 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
       const void* p = in ? (const void*)(d.Xq + (size_t)lr * K + k) : (const void*)g_dec_zero;
       fa[u] = *reinterpret_cast<const v4i*>(p);
     }
+  };
+  v4i acc[kDecP];
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
+  for (int c = 0; c < kDecP; ++c) acc[c] = v4i{0, 0, 0, 0};
+  auto mma = [&](int b, const v4i (&fa)[kU]) {
 #pragma unroll
-      for (int c = 0; c < kDecP; ++c)
-        acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[u], fb[u][c], acc[c], 0, 0, 0);
-    if (s + kU < s1) load_b(s + kU);
+    for (int c = 0; c < kDecP; ++c)
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[u], fb[b][u][c], acc[c], 0, 0, 0);
+  };
+  load_b(0, s0);
+  for (int s = s0; s < s1; s += 2 * kU) {
+    v4i fa0[kU], fa1[kU];
+    // the codes go out before the next weight loads: the wait for them then
+    // leaves those loads in flight
+    load_a(s, fa0);
+    load_b(1, s + kU);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0, fa0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(s + kU, fa1);
+    load_b(0, s + 2 * kU);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1, fa1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   const int nout = *d.n_out;
@@ -658,7 +684,7 @@ kfn fused_decode_kernel(int M, int K) {
   int r = 1;   // k-steps packed per register set: M <= 16 / r, r <= ks
   while (r < ks && M <= 16 / (2 * r)) r *= 2;
   kfn f = nullptr;
-#define I8L_DEC(KS_, R_) if (ks == KS_ && r == R_) f = decode_kernel<KS_, R_, 2, ZP>;
+#define I8L_DEC(KS_, R_) if (ks == KS_ && r == R_) f = decode_kernel<KS_, R_, 4, ZP>;
   I8L_DEC(1, 1) I8L_DEC(2, 1) I8L_DEC(2, 2) I8L_DEC(4, 1) I8L_DEC(4, 2) I8L_DEC(4, 4)
   I8L_DEC(8, 1) I8L_DEC(8, 2) I8L_DEC(8, 4) I8L_DEC(8, 8)
 #undef I8L_DEC

@@ -67,6 +67,10 @@ WORKLOADS = {
         Workload("square_0pct", 8192, 8192, 8192, 1.0, 0.02, 0, 6.0, 100.0, seed=50),
         Workload("square_0.1pct", 8192, 8192, 8192, 1.0, 0.02, 8, 6.0, 100.0, seed=51),
         Workload("square_1pct", 8192, 8192, 8192, 1.0, 0.02, 82, 6.0, 100.0, seed=52),
+        # decode batch (8 tokens) through the two BLOOM-176B prefill layers
+        # above: the weight stream of the small-M path at K > 4096
+        Workload("decode_qkv", 8, 14336, 43008, 1.0, 0.02, 8, 8.0, 60.0, seed=6),
+        Workload("decode_mlp_down", 8, 57344, 14336, 0.5, 0.01, 16, 8.0, 60.0, seed=7),
     ]
 }
 

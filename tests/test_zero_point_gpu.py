@@ -220,7 +220,8 @@ def test_linear_zp_rejects_large_k(lib):
         lib.quantize_activation_zp(X, 6.0)
 
 
-@pytest.mark.parametrize("name", ["decode", "qkv_prefill", "mlp_down_prefill"])
+@pytest.mark.parametrize("name", ["decode", "qkv_prefill", "mlp_down_prefill",
+                                  "decode_mlp_down"])
 def test_workload_zp_sampled(lib, name):
     """The benchmark workloads at full size through int8_linear_zp: the whole
     activation stage bit-exact, sampled outputs against the oracle."""
