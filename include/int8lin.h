@@ -76,6 +76,10 @@ typedef enum {
  *   zero_points  int32 [M]        int8_linear_zp only: the row zero points;
  *                                 sx then holds range / 255 and Xq the codes
  *                                 minus 128 (see int8_quantize_activation_zp)
+ *   act_partials uint32           internal (1 <= M <= 16): per 512-column
+ *                                 slice of K, its outlier count and per-row
+ *                                 partial maxima / minima of the activation
+ *                                 stage (0 bytes for other M)
  *   gemm_counters, gemm_partials   internal (M > 16): arrival counters and
  *                                 int32 partial tiles of the GEMM's split-K
  *                                 tail; gemm_slices partial tiles of 256x256
@@ -92,6 +96,7 @@ typedef struct {
   size_t gemm_partials;
   size_t gemm_slices;
   size_t zero_points;
+  size_t act_partials;
 } i8l_workspace_layout;
 
 /* Fills *layout for an int8_linear call of this shape.

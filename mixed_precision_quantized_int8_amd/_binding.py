@@ -59,6 +59,7 @@ class WorkspaceLayout(ctypes.Structure):
         ("gemm_partials", ctypes.c_size_t),
         ("gemm_slices", ctypes.c_size_t),
         ("zero_points", ctypes.c_size_t),
+        ("act_partials", ctypes.c_size_t),
     ]
 
 

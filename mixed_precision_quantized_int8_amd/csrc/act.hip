@@ -7,7 +7,7 @@
 // states are quantized row by row.  [blog, "Introduction to model
 // quantization"]: absmax codes are round(x * 127 / absmax) in [-127, 127].
 //
-// Three launches on the caller's stream:
+// For M > 16, three launches on the caller's stream:
 //   clear     zero the column bitmask (a fill kernel, safe under graph capture)
 //   colflags  one pass over X: per thread 16-byte loads, 8 running column
 //             maxima; a set bit for every column whose absmax reaches the
@@ -26,6 +26,9 @@
 // fl32(range / 255) to sx and zp to the zero-point array.
 // The column dependency (every row must be seen before any row scale) is why
 // X is read twice; the second read is one coalesced pass per row.
+// For 1 <= M <= 16 (the small-M path with K > 4096, and the stage export) two
+// launches over 512-column slices do the same work with many workgroups
+// instead of one per row (see the kernels below).
 #include "common.h"
 #include "launch.h"
 
@@ -299,6 +302,240 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
   }
 }
 
+// ---- small M (1 <= M <= 16): one workgroup per 512-column slice -------------------
+// All rows of a slice sit in one workgroup, so its column maxima are complete
+// there.  The scan kernel writes the slice's flag words (every word is written,
+// so no clear is needed), its outlier count and, per row, the maximum over the
+// regular columns: magnitude bits, or in zero-point mode the largest and
+// smallest value keys (an outlier or out-of-range value counts as 0, which the
+// range contains anyway).  The quantize kernel reduces the partials of all
+// slices to the row scales, ranks its outlier columns after those of the
+// slices before it, and writes the codes, outlier values and indices of its
+// slice; slice 0 writes the row scales, zero points and the outlier count.
+constexpr int kSmallThreads = 256;   // wave w holds rows w, w + 4, w + 8, w + 12
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off, 64);
+    v = o < v ? o : v;
+  }
+  return v;
+}
+
+// X[r][c .. c+8) of the lane's rows as fp16 (zero past M or K).
+__device__ __forceinline__ void small_load_rows(const uint16_t* X, int M, int K, int c,
+                                                v4i (&x)[4]) {
+  const int wave = threadIdx.x >> 6;
+  const buf_rsrc rx = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave + 4 * i;
+    x[i] = buf_load16(rx, r < M && c < K ? (uint32_t)(r * K + c) * 2u : kBufOff);
+  }
+}
+
+template <bool ZP>
+__global__ __launch_bounds__(kSmallThreads) void act_small_scan_kernel(
+    const uint16_t* __restrict__ X, int M, int K, float threshold, int enabled,
+    uint32_t* __restrict__ flags, uint32_t* __restrict__ part) {
+  __shared__ uint32_t s_cm[kSmallThreads / 64][64][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sl = blockIdx.x, nsl = gridDim.x;
+  const int c = sl * kActSlice + lane * 8;
+  v4i x[4];
+  small_load_rows(X, M, K, c, x);
+
+  // column maxima of the lane's 8 columns: over the wave's rows, then the waves
+  u16x2 cm[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    cm[j] = u16x2{0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      cm[j] = __builtin_elementwise_max(cm[j],
+                                        __builtin_bit_cast(u16x2, (uint32_t)x[i][j] & 0x7fff7fffu));
+    s_cm[wave][lane][j] = __builtin_bit_cast(uint32_t, cm[j]);
+  }
+  lds_sync();
+  uint32_t bits = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u16x2 v = {0, 0};
+#pragma unroll
+    for (int w = 0; w < kSmallThreads / 64; ++w)
+      v = __builtin_elementwise_max(v, __builtin_bit_cast(u16x2, s_cm[w][lane][j]));
+    if (enabled) {
+      if (h2f(v[0]) >= threshold) bits |= 1u << (2 * j);
+      if (h2f(v[1]) >= threshold) bits |= 2u << (2 * j);
+    }
+  }
+
+  // the slice's flag words (4 lanes per word) and outlier count
+  uint32_t wb = bits << ((lane & 3) * 8);
+  wb |= __shfl_xor(wb, 1, 64);
+  wb |= __shfl_xor(wb, 2, 64);
+  const int word = sl * (kActSlice / 32) + (lane >> 2);
+  if (wave == 0 && (lane & 3) == 0 && word < ((K + 31) >> 5)) flags[word] = wb;
+  const int cnt = wave_sum(__builtin_popcount(bits));
+  if (threadIdx.x == 0) part[sl] = (uint32_t)cnt;
+
+  // per row: the maximum (and minimum key) over the regular columns
+  uint32_t keep[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t b0 = (bits >> (2 * j)) & 1u, b1 = (bits >> (2 * j + 1)) & 1u;
+    keep[j] = ((b0 - 1u) & 0xffffu) | ((b1 - 1u) << 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave + 4 * i;
+    if (r >= M) break;   // uniform over the wave
+    u16x2 hi2 = {0, 0}, lo2 = {0xffff, 0xffff};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t v = (uint32_t)x[i][j] & keep[j];
+      if constexpr (ZP) {
+        const u16x2 k2 = __builtin_bit_cast(u16x2, f16x2_keys(v));
+        hi2 = __builtin_elementwise_max(hi2, k2);
+        lo2 = __builtin_elementwise_min(lo2, k2);
+      } else {
+        hi2 = __builtin_elementwise_max(hi2, __builtin_bit_cast(u16x2, v & 0x7fff7fffu));
+      }
+    }
+    const uint32_t hi = wave_max_u32(hi2[0] > hi2[1] ? hi2[0] : hi2[1]);
+    if (lane == 0) part[nsl + sl * kActSmallRows + r] = hi;
+    if constexpr (ZP) {
+      const uint32_t lo = wave_min_u32(lo2[0] < lo2[1] ? lo2[0] : lo2[1]);
+      if (lane == 0) part[nsl + (nsl + sl) * kActSmallRows + r] = lo;
+    }
+  }
+}
+
+template <bool ZP>
+__global__ __launch_bounds__(kSmallThreads) void act_small_quant_kernel(
+    const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ flags,
+    const uint32_t* __restrict__ part, int8_t* __restrict__ Xq, float* __restrict__ sx,
+    int32_t* __restrict__ zp, int32_t* __restrict__ idx, int32_t* __restrict__ n_out,
+    uint16_t* __restrict__ X_O) {
+  constexpr int kGroups = kSmallThreads / kActSmallRows;   // 16 slice groups
+  __shared__ uint32_t s_hi[kGroups][kActSmallRows];
+  __shared__ uint32_t s_lo[ZP ? kGroups : 1][kActSmallRows];
+  __shared__ int s_cnt[kSmallThreads / 64][2];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int sl = blockIdx.x, nsl = gridDim.x;
+  const int c = sl * kActSlice + lane * 8;
+  const int nw = (K + 31) >> 5;
+  v4i x[4];
+  small_load_rows(X, M, K, c, x);
+  const int word = sl * (kActSlice / 32) + (lane >> 2);
+  const uint32_t fw = buf_load_u32(make_rsrc(flags, (uint32_t)nw * 4u), (uint32_t)word * 4u);
+
+  // row partials of all slices: thread (g, m) reduces slices g, g + 16, ...
+  {
+    const int m = t % kActSmallRows, g = t / kActSmallRows;
+    uint32_t hi = 0, lo = 0xffffu;
+    if (m < M) {
+      for (int s = g; s < nsl; s += kGroups) {
+        const uint32_t h = part[nsl + s * kActSmallRows + m];
+        hi = h > hi ? h : hi;
+        if constexpr (ZP) {
+          const uint32_t l = part[nsl + (nsl + s) * kActSmallRows + m];
+          lo = l < lo ? l : lo;
+        }
+      }
+    }
+    s_hi[g][m] = hi;
+    if constexpr (ZP) s_lo[g][m] = lo;
+  }
+  // outliers of the slices before this one, and of all slices
+  int before = 0, total = 0;
+  for (int s = t; s < nsl; s += kSmallThreads) {
+    const int v = (int)part[s];
+    total += v;
+    before += s < sl ? v : 0;
+  }
+  before = wave_sum(before);
+  total = wave_sum(total);
+  if (lane == 0) {
+    s_cnt[wave][0] = before;
+    s_cnt[wave][1] = total;
+  }
+  lds_sync();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kSmallThreads / 64; ++w) {
+    base += s_cnt[w][0];
+    total += s_cnt[w][1];
+  }
+
+  // ranks of the lane's outlier columns: after the slices before and the lanes before
+  const uint32_t bits = (fw >> ((lane & 3) * 8)) & 0xffu;
+  const int pc = __builtin_popcount(bits);
+  const int rank0 = base + wave_incl_scan(pc) - pc;
+  if (wave == 0 && bits) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((bits >> e) & 1u) idx[rank0 + __builtin_popcount(bits & ((1u << e) - 1u))] = c + e;
+  }
+  if (sl == 0 && t == 0) *n_out = total;
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave + 4 * i;
+    if (r >= M) break;   // uniform over the wave
+    uint32_t mh = 0, ml = 0xffffu;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      mh = s_hi[g][r] > mh ? s_hi[g][r] : mh;
+      if constexpr (ZP) ml = s_lo[g][r] < ml ? s_lo[g][r] : ml;
+    }
+    float inv, scale;
+    int zpv = 0;
+    if constexpr (ZP) {
+      // [blog, "Introduction to model quantization"], the unsigned scheme
+      const float hi = __builtin_fmaxf(f16_of_key(mh), 0.0f);
+      const float lo = __builtin_fminf(f16_of_key(ml), 0.0f);
+      const float range = hi - lo;
+      inv = range > 0.0f ? 255.0f / range : 0.0f;
+      zpv = (int)__builtin_roundf(-lo * inv);
+      scale = range / 255.0f;
+    } else {
+      scale = h2f((uint16_t)mh);
+      inv = quant_scale(scale);
+    }
+    if (c < K) {
+      int code[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t hb = (uint16_t)(((uint32_t)x[i][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+        const bool out = (bits >> e) & 1u;
+        if constexpr (ZP) {
+          int cc = out ? zpv : (int)__builtin_roundf(h2f(hb) * inv) + zpv;
+          cc = cc < 0 ? 0 : (cc > 255 ? 255 : cc);
+          code[e] = cc - 128;
+        } else {
+          code[e] = out ? 0 : quant_code(h2f(hb), inv);
+        }
+      }
+      const v2i packed = {(int)pack4_i8(code[0], code[1], code[2], code[3]),
+                          (int)pack4_i8(code[4], code[5], code[6], code[7])};
+      *reinterpret_cast<v2i*>(Xq + (size_t)r * K + c) = packed;
+      if (bits) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if ((bits >> e) & 1u)
+            X_O[(size_t)r * K + rank0 + __builtin_popcount(bits & ((1u << e) - 1u))] =
+                (uint16_t)(((uint32_t)x[i][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+      }
+    }
+    if (sl == 0 && lane == 0) {
+      sx[r] = scale;
+      if constexpr (ZP) zp[r] = zpv;
+    }
+  }
+}
+
 template <int BS, int NCH>
 static void launch_rowquant(const uint16_t* X, int M, int K, bool zp, const Workspace& ws,
                             hipStream_t stream) {
@@ -314,6 +551,23 @@ static void launch_rowquant(const uint16_t* X, int M, int K, bool zp, const Work
 hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float threshold,
                                       bool enabled, const Workspace& ws, hipStream_t stream,
                                       bool zp) {
+  if (M >= 1 && M <= kActSmallRows) {
+    const dim3 grid(act_slices(K)), block(kSmallThreads);
+    if (zp) {
+      hipLaunchKernelGGL(act_small_scan_kernel<true>, grid, block, 0, stream, X, M, K, threshold,
+                         (int)enabled, ws.flags, ws.act_part);
+      hipLaunchKernelGGL(act_small_quant_kernel<true>, grid, block, 0, stream, X, M, K,
+                         (const uint32_t*)ws.flags, (const uint32_t*)ws.act_part, ws.Xq, ws.sx,
+                         ws.zp, ws.idx, ws.n_out, ws.X_O);
+    } else {
+      hipLaunchKernelGGL(act_small_scan_kernel<false>, grid, block, 0, stream, X, M, K, threshold,
+                         (int)enabled, ws.flags, ws.act_part);
+      hipLaunchKernelGGL(act_small_quant_kernel<false>, grid, block, 0, stream, X, M, K,
+                         (const uint32_t*)ws.flags, (const uint32_t*)ws.act_part, ws.Xq, ws.sx,
+                         nullptr, ws.idx, ws.n_out, ws.X_O);
+    }
+    return hipGetLastError();
+  }
   const int nw = (K + 31) / 32;
   launch_fill_u32(ws.flags, nw, 0u, stream);
   if (enabled && M > 0) {

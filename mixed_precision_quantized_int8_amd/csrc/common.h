@@ -98,6 +98,18 @@ __device__ __forceinline__ int wave_sum(int v) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Order-preserving u16 key of an fp16 value (finite values): positive values
+// get the top bit set, negative ones are bit-inverted; applied to both halves.
+__device__ __forceinline__ uint32_t f16x2_keys(uint32_t x) {
+  const uint32_t neg = ((x >> 15) & 0x00010001u) * 0xffffu;
+  return x ^ (0x80008000u | (neg & 0x7fff7fffu));
+}
+__device__ __forceinline__ float f16_of_key(uint32_t k) {
+  return h2f((uint16_t)(k & 0x8000u ? k ^ 0x8000u : ~k & 0xffffu));
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;

@@ -77,8 +77,6 @@ struct DecodeArgs {
 
 bool decode_fits(int M, int K) { return M >= 1 && M <= 16 && K <= kDecWaves * kDecMaxKS * 64; }
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ uint32_t half_at(const v4i (&v)[2], int e) {
   return ((uint32_t)v[e >> 3][(e & 7) >> 1] >> ((e & 1) * 16)) & 0xffffu;
 }
@@ -128,15 +126,7 @@ __device__ __forceinline__ v4i codes16_zp(const v4i (&x)[2], float inv65, int zp
   return a;
 }
 
-// Order-preserving u16 key of an fp16 value (finite values): positive values
-// get the top bit set, negative ones are bit-inverted; applied to both halves.
-__device__ __forceinline__ uint32_t f16x2_keys(uint32_t x) {
-  const uint32_t neg = ((x >> 15) & 0x00010001u) * 0xffffu;
-  return x ^ (0x80008000u | (neg & 0x7fff7fffu));
-}
-__device__ __forceinline__ float f16_of_key(uint32_t k) {
-  return h2f((uint16_t)(k & 0x8000u ? k ^ 0x8000u : ~k & 0xffffu));
-}
+
 
 // KS: k-steps of 64 per wave (>= ceil(K / 64 / 8));
 // R: k-steps packed into one register set (M <= 16 / R): lane row lr holds X

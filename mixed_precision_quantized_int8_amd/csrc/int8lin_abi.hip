@@ -76,6 +76,10 @@ i8l_workspace_layout layout_of(int64_t M, int64_t K, int64_t N) {
   L.X_outliers = off; off += up((size_t)M * (size_t)K * sizeof(uint16_t));
   // before the GEMM's part, so that its offset does not depend on N
   L.zero_points = off; off += up((size_t)M * sizeof(int32_t));
+  // small M: per 512-column slice an outlier count and 16 row maxima and minima
+  const size_t act_words =
+      (M >= 1 && M <= i8l::kActSmallRows) ? (size_t)i8l::act_slices((int)K) * (1 + 2 * i8l::kActSmallRows) : 0;
+  L.act_partials = off; off += up(act_words * sizeof(uint32_t));
   int slices = 0;
   if (M > 16 && N > 0) {
     const i8l::GemmSplit p = i8l::gemm_split_plan((int)M, (int)N, (int)K, i8l::kGemmMaxSlices);
@@ -101,6 +105,7 @@ i8l::Workspace carve(void* ws, const i8l_workspace_layout& L) {
   w.gemm_part = reinterpret_cast<int32_t*>(b + L.gemm_partials);
   w.gemm_slices = (int)L.gemm_slices;
   w.zp = reinterpret_cast<int32_t*>(b + L.zero_points);
+  w.act_part = reinterpret_cast<uint32_t*>(b + L.act_partials);
   return w;
 }
 

@@ -20,6 +20,8 @@ struct Workspace {
   int32_t* gemm_cnt;   // [kGemmMaxSlices] arrival counters of split tiles
   int32_t* gemm_part;  // [gemm_slices][256][256] int32 partial tiles
   int gemm_slices;     // partial tiles the workspace holds
+  uint32_t* act_part;  // M <= 16: per 512-column slice, the outlier count, then
+                       // the row partials (see launch_quantize_activation)
 };
 
 // Split-K tail of the GEMM: the tiles of the last, partial round over the
@@ -39,9 +41,16 @@ hipError_t launch_fill_u32(uint32_t* p, int n, uint32_t v, hipStream_t stream);
 hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, float* sw,
                                   hipStream_t stream);
 
-// Outlier column scan + row quantization (two kernels after a flag clear).
+// Outlier column scan + row quantization: for M > 16 two kernels after a flag
+// clear; for 1 <= M <= 16 two kernels over 512-column slices that pass
+// per-slice outlier counts and row partials through ws.act_part
+// ([act_slices(K)] counts, then [act_slices(K)][16] row maxima, then, in
+// zero-point mode, [act_slices(K)][16] row minima).
 // `enabled` false skips the scan: no column is an outlier.  `zp`: zero-point
 // codes (stored minus 128), range / 255 in ws.sx and the zero points in ws.zp.
+constexpr int kActSlice = 512;
+constexpr int kActSmallRows = 16;
+inline int act_slices(int K) { return (K + kActSlice - 1) / kActSlice; }
 hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float threshold,
                                       bool enabled, const Workspace& ws, hipStream_t stream,
                                       bool zp = false);

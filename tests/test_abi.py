@@ -159,7 +159,11 @@ def test_workspace_layout(i8l):
         assert L["Xq"] - L["flags"] >= 4 * ((K + 31) // 32)
         assert L["X_outliers"] - L["Xq"] >= M * K
         assert L["zero_points"] - L["X_outliers"] >= 2 * M * K
-        assert L["gemm_counters"] - L["zero_points"] >= 4 * M
+        assert L["act_partials"] - L["zero_points"] >= 4 * M
+        assert L["act_partials"] % 256 == 0
+        act_words = -(-K // 512) * 33 if 1 <= M <= 16 else 0
+        assert L["gemm_counters"] - L["act_partials"] >= 4 * act_words
+        assert L["act_partials"] == i8l.workspace_layout(M, K, 0)["act_partials"]
         assert L["zero_points"] % 256 == 0
         assert L["zero_points"] == i8l.workspace_layout(M, K, 0)["zero_points"]
         assert L["gemm_partials"] >= L["gemm_counters"]

@@ -119,6 +119,19 @@ def _act_cases():
     yield "all_outliers", X, c, 2.0 ** -24
     yield "disabled_inf", X, c, math.inf
     yield "disabled_zero", X, c, 0.0
+    # small M (<= 16): 512-column slices; outliers on both sides of slice edges,
+    # K ending in the middle of a flag word, a zero row, many outliers
+    X, c = wl.make_x(16, 1552, 1.0, 0, 8, 20, 14)
+    for k in (0, 511, 512, 1023, 1024, 1535, 1536, 1551):
+        X[:, k] = np.float16(7.0)
+    X[9, :] = 0
+    X[2, 700] = 6.0
+    X[4, 701] = np.float16(5.99609375)
+    yield "small_slice_edges", X, [0, 511, 512, 700, 1023, 1024, 1535, 1536, 1551], 6.0
+    yield "small_many_outliers", *wl.make_x(7, 2048, 1.0, 300, 8, 20, 15), 6.0
+    X, c = wl.make_x(6, 256, 1.0, 0, 8, 20, 16)
+    yield "small_all_outliers", X, c, 2.0 ** -24
+    yield "small_disabled", *wl.make_x(10, 1040, 1.0, 3, 8, 20, 17), math.inf
     X, c = wl.make_x(24, 128, 0.25, 0, 8, 20, 8)
     X[3, 5] = 6.0
     X[7, 9] = np.float16(5.99609375)
@@ -179,6 +192,7 @@ def _linear_cases():
     yield "decode_k8192", 8, 8192, 256, 5, 6.0, 1.0
     yield "decode_k_mod64", 5, 1040, 200, 2, 6.0, 1.0
     yield "decode_unfused_bigk", 8, 16384, 256, 4, 6.0, 1.0
+    yield "decode_bigk_many_outliers", 3, 4112, 200, 90, 6.0, 1.0
     yield "decode_many_outliers", 4, 1024, 130, 70, 6.0, 1.0
     yield "prefill_m17", 17, 1024, 600, 2, 6.0, 1.0
     yield "prefill_ragged", 300, 272, 520, 5, 6.0, 1.0

@@ -117,6 +117,16 @@ def _act_cases():
     yield "k_mod32_16", *shaped_x("offset", 17, 1040, 3, 6), 6.0
     yield "wide_k", *shaped_x("offset", 3, 40000, 6, 7), 6.0
     yield "max_k", *shaped_x("positive", 2, O.ZP_MAX_K, 2, 8), 6.0
+    # small M (<= 16): 512-column slices
+    X, c = shaped_x("offset", 16, 1552, 0, 10)
+    for k in (0, 511, 512, 1023, 1024, 1535, 1536, 1551):
+        X[:, k] = np.float16(-7.0)
+    X[9, :] = 0
+    yield "small_slice_edges", X, [0, 511, 512, 1023, 1024, 1535, 1536, 1551], 6.0
+    yield "small_many_outliers", *shaped_x("negative", 7, 2048, 300, 11), 6.0
+    X, c = shaped_x("positive", 6, 256, 0, 12)
+    yield "small_all_outliers", X, c, 2.0 ** -24
+    yield "small_disabled", *shaped_x("offset", 10, 1040, 3, 13), math.inf
     X, c = shaped_x("offset", 33, 256, 0, 9)
     yield "all_outliers", X, c, 2.0 ** -24
     yield "disabled_inf", X, c, math.inf
@@ -146,6 +156,7 @@ def _linear_cases():
     yield "decode_m1_bias", 1, 512, 1000, 1, 6.0, "positive", True, True
     yield "decode_m16", 16, 4096, 512, 3, 6.0, "offset", True, False
     yield "decode_k8192", 8, 8192, 256, 5, 6.0, "negative", False, True
+    yield "decode_bigk_many_outliers", 3, 4112, 200, 90, 6.0, "offset", True, True
     yield "decode_k_mod64", 5, 1040, 200, 2, 6.0, "offset", False, False
     yield "decode_m3_k272", 3, 272, 130, 1, 6.0, "negative", True, True
     yield "decode_m12_k2048", 12, 2048, 300, 2, 6.0, "positive", False, True
