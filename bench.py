@@ -42,10 +42,10 @@ PEAK_INT8_TOPS = 5000.0
 # (profiles/traffic-decode.md: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB, the
 # factors a 512 MiB device copy gives).
 TRAFFIC = {
-    ("decode_kernel", "decode"): {"bytes": 68496351, "src": "f31fc41b81e6ea34"},
-    ("decode_stream_kernel", "decode_mlp_down"): {"bytes": 827889756, "src": "f31fc41b81e6ea34"},
-    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2234511970, "src": "67c44cb98a422e57"},
-    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5558268378, "src": "67c44cb98a422e57"},
+    ("decode_kernel", "decode"): {"bytes": 68503069, "src": "459a6c14cbd3f348"},
+    ("decode_stream_kernel", "decode_mlp_down"): {"bytes": 827888884, "src": "459a6c14cbd3f348"},
+    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2234153488, "src": "60dcc0ebc13aba2d"},
+    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5557367181, "src": "60dcc0ebc13aba2d"},
 }
 
 
