@@ -327,8 +327,10 @@ def test_workload_full_sampled(lib, name):
 # graph capture: replays of a captured int8_linear equal the eager call
 # ---------------------------------------------------------------------------------
 # (520, 2048, 1300): 18 tiles, split in 2 along K (arrival counters cleared by
-# a fill kernel inside the graph)
-@pytest.mark.parametrize("M,K,N", [(8, 1024, 4096), (300, 272, 520), (520, 2048, 1300)])
+# a fill kernel inside the graph); (8, 8192, 300): small-M activation kernels
+# and the stream kernel
+@pytest.mark.parametrize("M,K,N", [(8, 1024, 4096), (300, 272, 520), (520, 2048, 1300),
+                                   (8, 8192, 300)])
 def test_linear_graph_replay(lib, M, K, N):
     say(f"int8_linear graph replay M={M} K={K} N={N}")
     X, W, _ = wl.make_small(M, K, N, seed=M + K, n_out=3, x_sigma=1.0)
