@@ -109,19 +109,23 @@ __device__ __forceinline__ v4i codes16(const v4i (&x)[2], float inv65) {
 // Zero-point codes of 16 values: clamp(round_half_away(x * inv) + zp, 0, 255)
 // - 128 per byte, with inv65 = inv * 2^16 as above; |x * inv| <= 255, so the
 // fixed-point rounding is exact.  Zeroed outlier values give zp - 128.
-__device__ __forceinline__ v4i codes16_zp(const v4i (&x)[2], float inv65, int zp) {
+// zpc = 0x8000 + (zp - 128) * 2^16: adding a multiple of 2^16 before the
+// arithmetic shift adds zp - 128 after it, so one add3 and one shift give
+// round_half_away(x * inv) + zp - 128, and med3 clamps it to [-128, 127].
+__device__ __forceinline__ v4i codes16_zp(const v4i (&x)[2], float inv65, int zpc) {
   v4i a;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint32_t b[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = (int)rhaz_sum(h2f((uint16_t)half_at(x, 4 * i + e)) * inv65) >> 16;
-      int q = r + zp;
-      q = q < 0 ? 0 : (q > 255 ? 255 : q);
-      b[e] = (uint32_t)(q - 128) & 0xffu;
+      const int w = (int)(h2f((uint16_t)half_at(x, 4 * i + e)) * inv65);   // truncates
+      const int q = (w + (w >> 31) + zpc) >> 16;
+      b[e] = (uint32_t)(q < -128 ? -128 : (q > 127 ? 127 : q));   // v_med3_i32
     }
-    a[i] = (int)(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24));
+    const uint32_t p01 = __builtin_amdgcn_perm(b[1], b[0], 0x04000400u);   // b0.b0 b1.b0 ..
+    const uint32_t p23 = __builtin_amdgcn_perm(b[3], b[2], 0x04000400u);   // b2.b0 b3.b0 ..
+    a[i] = (int)__builtin_amdgcn_perm(p23, p01, 0x05040100u);
   }
   return a;
 }
@@ -347,6 +351,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     sSx[lane] = lane < MR ? rowscale : 0.0f;
     sZp[lane] = lane < MR ? zpv : 0;
   }
+  const int zpc = 0x8000 + (zpv - 128) * 65536;   // zero-point codes: see codes16_zp
   v4i acc[kDecP];
 #pragma unroll
   for (int c = 0; c < kDecP; ++c) acc[c] = v4i{0, 0, 0, 0};
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
       // positions past K or past this wave's chunk must contribute nothing:
       // their code is 0 (the zero point's code is not)
       const int tq = s0 + j * R + q;
-      cj = tq < s1 && tq * 64 + 16 * g < K ? codes16_zp(xr[j], inv65, zpv) : v4i{0, 0, 0, 0};
+      cj = tq < s1 && tq * 64 + 16 * g < K ? codes16_zp(xr[j], inv65, zpc) : v4i{0, 0, 0, 0};
     } else {
       cj = codes16(xr[j], inv65);
     }
