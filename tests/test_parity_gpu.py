@@ -193,6 +193,8 @@ def _linear_cases():
     yield "decode_k_mod64", 5, 1040, 200, 2, 6.0, 1.0
     yield "decode_unfused_bigk", 8, 16384, 256, 4, 6.0, 1.0
     yield "decode_bigk_many_outliers", 3, 4112, 200, 90, 6.0, 1.0
+    yield "decode_bigk_m16_ragged_n", 16, 6160, 777, 3, 6.0, 1.0
+    yield "decode_bigk_m1", 1, 8192, 1000, 2, 6.0, 1.0
     yield "decode_many_outliers", 4, 1024, 130, 70, 6.0, 1.0
     yield "prefill_m17", 17, 1024, 600, 2, 6.0, 1.0
     yield "prefill_ragged", 300, 272, 520, 5, 6.0, 1.0
