@@ -44,8 +44,8 @@ PEAK_INT8_TOPS = 5000.0
 TRAFFIC = {
     ("decode_kernel", "decode"): {"bytes": 68505873, "src": "037dd7b7c51de0e2"},
     ("decode_stream_kernel", "decode_mlp_down"): {"bytes": 828017556, "src": "037dd7b7c51de0e2"},
-    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2234153488, "src": "60dcc0ebc13aba2d"},
-    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5557367181, "src": "60dcc0ebc13aba2d"},
+    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2234822072, "src": "3f556e59e4dac3a7"},
+    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5559667939, "src": "3f556e59e4dac3a7"},
 }
 
 
