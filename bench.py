@@ -65,9 +65,9 @@ def algorithmic_bytes(w):
 
 def dominant_kernel(w):
     """The kernel that carries the call: the fused small-M kernel (M <= 16,
-    K <= 4096), the streaming small-M kernel (M <= 16, larger K) or the GEMM."""
-    if w.M <= 16:
-        name = "decode_kernel" if w.K <= 4096 else "decode_stream_kernel"
+    K <= 4096), the streaming kernel (M <= 64 otherwise) or the GEMM."""
+    if w.M <= 64:
+        name = "decode_kernel" if w.M <= 16 and w.K <= 4096 else "decode_stream_kernel"
         return name, "hbm", ["decode.hip", "common.h"]
     return "gemm_i8_kernel", "mfma", ["gemm.hip", "common.h"]
 

@@ -50,6 +50,7 @@ constexpr int kDecCols = 16 * kDecP;
 constexpr int kDecMaxKS = 8;                  // fused kernel: k-steps per wave
 constexpr int kDecOutPre = 4;                 // outlier columns per wave preloaded
 constexpr int kDecMaxOutLds = 64;             // stream kernel: outlier values in LDS
+constexpr int kDecStreamRows = 64;            // stream kernel: rows of X (4 row groups)
 constexpr int kDecOutReg = 8;                 // stream kernel: outlier weights per lane
 
 // Zero bytes for lanes whose load is out of range (loads stay unconditional,
@@ -512,31 +513,35 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   }
 }
 
-// Stream kernel for small M with larger K: the activation kernels have written
-// the codes, the row scales and the outlier list to the workspace.
+// Stream kernel for M <= 64 when the fused kernel does not apply (K > 4096 or
+// M > 16): the activation kernels have written the codes, the row scales and
+// the outlier list to the workspace.  MG row groups of 16 rows (the A operand
+// of one MFMA each) against the same weight registers; KU k-steps per weight
+// buffer (fewer for more row groups, to stay within the register file).
+template <int MG, int KU>
 __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d) {
-  constexpr int kU = 4;
-  __shared__ v4i sRed[kDecWaves][kDecP][64];
-  __shared__ float sXO[16][kDecMaxOutLds];
+  __shared__ v4i sRed[kDecWaves][MG][kDecP][64];
+  __shared__ float sXO[kDecStreamRows][kDecMaxOutLds];
 
   const int M = d.M, K = d.K, N = d.N;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform
   const int lr = lane & 15, kl = (lane >> 4) * 16;
   const int n0 = blockIdx.x * kDecCols;
   const int nsteps = (K + 63) >> 6;
   const int kc = (wave + blockIdx.x) % kDecWaves;
   const int s0 = kc * nsteps / kDecWaves, s1 = (kc + 1) * nsteps / kDecWaves;
 
-  // weight registers double-buffered: the loads of the next kU k-steps are in
+  // weight registers double-buffered: the loads of the next KU k-steps are in
   // flight while the current ones are multiplied; each buffer is filled one
   // 16-feature block after the other, the k-steps of a block back to back.
   // Steps past s1 read the zero page, so the loop needs no tail.
-  v4i fb[2][kU][kDecP];
+  v4i fb[2][KU][kDecP];
   auto load_b = [&](int b, int s) {
 #pragma unroll
     for (int c = 0; c < kDecP; ++c) {
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
+      for (int u = 0; u < KU; ++u) {
         const int k = (s + u) * 64 + kl;
         const int n = n0 + c * 16 + lr;
         const bool in = s + u < s1 && n < N && k < K;
@@ -545,44 +550,54 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
       }
     }
   };
-  auto load_a = [&](int s, v4i (&fa)[kU]) {
+  // codes of rows 16 * g + lr, zero past M, K or s1
+  auto load_a = [&](int s, v4i (&fa)[MG][KU]) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int k = (s + u) * 64 + kl;
-      const bool in = s + u < s1 && lr < M && k < K;
-      const void* p = in ? (const void*)(d.Xq + (size_t)lr * K + k) : (const void*)g_dec_zero;
-      fa[u] = *reinterpret_cast<const v4i*>(p);
-    }
+    for (int g = 0; g < MG; ++g)
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int k = (s + u) * 64 + kl, row = 16 * g + lr;
+        const bool in = s + u < s1 && row < M && k < K;
+        const void* p = in ? (const void*)(d.Xq + (size_t)row * K + k) : (const void*)g_dec_zero;
+        fa[g][u] = *reinterpret_cast<const v4i*>(p);
+      }
   };
-  v4i acc[kDecP];
+  v4i acc[MG][kDecP];
 #pragma unroll
-  for (int c = 0; c < kDecP; ++c) acc[c] = v4i{0, 0, 0, 0};
-  auto mma = [&](int b, const v4i (&fa)[kU]) {
+  for (int g = 0; g < MG; ++g)
+#pragma unroll
+    for (int c = 0; c < kDecP; ++c) acc[g][c] = v4i{0, 0, 0, 0};
+  auto mma = [&](int b, const v4i (&fa)[MG][KU]) {
 #pragma unroll
     for (int c = 0; c < kDecP; ++c)
 #pragma unroll
-      for (int u = 0; u < kU; ++u)
-        acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[u], fb[b][u][c], acc[c], 0, 0, 0);
+      for (int u = 0; u < KU; ++u)
+#pragma unroll
+        for (int g = 0; g < MG; ++g)
+          acc[g][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[g][u], fb[b][u][c], acc[g][c], 0, 0, 0);
   };
   load_b(0, s0);
-  for (int s = s0; s < s1; s += 2 * kU) {
-    v4i fa0[kU], fa1[kU];
+  for (int s = s0; s < s1; s += 2 * KU) {
+    v4i fa0[MG][KU], fa1[MG][KU];
     // the codes go out before the next weight loads: the wait for them then
     // leaves those loads in flight
     load_a(s, fa0);
-    load_b(1, s + kU);
+    load_b(1, s + KU);
     __builtin_amdgcn_sched_barrier(0);
     mma(0, fa0);
     __builtin_amdgcn_sched_barrier(0);
-    load_a(s + kU, fa1);
-    load_b(0, s + 2 * kU);
+    load_a(s + KU, fa1);
+    load_b(0, s + 2 * KU);
     __builtin_amdgcn_sched_barrier(0);
     mma(1, fa1);
     __builtin_amdgcn_sched_barrier(0);
   }
 
   const int nout = *d.n_out;
-  const int n = n0 + (wave & (kDecP - 1)) * 16 + lr;
+  // every wave finishes features c * 16 + lr of its block (c = wave % 4), for
+  // row groups wave / 4, wave / 4 + 2, ...
+  const int c = wave & (kDecP - 1);
+  const int n = n0 + c * 16 + lr;
   // outlier weight value: the fp16 row, or rebuilt from the code (W_rows NULL)
   const float swn_raw = d.sw[n < N ? n : N - 1];
   auto wval = [&](int k) -> float {
@@ -591,59 +606,61 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
   };
   float wo[kDecOutReg];
 #pragma unroll
-  for (int j = 0; j < kDecOutReg; ++j)
-    wo[j] = (wave < kDecP && j < nout && n < N) ? wval(d.idx[j]) : 0.0f;
+  for (int j = 0; j < kDecOutReg; ++j) wo[j] = (j < nout && n < N) ? wval(d.idx[j]) : 0.0f;
   const int nl = min(nout, kDecMaxOutLds);
   for (int e = t; e < nl * M; e += kDecThreads) {
     const int m = e / nl, j = e % nl;
     sXO[m][j] = h2f(d.X_O[(size_t)m * K + j]);
   }
 #pragma unroll
-  for (int c = 0; c < kDecP; ++c) sRed[wave][c][lane] = acc[c];
-  lds_sync();
-  if (wave >= kDecP) return;
-  const int c = wave;
-  v4i tot = {0, 0, 0, 0};
+  for (int g = 0; g < MG; ++g)
 #pragma unroll
-  for (int w = 0; w < kDecWaves; ++w) {
-    const v4i p = sRed[w][c][lane];
-    tot[0] += p[0]; tot[1] += p[1]; tot[2] += p[2]; tot[3] += p[3];
-  }
-  const int mb = (lane >> 4) * 4;
-  if (n >= N || mb >= M) return;
+    for (int cc = 0; cc < kDecP; ++cc) sRed[wave][g][cc][lane] = acc[g][cc];
+  lds_sync();
+  if (n >= N) return;
   const float swn = swn_raw * (d.zp ? 1.0f / 127.0f : 1.0f / 16129.0f);
   const float bv = d.bias ? h2f(d.bias[n]) : 0.0f;
-  if (d.zp) {   // sum (q - zp) w = sum (q - 128) w + (128 - zp) S[n], mod 2^32
-    const uint32_t wsv = (uint32_t)d.wsum[n];
+  const uint32_t wsv = d.zp ? (uint32_t)d.wsum[n] : 0u;
+  for (int g = wave / kDecP; g < MG; g += kDecWaves / kDecP) {   // uniform per wave
+    const int mb = 16 * g + (lane >> 4) * 4;   // D rows of this lane: mb .. mb + 3
+    if (mb >= M) continue;
+    v4i tot = {0, 0, 0, 0};
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (mb + r < M) tot[r] = (int)((uint32_t)tot[r] + (uint32_t)(128 - d.zp[mb + r]) * wsv);
-  }
-  float y[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = mb + r;
-    y[r] = m < M ? (float)tot[r] * (d.sx[m] * swn) : 0.0f;
-  }
-#pragma unroll
-  for (int j = 0; j < kDecOutReg; ++j)
-    if (j < nout) {
+    for (int w = 0; w < kDecWaves; ++w) {
+      const v4i p = sRed[w][g][c][lane];
+      tot[0] += p[0]; tot[1] += p[1]; tot[2] += p[2]; tot[3] += p[3];
+    }
+    if (d.zp) {   // sum (q - zp) w = sum (q - 128) w + (128 - zp) S[n], mod 2^32
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (mb + r < M) y[r] += sXO[mb + r][j] * wo[j];
+        if (mb + r < M) tot[r] = (int)((uint32_t)tot[r] + (uint32_t)(128 - d.zp[mb + r]) * wsv);
     }
-  for (int j = kDecOutReg; j < nout; ++j) {
-    const float w = wval(d.idx[j]);
+    float y[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = mb + r;
-      if (m < M) y[r] += (j < kDecMaxOutLds ? sXO[m][j] : h2f(d.X_O[(size_t)m * K + j])) * w;
+      y[r] = m < M ? (float)tot[r] * (d.sx[m] * swn) : 0.0f;
     }
-  }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = mb + r;
-    if (m < M) d.Y[(size_t)m * N + n] = f2h(y[r] + bv);
+    for (int j = 0; j < kDecOutReg; ++j)
+      if (j < nout) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (mb + r < M) y[r] += sXO[mb + r][j] * wo[j];
+      }
+    for (int j = kDecOutReg; j < nout; ++j) {
+      const float w = wval(d.idx[j]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mb + r;
+        if (m < M) y[r] += (j < kDecMaxOutLds ? sXO[m][j] : h2f(d.X_O[(size_t)m * K + j])) * w;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = mb + r;
+      if (m < M) d.Y[(size_t)m * N + n] = f2h(y[r] + bv);
+    }
   }
 }
 
@@ -671,6 +688,13 @@ uint32_t threshold_bits(float t) {
 typedef void (*kfn)(DecodeArgs);
 
 namespace {
+// Stream kernel instantiation for M <= 64: row groups of 16 rows.
+kfn stream_kernel(int M) {
+  if (M <= 16) return decode_stream_kernel<1, 4>;
+  if (M <= 32) return decode_stream_kernel<2, 4>;
+  return decode_stream_kernel<4, 2>;
+}
+
 // Fused kernel instantiation for M <= 16, K <= 4096.
 template <bool ZP>
 kfn fused_decode_kernel(int M, int K) {
@@ -699,7 +723,7 @@ hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, cons
   }
   hipError_t e = launch_quantize_activation(X, M, K, threshold, enabled, ws, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_stream_kernel, grid, block, 0, stream, d);
+  hipLaunchKernelGGL(stream_kernel(M), grid, block, 0, stream, d);
   return hipGetLastError();
 }
 
@@ -717,7 +741,7 @@ hipError_t launch_decode_zp(const uint16_t* X, int M, int K, const int8_t* Wq, c
   }
   hipError_t e = launch_quantize_activation(X, M, K, threshold, enabled, ws, stream, true);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_stream_kernel, grid, block, 0, stream, d);
+  hipLaunchKernelGGL(stream_kernel(M), grid, block, 0, stream, d);
   return hipGetLastError();
 }
 

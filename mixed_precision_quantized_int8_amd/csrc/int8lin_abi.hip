@@ -196,7 +196,7 @@ i8l_status linear_impl(const char* fn, const uint16_t* X, int64_t M, int64_t K, 
   const i8l::Workspace w = carve(workspace, L);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int m = (int)M, k = (int)K, n = (int)N;
-  if (m <= 16) {
+  if (m <= i8l::kStreamMaxM) {   // weight-bound: the fused or the streaming kernel
     if (zp)
       return hip_status(fn, i8l::launch_decode_zp(X, m, k, Wq, sw, wsum, n, W_outlier_rows, bias,
                                                   threshold, enabled, Y, w, st));

@@ -88,15 +88,16 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
-// Small-M (decode) path, M <= 16: when decode_fits(M, K) one fused kernel does
-// the activation stage, the int8 product, the outlier product and the
-// epilogue; otherwise the activation kernels run first and a streaming kernel
-// does the rest.
+// Small-M (decode) path, M <= kStreamMaxM: when decode_fits(M, K) (M <= 16,
+// K <= 4096) one fused kernel does the activation stage, the int8 product,
+// the outlier product and the epilogue; otherwise the activation kernels run
+// first and a weight-streaming kernel does the rest.
+constexpr int kStreamMaxM = 64;
 bool decode_fits(int M, int K);
 hipError_t launch_decode(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,
                          int N, const uint16_t* W_rows, const uint16_t* bias, float threshold,
                          bool enabled, uint16_t* Y, const Workspace& ws, hipStream_t stream);
-// Zero-point mode for M <= 16: the fused kernel when decode_fits(M, K), else the
+// Zero-point mode for M <= kStreamMaxM: the fused kernel when decode_fits(M, K), else the
 // activation kernels (zero-point codes), then the streaming kernel with the
 // corrected epilogue.
 hipError_t launch_decode_zp(const uint16_t* X, int M, int K, const int8_t* Wq, const float* sw,

@@ -71,6 +71,9 @@ WORKLOADS = {
         # above: the weight stream of the small-M path at K > 4096
         Workload("decode_qkv", 8, 14336, 43008, 1.0, 0.02, 8, 8.0, 60.0, seed=6),
         Workload("decode_mlp_down", 8, 57344, 14336, 0.5, 0.01, 16, 8.0, 60.0, seed=7),
+        # a batch of 32 tokens on the decode layer: the weight-bound path for
+        # 16 < M <= 64
+        Workload("decode_m32", 32, 4096, 16384, 1.0, 0.02, 4, 6.5, 40.0, seed=8),
     ]
 }
 

@@ -195,6 +195,14 @@ def _linear_cases():
     yield "decode_bigk_many_outliers", 3, 4112, 200, 90, 6.0, 1.0
     yield "decode_bigk_m16_ragged_n", 16, 6160, 777, 3, 6.0, 1.0
     yield "decode_bigk_m1", 1, 8192, 1000, 2, 6.0, 1.0
+    # 17 <= M <= 64: activation kernels + the streaming kernel with 2 or 4 row groups
+    yield "stream_m17", 17, 1024, 600, 2, 6.0, 1.0
+    yield "stream_m24_k4112", 24, 4112, 300, 3, 6.0, 1.0
+    yield "stream_m32", 32, 4096, 1000, 3, 6.0, 1.0
+    yield "stream_m33", 33, 272, 130, 1, 6.0, 1.0
+    yield "stream_m48_k8192", 48, 8192, 777, 5, 6.0, 1.0
+    yield "stream_m64", 64, 2048, 520, 4, 6.0, 1.0
+    yield "stream_m64_many_outliers", 64, 1024, 200, 90, 6.0, 1.0
     yield "decode_many_outliers", 4, 1024, 130, 70, 6.0, 1.0
     yield "prefill_m17", 17, 1024, 600, 2, 6.0, 1.0
     yield "prefill_ragged", 300, 272, 520, 5, 6.0, 1.0
@@ -281,7 +289,7 @@ def test_workload_full_oracle(lib, name):
 
 @pytest.mark.parametrize("name", ["qkv_prefill", "mlp_down_prefill", "square_0pct",
                                   "square_0.1pct", "square_1pct", "decode_qkv",
-                                  "decode_mlp_down"])
+                                  "decode_mlp_down", "decode_m32"])
 def test_workload_full_sampled(lib, name):
     w = wl.WORKLOADS[name]
     say(f"workload {name} (sampled): generating inputs")
@@ -330,9 +338,9 @@ def test_workload_full_sampled(lib, name):
 # ---------------------------------------------------------------------------------
 # (520, 2048, 1300): 18 tiles, split in 2 along K (arrival counters cleared by
 # a fill kernel inside the graph); (8, 8192, 300): small-M activation kernels
-# and the stream kernel
+# and the stream kernel; (40, 4096, 1000): the stream kernel with 4 row groups
 @pytest.mark.parametrize("M,K,N", [(8, 1024, 4096), (300, 272, 520), (520, 2048, 1300),
-                                   (8, 8192, 300)])
+                                   (8, 8192, 300), (40, 4096, 1000)])
 def test_linear_graph_replay(lib, M, K, N):
     say(f"int8_linear graph replay M={M} K={K} N={N}")
     X, W, _ = wl.make_small(M, K, N, seed=M + K, n_out=3, x_sigma=1.0)
@@ -404,6 +412,8 @@ def test_linear_split_tail_sampled(lib):
     ("decode_m1", 1, 1040, 300, 2),
     ("decode_many", 4, 1024, 130, 9),        # more outliers than a wave preloads
     ("decode_bigk", 8, 16384, 256, 4),       # activation kernels + streaming kernel
+    ("stream_m32", 32, 4096, 520, 3),        # streaming kernel, 2 row groups
+    ("stream_m64_many", 64, 1024, 200, 70),  # 4 row groups, outliers past the LDS copy
     ("prefill", 300, 1040, 520, 5),          # GEMM, staged outlier rows
     ("prefill_many", 70, 1024, 300, 130),    # GEMM, rows straight from memory
     ("prefill_split", 520, 2048, 1300, 6),   # GEMM split-K tail

@@ -157,6 +157,9 @@ def _linear_cases():
     yield "decode_m16", 16, 4096, 512, 3, 6.0, "offset", True, False
     yield "decode_k8192", 8, 8192, 256, 5, 6.0, "negative", False, True
     yield "decode_bigk_many_outliers", 3, 4112, 200, 90, 6.0, "offset", True, True
+    yield "stream_m17_bias", 17, 1024, 600, 2, 6.0, "offset", True, True
+    yield "stream_m40_k4112", 40, 4112, 300, 3, 6.0, "negative", False, False
+    yield "stream_m64", 64, 2048, 520, 4, 6.0, "positive", True, True
     yield "decode_k_mod64", 5, 1040, 200, 2, 6.0, "offset", False, False
     yield "decode_m3_k272", 3, 272, 130, 1, 6.0, "negative", True, True
     yield "decode_m12_k2048", 12, 2048, 300, 2, 6.0, "positive", False, True
