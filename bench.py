@@ -42,8 +42,8 @@ PEAK_INT8_TOPS = 5000.0
 # (profiles/traffic-decode.md: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB, the
 # factors a 512 MiB device copy gives).
 TRAFFIC = {
-    ("decode_kernel", "decode"): {"bytes": 68505873, "src": "037dd7b7c51de0e2"},
-    ("decode_stream_kernel", "decode_mlp_down"): {"bytes": 828017556, "src": "037dd7b7c51de0e2"},
+    ("decode_kernel", "decode"): {"bytes": 68478750, "src": "9e0066366e1eb125"},
+    ("decode_stream_kernel", "decode_mlp_down"): {"bytes": 828172344, "src": "9e0066366e1eb125"},
     ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2234822072, "src": "3f556e59e4dac3a7"},
     ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5559667939, "src": "3f556e59e4dac3a7"},
 }
