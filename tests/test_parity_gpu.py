@@ -132,6 +132,7 @@ def _act_cases():
     X, c = wl.make_x(6, 256, 1.0, 0, 8, 20, 16)
     yield "small_all_outliers", X, c, 2.0 ** -24
     yield "small_disabled", *wl.make_x(10, 1040, 1.0, 3, 8, 20, 17), math.inf
+    yield "rows64_wide_k", *wl.make_x(64, 24592, 1.0, 7, 8, 20, 18), 6.0   # 64-row slices
     X, c = wl.make_x(24, 128, 0.25, 0, 8, 20, 8)
     X[3, 5] = 6.0
     X[7, 9] = np.float16(5.99609375)

@@ -127,6 +127,7 @@ def _act_cases():
     X, c = shaped_x("positive", 6, 256, 0, 12)
     yield "small_all_outliers", X, c, 2.0 ** -24
     yield "small_disabled", *shaped_x("offset", 10, 1040, 3, 13), math.inf
+    yield "rows64_wide_k", *shaped_x("offset", 64, 24592, 7, 14), 6.0
     X, c = shaped_x("offset", 33, 256, 0, 9)
     yield "all_outliers", X, c, 2.0 ** -24
     yield "disabled_inf", X, c, math.inf
