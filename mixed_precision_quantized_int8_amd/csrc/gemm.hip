@@ -116,14 +116,16 @@ __device__ __forceinline__ int d_row(int r, int lane) {
 }
 
 // SPLIT: the workgroups are the split tiles of the tail (S per tile), each on
-// its own range of k-steps; a separate instantiation, so that the whole-tile
-// kernel carries none of the split bookkeeping.  ZP: zero-point epilogue.
-template <bool OUT_I32, bool SPLIT, bool ZP>
+// its own range of k-steps; they store their int32 partials and end.  FIX
+// (with SPLIT): one workgroup per split tile, no main loop, the epilogue on
+// the sum of the S partials; a launch of its own, so that the partials are
+// visible to it without a fence per workgroup (a device-wide release writes
+// the XCD's L2 back: ~60 us per split workgroup, measured).  Separate
+// instantiations, so that the whole-tile kernel carries none of this.  ZP:
+// zero-point epilogue.
+template <bool OUT_I32, bool SPLIT, bool ZP, bool FIX = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) int8_t smem[kSlots * kSlot];
-  // split tiles' arrival flag, after the main loop only: the last word of the
-  // LDS, past the region the epilogue stages into
-  int& sLast = *reinterpret_cast<int*>(&smem[kSlots * kSlot - 4]);
 
   const int M = a.M, N = a.N, K = a.K;
   const int nkt = (K + kBK - 1) / kBK;   // k-steps of 128 bytes
@@ -133,6 +135,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   int tile, kb = 0, nk = nkt, slot = -1, sidx = 0;
   if constexpr (!SPLIT) {
     tile = xcd_tile(blockIdx.x, a.full_tiles);
+  } else if constexpr (FIX) {
+    slot = blockIdx.x;
+    tile = a.full_tiles + slot;
   } else {
     slot = blockIdx.x / a.split_S;
     sidx = blockIdx.x % a.split_S;
@@ -253,6 +258,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   // barrier at the end of iteration kt needs step kt+1 complete: issued after
   // its last load are only the four A loads of kt+2, so vmcnt(4).  (Measured:
   // ~10 % faster than issuing two of the A loads after the barrier.)
+  if constexpr (!FIX) {
   load(0, 0, false, 0); load(0, 0, false, 1); load(0, 0, false, 2); load(0, 0, false, 3);
   load(1, 0, true, 0); load(1, 0, true, 1); load(1, 0, true, 2); load(1, 0, true, 3);
   {
@@ -323,29 +329,29 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   }
   wait_vmcnt<0>();
   wait_lgkmcnt0();
+  }   // !FIX
   __syncthreads();   // all waves done with the ring before the epilogue reuses it
 
-  if constexpr (!OUT_I32 && SPLIT) {
-    // Split tile: publish this K range's int32 partial, count the arrival; the
-    // last of the S workgroups runs the epilogue on the sum of the S partials
-    // (exact integer sums, in any order), read back block by block.
+  if constexpr (!OUT_I32 && SPLIT && !FIX) {
+    // Split tile: store this K range's int32 partial and end; the fix-up
+    // launch sums the S partials (exact integer sums, in any order).  The
+    // partial is kept in register-fragment order (16-byte piece q of thread
+    // t's values of block (i, j) at ((i*2 + j)*4 + q)*512 + t): the fix-up
+    // workgroup has the same fragment layout, so each store and each read
+    // covers 1 KB contiguous per wave.
     constexpr int kTile = kBM * kBN;
-    int32_t* mine = a.part + (size_t)(slot * a.split_S + sidx) * kTile;
+    v4i* mine = reinterpret_cast<v4i*>(a.part + (size_t)(slot * a.split_S + sidx) * kTile);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          mine[(wm + i * 32 + d_row(r, lane)) * kBN + wn + j * 32 + l32] = acc[i][j][r];
+        for (int q = 0; q < 4; ++q)
+          mine[((i * 2 + j) * 4 + q) * kGemmThreads + t] =
+              v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         __builtin_amdgcn_sched_barrier(0);
       }
-    __threadfence();
-    __syncthreads();
-    if (t == 0) sLast = atomicAdd(&a.cnt[slot], 1) == a.split_S - 1;
-    __syncthreads();
-    if (!sLast) return;
-    __threadfence();   // the partials are read in the epilogue, block by block
+    return;
   }
 
   if constexpr (OUT_I32) {
@@ -382,8 +388,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     float* sBias = sSw + kBN;                                      // [256] (0 without bias)
     int* sZc = reinterpret_cast<int*>(sBias + kBN);                // [256] 128 - zp (ZP)
     int* sWs = sZc + kBM;                                          // [256] wsum (ZP)
-    static_assert(2 * kBM * kOutG * 2 + 5 * 256 * 4 <= (int)sizeof(smem) - 4,
-                  "epilogue staging must stay clear of the arrival flag");
+    static_assert(2 * kBM * kOutG * 2 + 5 * 256 * 4 <= (int)sizeof(smem),
+                  "epilogue staging must fit the LDS");
     // 16-byte chunk c of staged row r sits at c ^ ((r >> 2) & 3): conflict-free
     // fragment reads with the 192-byte row stride
     auto och = [](int r, int c) { return (c ^ ((r >> 2) & 3)) << 3; };
@@ -488,15 +494,29 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
         const float swv = sSw[wn + j * 32 + l32];
         int tot[16];
         if constexpr (SPLIT) {
-          // all S partials from memory (this workgroup's own included), so the
-          // accumulators are only stored after the loop and keep their registers
+          // the S partials of this fragment, four at a time, every load
+          // unconditional (partials past S read zero from the range check), so
+          // that they are in flight together
+          constexpr int kTile = kBM * kBN;
+          const buf_rsrc rp = make_rsrc(a.part + (size_t)slot * a.split_S * kTile,
+                                        (uint32_t)(a.split_S * kTile * 4));
+          const uint32_t fo = (uint32_t)(((i * 2 + j) * 4 * kGemmThreads + t) * 16);
 #pragma unroll
           for (int r = 0; r < 16; ++r) tot[r] = 0;
-          for (int s2 = 0; s2 < a.split_S; ++s2) {   // uniform
-            const int32_t* part = a.part + (size_t)(slot * a.split_S + s2) * (kBM * kBN);
+          for (int s2 = 0; s2 < a.split_S; s2 += 4) {   // uniform
+            v4i p[4][4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              tot[r] += part[(wm + i * 32 + d_row(r, lane)) * kBN + wn + j * 32 + l32];
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                p[k][q] = buf_load16(rp, (uint32_t)((s2 + k) * kTile * 4) + fo +
+                                             (uint32_t)(q * kGemmThreads * 16));
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tot[4 * q + e] += p[k][q][e];
           }
         } else {
 #pragma unroll
@@ -595,10 +615,6 @@ hipError_t launch_gemm(const GemmArgs& in, hipStream_t stream) {
   }
   a.full_tiles = p.full_tiles;
   a.split_S = p.S;
-  if (p.split_tiles > 0) {
-    hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(a.cnt), p.split_tiles, 0u, stream);
-    if (e != hipSuccess) return e;
-  }
   if (a.acc) {
     hipLaunchKernelGGL((gemm_i8_kernel<true, false, false>), dim3(p.full_tiles),
                        dim3(kGemmThreads), 0, stream, a);
@@ -614,13 +630,18 @@ hipError_t launch_gemm(const GemmArgs& in, hipStream_t stream) {
       hipLaunchKernelGGL((gemm_i8_kernel<false, false, false>), dim3(p.full_tiles),
                          dim3(kGemmThreads), 0, stream, a);
   }
-  if (p.split_tiles > 0) {
-    if (zp)
+  if (p.split_tiles > 0) {   // the split tiles' partials, then their fix-up
+    if (zp) {
       hipLaunchKernelGGL((gemm_i8_kernel<false, true, true>), dim3(p.split_tiles * p.S),
                          dim3(kGemmThreads), 0, stream, a);
-    else
+      hipLaunchKernelGGL((gemm_i8_kernel<false, true, true, true>), dim3(p.split_tiles),
+                         dim3(kGemmThreads), 0, stream, a);
+    } else {
       hipLaunchKernelGGL((gemm_i8_kernel<false, true, false>), dim3(p.split_tiles * p.S),
                          dim3(kGemmThreads), 0, stream, a);
+      hipLaunchKernelGGL((gemm_i8_kernel<false, true, false, true>), dim3(p.split_tiles),
+                         dim3(kGemmThreads), 0, stream, a);
+    }
   }
   return hipGetLastError();
 }
