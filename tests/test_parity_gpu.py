@@ -337,8 +337,8 @@ def test_workload_full_sampled(lib, name):
 # ---------------------------------------------------------------------------------
 # graph capture: replays of a captured int8_linear equal the eager call
 # ---------------------------------------------------------------------------------
-# (520, 2048, 1300): 18 tiles, split in 2 along K (arrival counters cleared by
-# a fill kernel inside the graph); (8, 8192, 300): small-M activation kernels
+# (520, 2048, 1300): 18 tiles, split in 2 along K (partials, then the fix-up
+# launch, inside the graph); (8, 8192, 300): small-M activation kernels
 # and the stream kernel; (40, 4096, 1000): the stream kernel with 4 row groups
 @pytest.mark.parametrize("M,K,N", [(8, 1024, 4096), (300, 272, 520), (520, 2048, 1300),
                                    (8, 8192, 300), (40, 4096, 1000)])
