@@ -17,7 +17,7 @@ struct Workspace {
   int8_t* Xq;          // [M][K]
   uint16_t* X_O;       // [M][K] capacity, row stride K
   uint32_t* flags;     // [ceil(K/32)]
-  int32_t* gemm_cnt;   // [kGemmMaxSlices] arrival counters of split tiles
+  int32_t* gemm_cnt;   // [kGemmMaxSlices] reserved (unused)
   int32_t* gemm_part;  // [gemm_slices][256][256] int32 partial tiles
   int gemm_slices;     // partial tiles the workspace holds
   uint32_t* act_part;  // M <= 16: per 512-column slice, the outlier count, then
@@ -80,7 +80,7 @@ struct GemmArgs {
   // is dequantized with sx * sw / 127
   const int32_t* zp;
   const int32_t* wsum;
-  int32_t* cnt;      // split-K tail (Y output only): workspace counters / partials
+  int32_t* cnt;      // split-K tail (Y output only): reserved (unused) / partials
   int32_t* part;
   int part_slices;   // 0: never split
   // set by launch_gemm
