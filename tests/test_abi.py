@@ -171,11 +171,11 @@ def test_workspace_layout(i8l):
         if L["gemm_slices"]:
             assert L["gemm_partials"] - L["gemm_counters"] >= 4 * 256
         assert i8l.workspace_bytes(M, K, 123) == L["total"]
-    # split-K tail of the GEMM: tiles of a last round over 256 compute units that
-    # is at least half full (or of a problem below one round), split along K (at
-    # least 16 k-steps per split); none for decode shapes
+    # split-K tail of the GEMM: the tiles of a partial last round over 256
+    # compute units, split along K into S = min(256 / tiles, k-steps / 8) >= 2
+    # parts; none for decode shapes
     assert i8l.workspace_layout(16, 4096, 16384)["gemm_slices"] == 0
-    assert i8l.workspace_layout(2048, 14336, 43008)["gemm_slices"] == 0        # 1344 tiles
+    assert i8l.workspace_layout(2048, 14336, 43008)["gemm_slices"] == 64 * 4   # 1344 tiles
     assert i8l.workspace_layout(2048, 2048, 12200)["gemm_slices"] == 128 * 2   # 384 tiles
     assert i8l.workspace_layout(4096, 57344, 14336)["gemm_slices"] == 128 * 2  # 896 tiles
     assert i8l.workspace_layout(8192, 8192, 8192)["gemm_slices"] == 0         # 1024 tiles
