@@ -7,11 +7,14 @@
 // states are quantized row by row.  [blog, "Introduction to model
 // quantization"]: absmax codes are round(x * 127 / absmax) in [-127, 127].
 //
-// For M > 16, three launches on the caller's stream:
-//   clear     zero the column bitmask (a fill kernel, safe under graph capture)
+// For M > 16, launches on the caller's stream:
+//   clear     zero the column bitmask (a fill kernel, safe under graph capture);
+//             only where several workgroups share a column (M > 64)
 //   colflags  one pass over X: per thread 16-byte loads, 8 running column
 //             maxima; a set bit for every column whose absmax reaches the
-//             threshold (atomicOr, issued only for the rare outlier columns)
+//             threshold (atomicOr, issued only for the rare outlier columns;
+//             for M <= 64, or with the threshold off, one workgroup holds
+//             every row of its columns and stores its flag words outright)
 //   rowquant  one workgroup per row: the bitmask and its prefix popcounts go
 //             to LDS, the row is held in registers while its absmax over the
 //             regular columns is reduced, then codes are written (8 bytes per
@@ -49,9 +52,13 @@ constexpr int kColThreads = 256;
 constexpr int kColStrip = kWave * 8;   // columns per workgroup: 8 fp16 per lane
 
 // grid = (ceil(K / 512), ceil(M / rows_per_block)); waves of a block stride over rows.
+// STORE: grid.y == 1 (the block scans every row of its columns), so it stores
+// all of its flag words, zeros included, and no clear is needed; scan == 0
+// then stores zeros without reading X (decomposition off).
+template <bool STORE>
 __global__ __launch_bounds__(kColThreads) void colflags_kernel(const uint16_t* __restrict__ X, int M,
                                                               int K, int rows_per_block,
-                                                              float threshold,
+                                                              float threshold, int scan,
                                                               uint32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -60,7 +67,7 @@ __global__ __launch_bounds__(kColThreads) void colflags_kernel(const uint16_t* _
   // K % 16 == 0, so c < K means all 8 columns are in range; lanes past K scan
   // no rows (they stay in for the block-wide combine below)
   const int r0 = blockIdx.y * rows_per_block;
-  const int r1 = c < K ? min(M, r0 + rows_per_block) : r0;
+  const int r1 = (c < K && scan) ? min(M, r0 + rows_per_block) : r0;
   const uint16_t* base = X + c;
   uint32_t mx[4] = {0, 0, 0, 0};   // packed pairs of |fp16| bit patterns
   int r = r0 + wave;
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(kColThreads) void colflags_kernel(const uint16_t* _
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t h = (mx[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-    if (h2f((uint16_t)h) >= threshold) bits |= 1u << e;
+    if (scan && h2f((uint16_t)h) >= threshold) bits |= 1u << e;
   }
   // one atomic per flag word and block: the 4 lanes of a word, then the 4
   // waves (which scanned other rows of the same columns), are combined first
@@ -110,7 +117,12 @@ __global__ __launch_bounds__(kColThreads) void colflags_kernel(const uint16_t* _
     uint32_t v = 0;
 #pragma unroll
     for (int w = 0; w < kColThreads / 64; ++w) v |= s_bits[w][t];
-    if (v) atomicOr(flags + blockIdx.x * (kColStrip / 32) + t, v);
+    const int word = blockIdx.x * (kColStrip / 32) + t;
+    if constexpr (STORE) {
+      if (word < (K + 31) / 32) flags[word] = v;
+    } else if (v) {
+      atomicOr(flags + word, v);
+    }
   }
 }
 
@@ -568,16 +580,19 @@ hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float thr
     }
     return hipGetLastError();
   }
-  const int nw = (K + 31) / 32;
-  launch_fill_u32(ws.flags, nw, 0u, stream);
-  if (enabled && M > 0) {
-    const int bx = (K + kColStrip - 1) / kColStrip;
+  const int bx = (K + kColStrip - 1) / kColStrip;
+  if (!enabled || M <= kStreamMaxM) {
+    // one row block: every flag word is stored, so no clear launch
+    hipLaunchKernelGGL(colflags_kernel<true>, dim3(bx, 1), dim3(kColThreads), 0, stream, X, M, K,
+                       M, threshold, (int)enabled, ws.flags);
+  } else {
+    launch_fill_u32(ws.flags, (K + 31) / 32, 0u, stream);
     long long want = ((long long)M * bx + 2047) / 2048;
     int rows = (int)((want + 15) / 16 * 16);
     if (rows < 16) rows = 16;
     const int by = (M + rows - 1) / rows;
-    hipLaunchKernelGGL(colflags_kernel, dim3(bx, by), dim3(kColThreads), 0, stream, X, M, K, rows,
-                       threshold, ws.flags);
+    hipLaunchKernelGGL(colflags_kernel<false>, dim3(bx, by), dim3(kColThreads), 0, stream, X, M,
+                       K, rows, threshold, 1, ws.flags);
   }
   if (M > 0) {
     // Few 16-byte chunks per thread and wide workgroups: the row's loads are

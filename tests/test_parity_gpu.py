@@ -155,6 +155,31 @@ def test_quantize_activation_bitexact(lib, case):
     np.testing.assert_array_equal(host(r["X_O"])[:, :n].view(np.uint16), XO_o.view(np.uint16))
 
 
+def test_quantize_activation_reused_workspace(lib):
+    """One workspace through calls whose outlier sets shrink: no column flag
+    of an earlier call may survive (rows <= 64 store every flag word; more
+    rows clear the flags first; the threshold off stores zeros)."""
+    K = 1040
+    ws = lib.new_workspace(300, K, 0, torch.device("cuda:0"))
+    ws.fill_(0xff)
+    calls = [("m40_many", wl.make_x(40, K, 1.0, 60, 8, 20, 21)[0], 6.0),
+             ("m40_none", wl.make_x(40, K, 1.0, 0, 8, 20, 22)[0], 6.0),
+             ("m300_many", wl.make_x(300, K, 1.0, 50, 8, 20, 23)[0], 6.0),
+             ("m64_few", wl.make_x(64, K, 1.0, 2, 8, 20, 24)[0], 6.0),
+             ("m300_off", wl.make_x(300, K, 1.0, 9, 8, 20, 25)[0], math.inf),
+             ("m20_off", wl.make_x(20, K, 1.0, 9, 8, 20, 26)[0], math.inf)]
+    for name, X, t in calls:
+        say(f"quantize_activation reused workspace {name} M={X.shape[0]} K={K} t={t}")
+        r = lib.quantize_activation(dev(X), t, workspace=ws)
+        Xq_o, sx_o, idx_o, XO_o = O.quantize_activation(X, t)
+        n = int(host(r["n_out"])[0])
+        assert n == len(idx_o), name
+        np.testing.assert_array_equal(host(r["idx"])[:n], idx_o, err_msg=name)
+        np.testing.assert_array_equal(host(r["sx"]).view(np.uint32), sx_o.view(np.uint32),
+                                      err_msg=name)
+        np.testing.assert_array_equal(host(r["Xq"]), Xq_o, err_msg=name)
+
+
 # ---------------------------------------------------------------------------------
 # exact int8 GEMM (stage export)
 # ---------------------------------------------------------------------------------
