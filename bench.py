@@ -44,8 +44,8 @@ PEAK_INT8_TOPS = 5000.0
 TRAFFIC = {
     ("decode_kernel", "decode"): {"bytes": 68478750, "src": "9e0066366e1eb125"},
     ("decode_stream_kernel", "decode_mlp_down"): {"bytes": 828172344, "src": "9e0066366e1eb125"},
-    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2187081333, "src": "2cf49153bfcb8e19"},
-    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5556368372, "src": "2cf49153bfcb8e19"},
+    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2187868548, "src": "ac825c3b6c127dcd"},
+    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5555909588, "src": "ac825c3b6c127dcd"},
 }
 
 

@@ -80,7 +80,7 @@ typedef enum {
  *                                 slice of K, its outlier count and per-row
  *                                 partial maxima / minima of the activation
  *                                 stage (0 bytes for other M)
- *   gemm_counters, gemm_partials   internal (M > 16): a reserved region and
+ *   gemm_counters, gemm_partials   internal (M > 64): a reserved region and
  *                                 int32 partial tiles of the GEMM's split-K
  *                                 tail; gemm_slices partial tiles of 256x256
  * `total` is the size the call requires; it depends on M, K and N. */

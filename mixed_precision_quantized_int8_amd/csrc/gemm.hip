@@ -54,6 +54,7 @@
 // tail adds it to the summed partials), exact in int32 for K within the
 // zero-point limit, and are dequantized by sx * sw / 127.
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "launch.h"
@@ -591,16 +592,20 @@ GemmSplit gemm_split_plan(int M, int N, int K, int cus) {
 }
 
 namespace {
+// Per-device compute-unit count, queried once (0: not yet, -1: unknown).
+// Atomic, since callers may launch from several host threads.
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-    cache[dev] = n > 0 ? n : -1;
+    c = n > 0 ? n : -1;
+    cache[dev].store(c, std::memory_order_relaxed);
   }
-  return cache[dev] > 0 ? std::min(cache[dev], kGemmMaxSlices) : 0;
+  return c > 0 ? std::min(c, kGemmMaxSlices) : 0;
 }
 }  // namespace
 
@@ -608,7 +613,7 @@ hipError_t launch_gemm(const GemmArgs& in, hipStream_t stream) {
   GemmArgs a = in;
   const int nTm = (a.M + kBM - 1) / kBM, nTn = (a.N + kBN - 1) / kBN;
   GemmSplit p{nTm * nTn, 0, 1};
-  if (!a.acc && a.part && a.cnt && a.part_slices > 0) {
+  if (!a.acc && a.part && a.part_slices > 0) {
     const GemmSplit q = gemm_split_plan(a.M, a.N, a.K, device_cus());
     if (q.split_tiles > 0 && q.split_tiles * q.S <= a.part_slices) p = q;
   }

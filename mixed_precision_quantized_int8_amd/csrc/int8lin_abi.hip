@@ -9,6 +9,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <string>
+
 #include "../../include/int8lin.h"
 #include "launch.h"
 
@@ -63,8 +65,9 @@ i8l_status check_zp_k(const char* fn, int64_t K) {
   return I8L_OK;
 }
 
-// The GEMM's split-K tail (M > 16) needs arrival counters and int32 partial
-// tiles; they are sized for a device with up to kGemmMaxSlices compute units.
+// The GEMM's split-K tail (M > 64, the only shapes that reach the GEMM) needs
+// int32 partial tiles, sized for a device with up to kGemmMaxSlices compute
+// units; the counters region before them is reserved.
 i8l_workspace_layout layout_of(int64_t M, int64_t K, int64_t N) {
   i8l_workspace_layout L;
   size_t off = 0;
@@ -81,7 +84,7 @@ i8l_workspace_layout layout_of(int64_t M, int64_t K, int64_t N) {
       (M >= 1 && M <= i8l::kActSmallRows) ? (size_t)i8l::act_slices((int)K) * (1 + 2 * i8l::kActSmallRows) : 0;
   L.act_partials = off; off += up(act_words * sizeof(uint32_t));
   int slices = 0;
-  if (M > 16 && N > 0) {
+  if (M > i8l::kStreamMaxM && N > 0) {
     const i8l::GemmSplit p = i8l::gemm_split_plan((int)M, (int)N, (int)K, i8l::kGemmMaxSlices);
     slices = p.split_tiles * p.S;
   }
@@ -321,8 +324,10 @@ I8L_API i8l_status int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, 
 I8L_API const char* i8l_last_error(void) { return g_err; }
 
 I8L_API const char* i8l_build_info(void) {
-  static char info[512];
-  snprintf(info, sizeof(info), "int8lin gfx950; %s; decode: fused small-M kernel",
-           i8l::gemm_tile_info());
-  return info;
+  // built once (thread-safe static initialization), read-only afterwards
+  static const std::string info =
+      std::string("int8lin gfx950; ") + i8l::gemm_tile_info() +
+      "; M <= 64: fused kernel (M <= 16, K <= 4096) or activation kernels + weight-streaming "
+      "kernel";
+  return info.c_str();
 }
