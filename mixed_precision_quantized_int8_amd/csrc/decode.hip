@@ -577,7 +577,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
           acc[g][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[g][u], fb[b][u][c], acc[g][c], 0, 0, 0);
   };
   load_b(0, s0);
-  for (int s = s0; s < s1; s += 2 * KU) {
+  int s = s0;
+  for (; s + 2 * KU < s1; s += 2 * KU) {
     v4i fa0[MG][KU], fa1[MG][KU];
     // the codes go out before the next weight loads: the wait for them then
     // leaves those loads in flight
@@ -590,6 +591,28 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
     load_b(0, s + 2 * KU);
     __builtin_amdgcn_sched_barrier(0);
     mma(1, fa1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // The last round (always run; steps past s1 read the zero page and add 0)
+  // issues no weight loads after it, and none at all for a second buffer
+  // that lies wholly past s1.  Two straight-line variants (uniform branch), so
+  // each keeps exact load counts for its waits.
+  if (s + KU < s1) {
+    v4i fa0[MG][KU], fa1[MG][KU];
+    load_a(s, fa0);
+    load_b(1, s + KU);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0, fa0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(s + KU, fa1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1, fa1);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    v4i fa0[MG][KU];
+    load_a(s, fa0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0, fa0);
     __builtin_amdgcn_sched_barrier(0);
   }
 
