@@ -42,8 +42,8 @@ PEAK_INT8_TOPS = 5000.0
 # (profiles/traffic-decode.md: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB, the
 # factors a 512 MiB device copy gives).
 TRAFFIC = {
-    ("decode_kernel", "decode"): {"bytes": 68478750, "src": "9e0066366e1eb125"},
-    ("decode_stream_kernel", "decode_mlp_down"): {"bytes": 828172344, "src": "9e0066366e1eb125"},
+    ("decode_kernel", "decode"): {"bytes": 68493926, "src": "8f99556e532f1095"},
+    ("decode_stream_kernel", "decode_mlp_down"): {"bytes": 828347298, "src": "8f99556e532f1095"},
     ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2187868548, "src": "ac825c3b6c127dcd"},
     ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5555909588, "src": "ac825c3b6c127dcd"},
 }
