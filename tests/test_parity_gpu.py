@@ -295,6 +295,47 @@ def test_linear_deterministic(lib):
         np.testing.assert_array_equal(host(Y1).view(np.uint16), host(Y2).view(np.uint16))
 
 
+def test_linear_concurrent_host_threads(lib):
+    """The library keeps no per-call state: host threads, each with its own
+    stream and workspace, get the results a single thread gets (fused kernel,
+    streaming kernel for 8 and 40 rows, GEMM with a split tail)."""
+    import threading
+    say("int8_linear from 4 host threads")
+    shapes = [(8, 4096, 2048), (8, 8192, 512), (40, 1024, 700), (520, 2048, 1300)]
+    jobs = []
+    for i, (M, K, N) in enumerate(shapes):
+        X, W, _ = wl.make_small(M, K, N, seed=40 + i, n_out=3)
+        Xd, Wd = dev(X), dev(W)
+        Wq, sw = lib.quantize_weight(Wd)
+        ref = lib.linear(Xd, Wq, sw, Wd, 6.0)
+        ws = lib.new_workspace(M, K, N, Xd.device)
+        out = torch.empty((M, N), dtype=torch.float16, device=Xd.device)
+        jobs.append((Xd, Wq, sw, Wd, ws, out, ref))
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(job):
+        Xd, Wq, sw, Wd, ws, out, ref = job
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(5):
+                    lib.linear(Xd, Wq, sw, Wd, 6.0, workspace=ws, out=out)
+            s.synchronize()
+        except Exception as e:   # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(j,)) for j in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for (M, K, N), (*_, out, ref) in zip(shapes, jobs):
+        np.testing.assert_array_equal(host(out).view(np.uint16), host(ref).view(np.uint16),
+                                      err_msg=f"{M}x{K}x{N}")
+
+
 # ---------------------------------------------------------------------------------
 # the benchmark workloads at full size, in the launch configuration bench.py times
 # ---------------------------------------------------------------------------------
