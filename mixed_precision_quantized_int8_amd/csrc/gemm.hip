@@ -389,8 +389,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     float* sBias = sSw + kBN;                                      // [256] (0 without bias)
     int* sZc = reinterpret_cast<int*>(sBias + kBN);                // [256] 128 - zp (ZP)
     int* sWs = sZc + kBM;                                          // [256] wsum (ZP)
-    static_assert(2 * kBM * kOutG * 2 + 5 * 256 * 4 <= (int)sizeof(smem),
+    // Per wave, one 32x32 fp16 block in row order (kTS halves per row), so
+    // that Y goes out in 16-byte row pieces instead of 2-byte column values.
+    constexpr int kTS = 40;
+    uint16_t* sT = reinterpret_cast<uint16_t*>(sWs + kBN) + wave * 32 * kTS;
+    static_assert(2 * kBM * kOutG * 2 + 5 * 256 * 4 + kGemmThreads / 64 * 32 * kTS * 2 <=
+                      (int)sizeof(smem),
                   "epilogue staging must fit the LDS");
+    // N % 8 == 0: every 8-column piece of a row lies wholly inside or outside
+    // N and starts 16-byte aligned (Y is 16-byte aligned)
+    const bool vec_store = (N & 7) == 0;
     // 16-byte chunk c of staged row r sits at c ^ ((r >> 2) & 3): conflict-free
     // fragment reads with the 192-byte row stride
     auto och = [](int r, int c) { return (c ^ ((r >> 2) & 3)) << 3; };
@@ -560,7 +568,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
             y = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb, y, 0, 0, 0);
           }
         }
-        if (n < N) {
+        if (vec_store) {   // uniform
+          const float bv = sBias[wn + j * 32 + l32];   // 0 past N
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sT[d_row(r, lane) * kTS + l32] = f2h(y[r] + bv);
+          // the wave's LDS writes before its reads of other lanes' values
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int row = lane >> 1, c0 = (lane & 1) * 16;
+          const v4i p0 = *reinterpret_cast<const v4i*>(&sT[row * kTS + c0]);
+          const v4i p1 = *reinterpret_cast<const v4i*>(&sT[row * kTS + c0 + 8]);
+          const int m = m0 + wm + i * 32 + row;
+          const int nb = n0 + wn + j * 32 + c0;
+          if (m < M) {
+            if (nb < N) *reinterpret_cast<v4i*>(&a.Y[(size_t)m * N + nb]) = p0;
+            if (nb + 8 < N) *reinterpret_cast<v4i*>(&a.Y[(size_t)m * N + nb + 8]) = p1;
+          }
+          // the reads done before the next block overwrites the wave's rows
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        } else if (n < N) {
           const float bv = sBias[wn + j * 32 + l32];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
