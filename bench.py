@@ -44,8 +44,8 @@ PEAK_INT8_TOPS = 5000.0
 TRAFFIC = {
     ("decode_kernel", "decode"): {"bytes": 68493926, "src": "8f99556e532f1095"},
     ("decode_stream_kernel", "decode_mlp_down"): {"bytes": 828347298, "src": "8f99556e532f1095"},
-    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2187868548, "src": "ac825c3b6c127dcd"},
-    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5555909588, "src": "ac825c3b6c127dcd"},
+    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2186834511, "src": "2d0553e1e5f71659"},
+    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5555634139, "src": "2d0553e1e5f71659"},
 }
 
 
