@@ -6,18 +6,24 @@ outlier fp16 product, dequantize + add) on synthetic seeded inputs already
 resident in HBM; the weight is quantized once, untimed, as the layer does when
 it is placed on the GPU.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload decode]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload mlp_down_prefill]
     python bench.py --copy-calibration 512   # plain 512 MiB device copy only
+
+The default (headline) workload is the largest single-GPU configuration, the
+BLOOM-176B MLP down-projection prefill: X 4096x57344 . W 57344x14336 with 16
+outlier columns, bound by the int8 matrix cores.  The same line carries, under
+"decode", the decode configuration X 8x4096 . W 4096x16384 with 4 outlier
+columns (bound by HBM), timed the same way in the same process
+(--no-decode skips it).
+
+The K timed steps are captured into one HIP graph and replayed (--no-graph
+launches each step from Python instead).  To keep the 256 MB Infinity Cache
+from serving the weight, steps rotate over several copies of (X, Wq, sw, W, Y,
+workspace) totalling more than 512 MB.
 
 --copy-calibration runs nothing but torch's device-to-device copy of a buffer
 of known size; under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it gives the
 factor that turns those counters into bytes.
-
-The default workload is the decode shape X 8x4096 . W 4096x16384 with 4
-outlier columns.  The K timed steps are captured into one HIP graph and
-replayed (--no-graph launches each step from Python instead).  To keep the 256 MB Infinity Cache from serving the weight,
-steps rotate over several copies of (X, Wq, sw, W, Y, workspace) totalling
-more than 512 MB.
 """
 from __future__ import annotations
 
@@ -36,17 +42,14 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0
 PEAK_INT8_TOPS = 5000.0
 
-# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs,
-# scaled by the copy-kernel calibration factor; valid only for the kernel
-# source it was measured on (sha256 of the listed files).
-# (profiles/traffic-decode.md: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB, the
-# factors a 512 MiB device copy gives).
-TRAFFIC = {
-    ("decode_kernel", "decode"): {"bytes": 68493926, "src": "8f99556e532f1095"},
-    ("decode_stream_kernel", "decode_mlp_down"): {"bytes": 828347298, "src": "8f99556e532f1095"},
-    ("gemm_i8_kernel", "qkv_prefill"): {"bytes": 2186834511, "src": "2d0553e1e5f71659"},
-    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5555634139, "src": "2d0553e1e5f71659"},
-}
+# Secondary (decode) measurement: a step is ~17 us, so it is timed over more
+# steps than the headline.
+DECODE_STEPS, DECODE_WARMUP = 200, 20
+
+# HBM traffic per call of the dominant kernels from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE counter runs, scaled by the copy-kernel calibration factor; valid
+# only for the kernel sources it was measured on (sha256 of the listed files).
+TRAFFIC = {}
 
 
 def kernel_source_hash(files):
@@ -69,16 +72,16 @@ def dominant_kernel(w):
     if w.M <= 64:
         name = "decode_kernel" if w.M <= 16 and w.K <= 4096 else "decode_stream_kernel"
         return name, "hbm", ["decode.hip", "common.h"]
-    return "gemm_i8_kernel", "mfma", ["gemm.hip", "common.h"]
+    return "gemm_i8_kernel", "mfma", ["gemm.hip", "act.hip", "common.h"]
 
 
-def cpu_baseline(w, X, W, budget_s=12.0, sample_rows=64):
-    """Time the CPU oracle (as it stands) on the same workload on the host cores.
+def cpu_baseline(w, X, W, budget_s=12.0):
+    """Time the CPU oracle (as it stands) on a bounded sample of the workload.
 
-    Small-M workloads run whole; for larger M the sample is the first
-    ``sample_rows`` rows of X against the whole weight (every row of X carries
-    the same injected outlier columns, so the sample's outlier set is the
-    workload's), and the rate is scaled by the sample's share of the ops."""
+    Small workloads (M*N*K <= 2^31) run whole.  Larger ones: the first 64 rows
+    of X against the first 2048 output columns of the weight (every row of X
+    carries the same injected outlier columns, so the sample's outlier set is
+    the workload's); the rate is scaled by the sample's share of the ops."""
     import numpy as np
     from oracle import int8_oracle as O
 
@@ -89,28 +92,31 @@ def cpu_baseline(w, X, W, budget_s=12.0, sample_rows=64):
         threads = max((i.get("num_threads") or 0) for i in info) if info else None
     except Exception:
         pass
-    Wq, sw = O.quantize_weight(W)            # untimed, as on the GPU side
-    rows = w.M if w.M <= 2 * sample_rows else sample_rows
+    whole = w.M * w.N * w.K <= 2**31
+    rows = w.M if whole else min(w.M, 64)
+    cols = w.N if whole else min(w.N, 2048)
+    Ws = W if cols == w.N else np.ascontiguousarray(W[:, :cols])
+    Wq, sw = O.quantize_weight(Ws)            # untimed, as on the GPU side
     Xs = X[:rows]
     reps, t_total, out = 0, 0.0, None
     t0 = time.perf_counter()
     while reps < 100 and (time.perf_counter() - t0) < budget_s:
         s = time.perf_counter()
-        out = O.int8_linear(Xs, Wq, sw, W, w.threshold)
+        out = O.int8_linear(Xs, Wq, sw, Ws, w.threshold)
         t_total += time.perf_counter() - s
         reps += 1
     per_call = t_total / reps
-    what = (f"full {w.name} call ({w.M}x{w.K}x{w.N})" if rows == w.M else
-            f"first {rows} of {w.M} rows of the {w.name} call ({rows}x{w.K}x{w.N}), "
-            f"rate scaled by the row share")
+    what = (f"full {w.name} call ({w.M}x{w.K}x{w.N})" if whole else
+            f"first {rows} rows x first {cols} output columns of the {w.name} call "
+            f"({rows}x{w.K}x{cols}), rate scaled by the op share")
     return {
-        "value": round(2.0 * rows * w.N * w.K / per_call / 1e12, 6),
+        "value": round(2.0 * rows * cols * w.K / per_call / 1e12, 6),
         "unit": "TOPS",
         "cores": threads or os.cpu_count(),
         "kind": "oracle",
         "sample": f"{what}, weight pre-quantized, {reps} calls, {per_call * 1e3:.1f} ms/call; "
                   f"host has {os.cpu_count()} cpus",
-    }, out, Wq, sw, rows
+    }, out, Wq, rows, cols
 
 
 def copy_ceiling(torch, dev, mib=1024, reps=10):
@@ -148,6 +154,7 @@ def fp16_context(torch, w, sets, int8_ms, reps):
     b.record()
     b.synchronize()
     ms = a.elapsed_time(b) / reps
+    del out
     return {"op": "torch.matmul fp16 X.W (vendor BLAS), eager launches, same buffer sets",
             "ms_per_call": round(ms, 5),
             "tflops": round(2.0 * w.M * w.N * w.K / (ms * 1e-3) / 1e12, 2),
@@ -167,12 +174,173 @@ def copy_calibration(mib):
                       "copy_calibration_bytes_written": mib << 20, "launches": 3}))
 
 
+def time_steps(torch, step, K, graph):
+    """Time exactly K steps: captured once into a HIP graph and replayed
+    (events around the replay), or launched eagerly with events per step.
+    Returns (ms per step, eager ms per step or None, per-step ms array or None)."""
+    import numpy as np
+    if graph:
+        # The K steps are captured once into a HIP graph and replayed: the
+        # kernels then run back to back, as in a serving loop, instead of
+        # waiting on the Python launch path.  The graph holds no memset nodes
+        # (the library clears its flags with a fill kernel).
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            for i in range(3):
+                step(i)
+        torch.cuda.current_stream().wait_stream(s_cap)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                step(i)
+        g.replay()   # untimed first replay
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / K
+        # eager launches, for reference (Python launch path included)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(K):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return ms, e0.elapsed_time(e1) / K, None
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(K):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    t1.record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    return t0.elapsed_time(t1) / K, None, per
+
+
+def measure(torch, pkg, workloads, w, args, steps, warmup, with_fp16_context):
+    """Set up one workload's rotated buffer sets, warm up, time `steps` steps.
+
+    Returns (result dict, X, W, the first set's Y and Wq) -- the caller checks
+    parity on them and frees them."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    X, W, _ = workloads.make_inputs(w)
+    Xd = torch.from_numpy(X).to(dev)
+    Wd = torch.from_numpy(W).to(dev)
+    Wq, sw = pkg.quantize_weight(Wd)
+    ws_bytes = pkg.workspace_bytes(w.M, w.K, w.N)
+    # bytes a step streams: X, Wq, Y (the fp16 weight is only read at outlier rows)
+    set_bytes = Xd.numel() * 2 + Wq.numel() + 2 * w.M * w.N
+    R = args.rotate or max(1, min(16, -(-512 * 2**20 // set_bytes)))
+    sets = []
+    for r in range(R):
+        s = (Xd, Wq, sw, Wd) if r == 0 else (Xd.clone(), Wq.clone(), sw.clone(), Wd.clone())
+        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+        Y = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+        S = pkg.weight_code_sums(s[1]) if args.zero_point else None   # once per layer
+        sets.append((*s, ws, Y, S))
+    bias_t = (torch.randn(w.N, device=dev) * 0.1).half() if args.bias else None
+
+    def step(i):
+        x, q, s, wf, ws, y, S = sets[i % R]
+        rows = None if args.rebuilt_rows else wf
+        if args.zero_point:
+            pkg.linear_zp(x, q, s, S, rows, w.threshold, workspace=ws, out=y, bias=bias_t)
+        else:
+            pkg.linear(x, q, s, rows, w.threshold, workspace=ws, out=y, bias=bias_t)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms, eager_ms, per = time_steps(torch, step, steps, not args.no_graph)
+
+    kname, bound, files = dominant_kernel(w)
+    src_hash = kernel_source_hash(files)
+    if bound == "hbm":
+        alg = algorithmic_bytes(w)
+        achieved = alg / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+        # one call is exactly one launch of the fused kernel
+        launch = ("one launch of decode_kernel per call" if kname == "decode_kernel" else
+                  "activation kernels + decode_stream_kernel per call")
+    else:
+        achieved = w.int_ops / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
+                "unit": "TOPS", "frac": round(achieved / PEAK_INT8_TOPS, 4)}
+        launch = ("whole call: flag clear, colflags_kernel, rowquant_kernel, then "
+                  "gemm_i8_kernel whole tiles, split-K tail and fix-up")
+    # counter figures were taken on the default layer (fp16 outlier rows, absmax codes)
+    tr = None if (args.zero_point or args.rebuilt_rows or args.bias) else TRAFFIC.get((kname, w.name))
+    roof["traffic"] = tr["bytes"] if tr and tr["src"] == src_hash else None
+    roof["kernel"] = kname
+    roof["timed"] = launch
+    roof["step_ms"] = round(ms, 5)
+    if per is not None:
+        roof["step_ms_p10_p50_p90"] = [round(float(np.percentile(per, q)), 5) for q in (10, 50, 90)]
+    roof["kernel_src"] = src_hash
+
+    res = {
+        "value": round(w.int_ops / (ms * 1e-3) / 1e12, 3),
+        "unit": "TOPS",
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N,
+                   "outlier_columns": w.n_out, "threshold": w.threshold,
+                   "buffer_sets": R, "x_dtype": "fp16", "y_dtype": "fp16",
+                   "outlier_rows": "rebuilt from codes" if args.rebuilt_rows else "fp16 weight",
+                   "bias": bool(args.bias),
+                   "activation_codes": "zero-point" if args.zero_point else "absmax",
+                   "ops_int8": 2 * w.M * w.N * (w.K - w.n_out),
+                   "ops_fp16": 2 * w.M * w.N * w.n_out,
+                   "algorithmic_bytes": algorithmic_bytes(w),
+                   "launch": "eager" if args.no_graph else "hip_graph"},
+        "roofline": roof,
+    }
+    if eager_ms is not None:
+        res["eager_ms_per_step"] = round(eager_ms, 5)
+    if with_fp16_context:
+        res["fp16_context"] = fp16_context(torch, w, sets, ms, min(steps, 50))
+    Y0, Wq0 = sets[0][5], sets[0][1]
+    del sets, Xd, Wd
+    return res, X, W, Y0, Wq0
+
+
+def parity_of(w, y_dev, wq_dev, ref, Wq_o, rows, cols):
+    """The benchmark's own output against the oracle on the sampled block."""
+    import numpy as np
+    y = y_dev[:rows, :cols].cpu().numpy().astype(np.float64)
+    err = np.abs(y - ref["Y64"])
+    tol = np.maximum(2e-3 * np.abs(ref["Y64"]), 1e-2)
+    return {"checked": f"Y[:{rows}, :{cols}], Wq[:{cols}]",
+            "Y_within_tol": bool(np.all(err <= tol)),
+            "Wq_bitexact": bool(np.array_equal(wq_dev[:cols].cpu().numpy(), Wq_o)),
+            "max_abs_err": float(err.max())}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mlp_down_prefill")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the secondary decode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: auto, >512 MB)")
     ap.add_argument("--rebuilt-rows", action="store_true",
@@ -197,7 +365,6 @@ def main():
         copy_calibration(args.copy_calibration)
         return
 
-    import numpy as np
     import torch
 
     import mixed_precision_quantized_int8_amd as pkg
@@ -207,165 +374,48 @@ def main():
         from mixed_precision_quantized_int8_amd import build
         build.build_library()
 
-    w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    X, W, _ = workloads.make_inputs(w)
-    Xd = torch.from_numpy(X).to(dev)
-    Wd = torch.from_numpy(W).to(dev)
-    Wq, sw = pkg.quantize_weight(Wd)
-    ws_bytes = pkg.workspace_bytes(w.M, w.K, w.N)
-    # bytes a step streams: X, Wq, Y (the fp16 weight is only read at outlier rows)
-    set_bytes = Xd.numel() * 2 + Wq.numel() + 2 * w.M * w.N
-    R = args.rotate or max(1, min(16, -(-512 * 2**20 // set_bytes)))
-    sets = []
-    for r in range(R):
-        if r == 0:
-            s = (Xd, Wq, sw, Wd)
-        else:
-            s = (Xd.clone(), Wq.clone(), sw.clone(), Wd.clone())
-        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
-        Y = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
-        S = pkg.weight_code_sums(s[1]) if args.zero_point else None   # once per layer
-        sets.append((*s, ws, Y, S))
-
-    bias_t = (torch.randn(w.N, device=dev) * 0.1).half() if args.bias else None
-
-    def step(i):
-        x, q, s, wf, ws, y, S = sets[i % R]
-        rows = None if args.rebuilt_rows else wf
-        if args.zero_point:
-            pkg.linear_zp(x, q, s, S, rows, w.threshold, workspace=ws, out=y, bias=bias_t)
-        else:
-            pkg.linear(x, q, s, rows, w.threshold, workspace=ws, out=y, bias=bias_t)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    K = args.steps
-    eager_ms = None
-    if not args.no_graph:
-        # The K steps are captured once into a HIP graph and replayed: the
-        # kernels then run back to back, as in a serving loop, instead of
-        # waiting on the Python launch path.  The graph holds no memset nodes
-        # (the library clears its flags with a fill kernel).
-        s_cap = torch.cuda.Stream()
-        s_cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s_cap):
-            for i in range(3):
-                step(i)
-        torch.cuda.current_stream().wait_stream(s_cap)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(K):
-                step(i)
-        graph.replay()   # untimed first replay
-        torch.cuda.synchronize()
-        t_begin = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        t_begin.record()
-        graph.replay()
-        t_end.record()
-        torch.cuda.synchronize()
-        ms_total = t_begin.elapsed_time(t_end)
-        ms_per_step = ms_total / K
-        per_launch = np.array([ms_per_step])
-        ms_launch = ms_per_step
-        # eager launches, for reference (Python launch path included)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(K):
-            step(i)
-        e1.record()
-        torch.cuda.synchronize()
-        eager_ms = e0.elapsed_time(e1) / K
-    else:
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-        t_begin = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t_begin.record()
-        for i in range(K):
-            starts[i].record()
-            step(i)
-            ends[i].record()
-        t_end.record()
-        torch.cuda.synchronize()
-        ms_total = t_begin.elapsed_time(t_end)
-        ms_per_step = ms_total / K
-        per_launch = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
-        ms_launch = float(per_launch.mean())
-
-    value = w.int_ops / (ms_per_step * 1e-3) / 1e12
-    kname, bound, files = dominant_kernel(w)
-    src_hash = kernel_source_hash(files)
-    if bound == "hbm":
-        alg = algorithmic_bytes(w)
-        achieved = alg / (ms_launch * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    else:
-        achieved = w.int_ops / (ms_launch * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
-                "unit": "TOPS", "frac": round(achieved / PEAK_INT8_TOPS, 4)}
-    # counter figures were taken on the default layer (fp16 outlier rows, absmax codes)
-    tr = None if (args.zero_point or args.rebuilt_rows) else TRAFFIC.get((kname, w.name))
-    roof["traffic"] = tr["bytes"] if tr and tr["src"] == src_hash else None
-    roof["kernel"] = kname
-    roof["kernel_ms"] = round(ms_launch, 5)
-    if args.no_graph:
-        roof["kernel_ms_p10_p50_p90"] = [round(float(np.percentile(per_launch, q)), 5)
-                                         for q in (10, 50, 90)]
-    roof["kernel_src"] = src_hash
-    roof["measured_copy_GBs"] = round(copy_ceiling(torch, dev), 1)
-
+    w = workloads.WORKLOADS[args.workload]
+    res, X, W, Y0, Wq0 = measure(torch, pkg, workloads, w, args, args.steps, args.warmup,
+                                 not args.no_fp16_context)
     result = {
         "metric": "int8_linear TOPS and % of int8-MFMA / HBM roofline on one MI355X",
-        "value": round(value, 3),
+        "value": res["value"],
         "unit": "TOPS",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N,
-                   "outlier_columns": w.n_out, "threshold": w.threshold,
-                   "buffer_sets": R, "x_dtype": "fp16", "y_dtype": "fp16",
-                   "outlier_rows": "rebuilt from codes" if args.rebuilt_rows else "fp16 weight",
-                   "bias": bool(args.bias),
-                   "activation_codes": "zero-point" if args.zero_point else "absmax",
-                   "ops_int8": 2 * w.M * w.N * (w.K - w.n_out), "ops_fp16": 2 * w.M * w.N * w.n_out,
-                   "launch": "eager" if args.no_graph else "hip_graph"},
-        "roofline": roof,
+        "config": res["config"],
+        "roofline": res["roofline"],
     }
-    if eager_ms is not None:
-        result["eager_ms_per_step"] = round(eager_ms, 5)
+    for k in ("eager_ms_per_step", "fp16_context"):
+        if k in res:
+            result[k] = res[k]
+    result["roofline"]["measured_copy_GBs"] = round(copy_ceiling(torch, dev), 1)
 
-    if not args.no_fp16_context:
-        result["fp16_context"] = fp16_context(torch, w, sets, ms_per_step, min(K, 50))
-
+    default_layer = not (args.rebuilt_rows or args.bias or args.zero_point)
     if not args.no_cpu_baseline:
-        if args.rebuilt_rows or args.bias or args.zero_point:
+        if not default_layer:
             raise SystemExit("the CPU baseline and parity check cover the default layer only "
                              "(run with --no-cpu-baseline)")
-        cb, ref, Wq_o, sw_o, rows = cpu_baseline(w, X, W)
+        cb, ref, Wq_o, rows, cols = cpu_baseline(w, X, W)
         result["cpu_baseline"] = cb
-        y = sets[0][5][:rows].cpu().numpy().astype(np.float64)
-        err = np.abs(y - ref["Y64"])
-        tol = np.maximum(2e-3 * np.abs(ref["Y64"]), 1e-2)
-        result["parity"] = {
-            "Y_within_tol": bool(np.all(err <= tol)),
-            "Wq_bitexact": bool(np.array_equal(Wq.cpu().numpy(), Wq_o)),
-            "max_abs_err": float(err.max()),
-        }
+        result["parity"] = parity_of(w, Y0, Wq0, ref, Wq_o, rows, cols)
+    del X, W, Y0, Wq0
+    torch.cuda.empty_cache()
+
+    if not args.no_decode and w.name != "decode":
+        wd = workloads.WORKLOADS["decode"]
+        dres, *_ = measure(torch, pkg, workloads, wd, args, DECODE_STEPS, DECODE_WARMUP,
+                           not args.no_fp16_context)
+        result["decode"] = dres
     print(json.dumps(result))
 
 

@@ -168,12 +168,19 @@ i8l_status int8_quantize_activation(const uint16_t *X, int64_t M, int64_t K, flo
 
 /* Exact int8 GEMM on its own ([blog, "Introduction to model quantization"]:
  * the normalised int8 matrices are multiplied), the kernel int8_linear uses
- * for M > 16 with its int32 result written out instead of dequantized.
- *   Xq   int8 [M][K]
- *   Wq   int8 [N][K]
- *   acc  int32 [M][N]  out: acc[i][n] = sum_k Xq[i][k] * Wq[n][k] */
+ * for M > 64 with its int32 result written out instead of dequantized.
+ *   Xq         int8 [M][K]
+ *   Wq         int8 [N][K]
+ *   acc        int32 [M][N]  out: acc[i][n] = sum_k Xq[i][k] * Wq[n][k]
+ *   workspace  NULL: every 256x256 output tile is computed whole.  Otherwise
+ *              at least i8l_linear_workspace_bytes(M, K, N) bytes, 16-byte
+ *              aligned: the tiles of a partial last round over the compute
+ *              units are then split along K, their int32 partials stored in
+ *              the workspace and summed by a fix-up launch, exactly as in
+ *              int8_linear (too small: I8L_ERR_WORKSPACE).  The result is the
+ *              same exact integer either way. */
 i8l_status int8_gemm_i32(const int8_t *Xq, const int8_t *Wq, int64_t M, int64_t N, int64_t K,
-                         int32_t *acc, void *stream);
+                         int32_t *acc, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---- Zero-point variant ----------------------------------------------------
  * [blog, "Introduction to model quantization"] describes, next to absmax, the

@@ -100,8 +100,14 @@ def _linear_args(X, Wq, sw, W, bias, workspace, out):
             raise ValueError(f"bias must be [{N}], got {tuple(bias.shape)}")
     if workspace is None:
         workspace = new_workspace(M, K, N, X.device)
+    else:
+        _require(workspace, torch.uint8, "workspace")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    else:
+        _require(out, torch.float16, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be [{M}][{N}], got {tuple(out.shape)}")
     return M, K, N, workspace, out
 
 
@@ -187,6 +193,8 @@ def quantize_activation(X, threshold=6.0, workspace=None):
     X_O = torch.empty((M, K), dtype=torch.float16, device=dev)
     if workspace is None:
         workspace = new_workspace(M, K, 0, dev)
+    else:
+        _require(workspace, torch.uint8, "workspace")
     with torch.cuda.device(dev):
         check(lib().int8_quantize_activation(
             X.data_ptr(), M, K, float(threshold), Xq.data_ptr(), sx.data_ptr(), idx.data_ptr(),
@@ -209,6 +217,8 @@ def quantize_activation_zp(X, threshold=6.0, workspace=None):
     X_O = torch.empty((M, K), dtype=torch.float16, device=dev)
     if workspace is None:
         workspace = new_workspace(M, K, 0, dev)
+    else:
+        _require(workspace, torch.uint8, "workspace")
     with torch.cuda.device(dev):
         check(lib().int8_quantize_activation_zp(
             X.data_ptr(), M, K, float(threshold), Xq.data_ptr(), zp.data_ptr(), xscale.data_ptr(),
@@ -217,8 +227,12 @@ def quantize_activation_zp(X, threshold=6.0, workspace=None):
     return {"Xq": Xq, "zp": zp, "xscale": xscale, "idx": idx, "n_out": n_out, "X_O": X_O}
 
 
-def gemm_i32(Xq, Wq):
-    """Exact int8 GEMM: Xq int8 [M][K], Wq int8 [N][K] -> int32 [M][N]."""
+def gemm_i32(Xq, Wq, workspace=None):
+    """Exact int8 GEMM: Xq int8 [M][K], Wq int8 [N][K] -> int32 [M][N].
+
+    With ``workspace`` (uint8, at least ``workspace_bytes(M, K, N)``) the
+    output tiles of a partial last round are split along K and summed as in
+    ``linear``; without it every tile is computed whole."""
     torch = _torch()
     _require(Xq, torch.int8, "Xq")
     _require(Wq, torch.int8, "Wq")
@@ -227,7 +241,11 @@ def gemm_i32(Xq, Wq):
     if Wq.shape[1] != K:
         raise ValueError("Xq and Wq must share K")
     acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    if workspace is not None:
+        _require(workspace, torch.uint8, "workspace")
+    ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel()) if workspace is not None \
+        else (None, 0)
     with torch.cuda.device(Xq.device):
         check(lib().int8_gemm_i32(Xq.data_ptr(), Wq.data_ptr(), M, N, K, acc.data_ptr(),
-                                  _stream(Xq)))
+                                  ws_ptr, ws_bytes, _stream(Xq)))
     return acc

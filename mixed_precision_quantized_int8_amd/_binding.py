@@ -90,7 +90,7 @@ def lib() -> ctypes.CDLL:
     L.int8_linear_bias.restype = ctypes.c_int
     L.int8_quantize_activation.argtypes = [vp, i64, i64, f32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.int8_quantize_activation.restype = ctypes.c_int
-    L.int8_gemm_i32.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+    L.int8_gemm_i32.argtypes = [vp, vp, i64, i64, i64, vp, vp, sz, vp]
     L.int8_gemm_i32.restype = ctypes.c_int
     L.int8_weight_code_sums.argtypes = [vp, i64, i64, vp, vp]
     L.int8_weight_code_sums.restype = ctypes.c_int

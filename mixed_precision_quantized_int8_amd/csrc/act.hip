@@ -11,7 +11,8 @@
 //   clear     zero the column bitmask (a fill kernel, safe under graph capture);
 //             only where several workgroups share a column (M > 64)
 //   colflags  one pass over X: per thread 16-byte loads, 8 running column
-//             maxima; a set bit for every column whose absmax reaches the
+//             maxima (NaN entries count as 0: a NaN never reaches the
+//             threshold); a set bit for every column whose maximum reaches the
 //             threshold (atomicOr, issued only for the rare outlier columns;
 //             for M <= 64, or with the threshold off, one workgroup holds
 //             every row of its columns and stores its flag words outright)
@@ -79,8 +80,8 @@ __global__ __launch_bounds__(kColThreads) void colflags_kernel(const uint16_t* _
     v4i e = *reinterpret_cast<const v4i*>(base + (size_t)(r + 12) * K);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t x0 = (uint32_t)a[j] & 0x7fff7fffu, x1 = (uint32_t)b[j] & 0x7fff7fffu;
-      uint32_t x2 = (uint32_t)d[j] & 0x7fff7fffu, x3 = (uint32_t)e[j] & 0x7fff7fffu;
+      uint32_t x0 = habs2_nonan((uint32_t)a[j]), x1 = habs2_nonan((uint32_t)b[j]);
+      uint32_t x2 = habs2_nonan((uint32_t)d[j]), x3 = habs2_nonan((uint32_t)e[j]);
       // per-halfword unsigned max
       uint32_t lo = max(max(x0 & 0xffffu, x1 & 0xffffu), max(x2 & 0xffffu, x3 & 0xffffu));
       uint32_t hi = max(max(x0 >> 16, x1 >> 16), max(x2 >> 16, x3 >> 16));
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kColThreads) void colflags_kernel(const uint16_t* _
     v4i a = *reinterpret_cast<const v4i*>(base + (size_t)r * K);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t x0 = (uint32_t)a[j] & 0x7fff7fffu;
+      uint32_t x0 = habs2_nonan((uint32_t)a[j]);
       uint32_t lo = max(x0 & 0xffffu, mx[j] & 0xffffu);
       uint32_t hi = max(x0 >> 16, mx[j] >> 16);
       mx[j] = lo | (hi << 16);
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(kSmallThreads) void act_small_scan_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       cm[j] = __builtin_elementwise_max(cm[j],
-                                        __builtin_bit_cast(u16x2, (uint32_t)x[i][j] & 0x7fff7fffu));
+                                        __builtin_bit_cast(u16x2, habs2_nonan((uint32_t)x[i][j])));
     s_cm[wave][lane][j] = __builtin_bit_cast(uint32_t, cm[j]);
   }
   lds_sync();

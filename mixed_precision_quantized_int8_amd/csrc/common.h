@@ -24,6 +24,16 @@ __device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even, ov
 // |x| of an fp16 value as an fp16 bit pattern; for finite values the unsigned
 // order of these patterns is the order of the magnitudes.
 __device__ __forceinline__ uint32_t habs_bits(uint32_t b) { return b & 0x7fffu; }
+// The same for the two fp16 values of a dword, with NaN patterns (above
+// 0x7c00) mapped to 0: the outlier test asks whether some entry of a column
+// has |x| >= threshold, which a NaN never does, so a column maximum built from
+// these magnitudes ignores NaNs.  (m + 0x3ff carries into bit 15 of its half
+// exactly when m > 0x7c00, and never into the other half.)
+__device__ __forceinline__ uint32_t habs2_nonan(uint32_t x) {
+  const uint32_t m = x & 0x7fff7fffu;
+  const uint32_t nan = ((m + 0x03ff03ffu) >> 15) & 0x00010001u;
+  return m & ~(nan * 0xffffu);
+}
 
 // Absmax code of one value: clamp(round_half_away(fp32(x) * inv), -127, 127),
 // where inv = fl32(127 / absmax) is computed once per vector by the caller

@@ -226,9 +226,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     const uint32_t lmax = smax[0] > smax[1] ? smax[0] : smax[1];
     hm[j] = 0;
     if (__ballot(lmax >= T) != 0) {
+      // a column is an outlier when some entry has |x| >= T; a NaN (pattern
+      // above 0x7c00) never does
       uint32_t h = 0;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) h |= (habs_bits(half_at(xr[j], e)) >= T ? 1u : 0u) << e;
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t b = habs_bits(half_at(xr[j], e));
+        h |= (b >= T && b <= 0x7c00u ? 1u : 0u) << e;
+      }
 #pragma unroll
       for (int off = 1; off < MR; off <<= 1) h |= __shfl_xor(h, off, 64);
       hm[j] = h;

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   }   // !FIX
   __syncthreads();   // all waves done with the ring before the epilogue reuses it
 
-  if constexpr (!OUT_I32 && SPLIT && !FIX) {
+  if constexpr (SPLIT && !FIX) {
     // Split tile: store this K range's int32 partial and end; the fix-up
     // launch sums the S partials (exact integer sums, in any order).  The
     // partial is kept in register-fragment order (16-byte piece q of thread
@@ -355,17 +355,52 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     return;
   }
 
+  // Exact int32 value of fragment (i, j): the accumulators of a whole tile,
+  // or, in the fix-up of a split tile, the sum of its S partials, read four at
+  // a time with every load unconditional (partials past S read zero from the
+  // range check), so that they are in flight together.
+  auto tile_sum = [&](int i, int j, int (&tot)[16]) {
+    if constexpr (SPLIT) {
+      constexpr int kTile = kBM * kBN;
+      const buf_rsrc rp = make_rsrc(a.part + (size_t)slot * a.split_S * kTile,
+                                    (uint32_t)(a.split_S * kTile * 4));
+      const uint32_t fo = (uint32_t)(((i * 2 + j) * 4 * kGemmThreads + t) * 16);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tot[r] = 0;
+      for (int s2 = 0; s2 < a.split_S; s2 += 4) {   // uniform
+        v4i p[4][4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            p[k][q] = buf_load16(rp, (uint32_t)((s2 + k) * kTile * 4) + fo +
+                                         (uint32_t)(q * kGemmThreads * 16));
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tot[4 * q + e] += p[k][q][e];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tot[r] = acc[i][j][r];
+    }
+  };
+
   if constexpr (OUT_I32) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int n = n0 + wn + j * 32 + l32;
+        int tot[16];
+        tile_sum(i, j, tot);
         if (n >= N) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm + i * 32 + d_row(r, lane);
-          if (m < M) a.acc[(size_t)m * N + n] = acc[i][j][r];
+          if (m < M) a.acc[(size_t)m * N + n] = tot[r];
         }
       }
     return;
@@ -502,35 +537,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
         const int n = n0 + wn + j * 32 + l32;
         const float swv = sSw[wn + j * 32 + l32];
         int tot[16];
-        if constexpr (SPLIT) {
-          // the S partials of this fragment, four at a time, every load
-          // unconditional (partials past S read zero from the range check), so
-          // that they are in flight together
-          constexpr int kTile = kBM * kBN;
-          const buf_rsrc rp = make_rsrc(a.part + (size_t)slot * a.split_S * kTile,
-                                        (uint32_t)(a.split_S * kTile * 4));
-          const uint32_t fo = (uint32_t)(((i * 2 + j) * 4 * kGemmThreads + t) * 16);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) tot[r] = 0;
-          for (int s2 = 0; s2 < a.split_S; s2 += 4) {   // uniform
-            v4i p[4][4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                p[k][q] = buf_load16(rp, (uint32_t)((s2 + k) * kTile * 4) + fo +
-                                             (uint32_t)(q * kGemmThreads * 16));
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tot[4 * q + e] += p[k][q][e];
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) tot[r] = acc[i][j][r];
-        }
+        tile_sum(i, j, tot);
         if constexpr (ZP && SPLIT) {   // sum (q - zp) w = sum (q - 128) w + (128 - zp) S[n], mod 2^32
           const uint32_t wsv = (uint32_t)sWs[wn + j * 32 + l32];
 #pragma unroll
@@ -642,15 +649,22 @@ hipError_t launch_gemm(const GemmArgs& in, hipStream_t stream) {
   GemmArgs a = in;
   const int nTm = (a.M + kBM - 1) / kBM, nTn = (a.N + kBN - 1) / kBN;
   GemmSplit p{nTm * nTn, 0, 1};
-  if (!a.acc && a.part && a.part_slices > 0) {
+  if (a.part && a.part_slices > 0) {
     const GemmSplit q = gemm_split_plan(a.M, a.N, a.K, device_cus());
     if (q.split_tiles > 0 && q.split_tiles * q.S <= a.part_slices) p = q;
   }
   a.full_tiles = p.full_tiles;
   a.split_S = p.S;
-  if (a.acc) {
-    hipLaunchKernelGGL((gemm_i8_kernel<true, false, false>), dim3(p.full_tiles),
-                       dim3(kGemmThreads), 0, stream, a);
+  if (a.acc) {   // int32 output: the same tiles, splits and fix-up sums as for Y
+    if (p.full_tiles > 0)
+      hipLaunchKernelGGL((gemm_i8_kernel<true, false, false>), dim3(p.full_tiles),
+                         dim3(kGemmThreads), 0, stream, a);
+    if (p.split_tiles > 0) {
+      hipLaunchKernelGGL((gemm_i8_kernel<true, true, false>), dim3(p.split_tiles * p.S),
+                         dim3(kGemmThreads), 0, stream, a);
+      hipLaunchKernelGGL((gemm_i8_kernel<true, true, false, true>), dim3(p.split_tiles),
+                         dim3(kGemmThreads), 0, stream, a);
+    }
     return hipGetLastError();
   }
   // whole tiles, then the split tail (both launches fill the chip)

@@ -307,7 +307,8 @@ I8L_API i8l_status int8_quantize_activation_zp(const uint16_t* X, int64_t M, int
 }
 
 I8L_API i8l_status int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N,
-                                 int64_t K, int32_t* acc, void* stream) {
+                                 int64_t K, int32_t* acc, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   const char* fn = "int8_gemm_i32";
   i8l_status s = check_shape(fn, M, K, N);
   if (s != I8L_OK) return s;
@@ -315,9 +316,24 @@ I8L_API i8l_status int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, 
   REQUIRE_PTR(fn, Xq, 16);
   REQUIRE_PTR(fn, Wq, 16);
   REQUIRE_PTR(fn, acc, 16);
+  // with a workspace the tiles are split along K exactly as int8_linear splits
+  // them; without one every tile is computed whole
+  int32_t* part = nullptr;
+  int slices = 0;
+  if (workspace) {
+    if (!aligned(workspace, 16))
+      return fail(I8L_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+    const i8l_workspace_layout L = layout_of(M, K, N);
+    if (workspace_bytes < L.total)
+      return fail(I8L_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn,
+                  workspace_bytes, L.total);
+    const i8l::Workspace w = carve(workspace, L);
+    part = w.gemm_part;
+    slices = w.gemm_slices;
+  }
   (void)hipGetLastError();
   i8l::GemmArgs g{Xq, Wq, (int)M, (int)N, (int)K, nullptr, nullptr, nullptr, nullptr, nullptr,
-                  nullptr, nullptr, acc, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 1};
+                  nullptr, nullptr, acc, nullptr, nullptr, nullptr, nullptr, part, slices, 0, 1};
   return hip_status(fn, i8l::launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 

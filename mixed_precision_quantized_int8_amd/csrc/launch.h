@@ -61,7 +61,9 @@ hipError_t launch_weight_code_sums(const int8_t* Wq, int N, int K, int32_t* S,
 
 // int8 GEMM on the matrix cores.  With Y != nullptr: dequantize with sx/sw, add
 // the fp16 outlier product (X_O against rows idx of W_rows) and store fp16 Y.
-// With acc != nullptr: store the raw int32 accumulators instead.
+// With acc != nullptr: store the raw int32 accumulators instead.  Either way,
+// given partial-tile space (part, part_slices) the tiles of a partial last
+// round are split along K and summed by a fix-up launch.
 struct GemmArgs {
   const int8_t* Xq;
   const int8_t* Wq;
@@ -80,7 +82,7 @@ struct GemmArgs {
   // is dequantized with sx * sw / 127
   const int32_t* zp;
   const int32_t* wsum;
-  int32_t* cnt;      // split-K tail (Y output only): reserved (unused) / partials
+  int32_t* cnt;      // split-K tail: reserved (unused) / partials
   int32_t* part;
   int part_slices;   // 0: never split
   // set by launch_gemm

@@ -55,6 +55,11 @@ its reason in the design notes of the repository):
       Codes are kept as q - 128 (int8) and the weight stays absmax per
       column, so sum_k (q - zp) w = sum_k (q - 128) w + (128 - zp) S[n] with
       S[n] = sum_k Wq[n][k]; K <= 66304 keeps every such sum inside int32.
+  r12 non-finite X (outside the layer's contract, but the outlier set is still
+      defined once): a column is an outlier when some entry has |x| >= t; a
+      NaN entry never satisfies that (NaN >= t is false), so it neither makes
+      its column an outlier nor keeps a large entry beside it from doing so;
+      +/-inf reaches every finite t.
 
 Layouts (row-major numpy arrays):
   X  fp16 [M][K]        W  fp16 [K][N]  (math layout, Y = X @ W)
@@ -78,7 +83,6 @@ __all__ = [
     "outlier_columns",
     "quantize_activation",
     "int8_matmul",
-    "int8_matmul_entries",
     "outlier_matmul",
     "dequantize_add",
     "int8_linear",
@@ -159,14 +163,15 @@ def outlier_columns(X16: np.ndarray, threshold: float) -> np.ndarray:
 
     [blog, "A gentle summary of LLM.int8()"], step 1: outliers are taken out of
     the hidden states column by column; [blog, "A closer look at the MatMul"]:
-    magnitude 6 or more.  A column is an outlier when its absolute maximum over
-    all rows reaches the threshold.
+    magnitude 6 or more.  A column is an outlier when some entry of it, in any
+    row, has magnitude at least the threshold (r12: a NaN entry never does).
     """
     X = np.asarray(X16, dtype=np.float16)
     if not decomposition_enabled(threshold) or X.shape[0] == 0:
         return np.zeros(0, dtype=np.int32)
-    colmax = np.abs(X.astype(np.float32)).max(axis=0)
-    return np.nonzero(colmax >= np.float32(threshold))[0].astype(np.int32)
+    with np.errstate(invalid="ignore"):
+        hit = np.abs(X.astype(np.float32)) >= np.float32(threshold)
+    return np.nonzero(hit.any(axis=0))[0].astype(np.int32)
 
 
 def quantize_activation(X16: np.ndarray, threshold: float):
@@ -213,17 +218,6 @@ def int8_matmul(Xq: np.ndarray, Wq: np.ndarray, block: int = 2048) -> np.ndarray
         B = Wq[n0:n0 + block].astype(np.float64)
         acc[:, n0:n0 + block] = (A @ B.T).astype(np.int32)
     return acc
-
-
-def int8_matmul_entries(Xq, Wq, rows, cols) -> np.ndarray:
-    """acc at the listed (rows[j], cols[j]) pairs, one dot product each."""
-    Xq = np.asarray(Xq, dtype=np.int8)
-    Wq = np.asarray(Wq, dtype=np.int8)
-    rows = np.asarray(rows, dtype=np.int64)
-    cols = np.asarray(cols, dtype=np.int64)
-    return np.einsum(
-        "jk,jk->j", Xq[rows].astype(np.float64), Wq[cols].astype(np.float64)
-    ).astype(np.int32)
 
 
 def outlier_matmul(X_O: np.ndarray, W16: np.ndarray, idx: np.ndarray) -> np.ndarray:

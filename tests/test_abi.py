@@ -91,9 +91,12 @@ def test_other_entry_points_validate(i8l):
     assert L.int8_quantize_weight(P16, 70, 32, P16, P16, None) == INVALID
     assert L.int8_quantize_weight(P16, 200000, 32, P16, P16, None) == K_TOO_LARGE
     assert L.int8_quantize_weight(P16, 64, 0, P16, P16, None) == OK
-    assert L.int8_gemm_i32(P16, P16, 4, 4, 24, P16, None) == INVALID
-    assert L.int8_gemm_i32(None, P16, 4, 4, 32, P16, None) == INVALID
-    assert L.int8_gemm_i32(P16, P16, 0, 4, 32, P16, None) == OK
+    assert L.int8_gemm_i32(P16, P16, 4, 4, 24, P16, None, 0, None) == INVALID
+    assert L.int8_gemm_i32(None, P16, 4, 4, 32, P16, None, 0, None) == INVALID
+    assert L.int8_gemm_i32(P16, P16, 0, 4, 32, P16, None, 0, None) == OK
+    # a workspace must be aligned and large enough for the split tail
+    assert L.int8_gemm_i32(P16, P16, 520, 1300, 2048, P16, P16 + 8, 1 << 40, None) == INVALID
+    assert L.int8_gemm_i32(P16, P16, 520, 1300, 2048, P16, P16, 16, None) == WORKSPACE
     args = [P16, 8, 64, 6.0, P16, P16, P16, P16, P16, P16, 1 << 40, None]
     for i in (0, 4, 5, 6, 7, 8, 9):
         bad = list(args)

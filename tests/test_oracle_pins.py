@@ -204,6 +204,22 @@ def test_threshold_boundary_is_inclusive():
     assert sx[2] == np.float32(np.float16(5.99609375)) and Xq[2, 2] == 127
 
 
+def test_nan_and_inf_columns():
+    """r12: a column is an outlier when some entry has |x| >= t; NaN >= t is
+    false, so a NaN alone never makes an outlier and does not hide a large
+    entry beside it; an infinity reaches any finite t."""
+    X = np.full((3, 6), 0.5, dtype=np.float16)
+    X[0, 1] = np.nan                  # NaN alone
+    X[1, 2] = np.nan                  # NaN beside an outlier-sized value
+    X[2, 2] = 9.0
+    X[2, 3] = 9.0                     # a plain outlier column
+    X[1, 4] = -np.inf                 # infinity: an outlier for finite thresholds
+    X[0, 5] = np.float16(-np.nan)     # a negative NaN pattern (sign bit set)
+    np.testing.assert_array_equal(O.outlier_columns(X, 6.0), [2, 3, 4])
+    np.testing.assert_array_equal(O.outlier_columns(X, 60000.0), [4])
+    assert len(O.outlier_columns(X, np.inf)) == 0
+
+
 def test_threshold_disabled_values():
     X = np.full((2, 4), 7.0, dtype=np.float16)
     for t in (0.0, -1.0, INF):

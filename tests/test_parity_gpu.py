@@ -365,38 +365,54 @@ def test_workload_full_sampled(lib, name):
     Xd, Wd = dev(X), dev(W)
     Wq, sw = lib.quantize_weight(Wd)
     ws = lib.new_workspace(w.M, w.K, w.N, Xd.device)
-    Y = lib.linear(Xd, Wq, sw, Wd, w.threshold, workspace=ws)
+    # NaN-filled output: an entry the layer never writes stays NaN
+    Y = torch.full((w.M, w.N), float("nan"), dtype=torch.float16, device=Xd.device)
+    lib.linear(Xd, Wq, sw, Wd, w.threshold, workspace=ws, out=Y)
     torch.cuda.synchronize()
+    assert not torch.isnan(Y).any().item(), f"{name}: output entries left unwritten"
+    assert torch.isfinite(Y).all().item()
     say(f"workload {name}: activation stage, full")
     act = O.quantize_activation(X, w.threshold)
     np.testing.assert_array_equal(act[2], np.sort(cols))
     check_workspace(lib, ws, w.M, w.K, act, name)
 
+    # sampled outputs: one random entry in every 256 x 256 output tile (the
+    # GEMM's tile; whole tiles, split-K tail tiles and ragged edge tiles),
+    # plus random entries and the tile edges and last row / column
     rng = np.random.default_rng(1234)
-    ns = np.unique(np.concatenate([rng.integers(0, w.N, 48), [0, 255, 256, w.N - 1]]))
-    say(f"workload {name}: {len(ns)} weight rows")
-    Wq_r, sw_r = O.quantize_weight_rows(W, ns)
-    np.testing.assert_array_equal(host(Wq[torch.as_tensor(ns, device='cuda:0')]), Wq_r)
-    np.testing.assert_array_equal(host(sw[torch.as_tensor(ns, device='cuda:0')]).view(np.uint32),
-                                  sw_r.view(np.uint32))
-
-    # sampled outputs (inside, on tile edges and on the last row / column)
+    T0, T1 = np.meshgrid(np.arange(0, w.M, 256), np.arange(0, w.N, 256), indexing="ij")
+    t_rows = np.minimum(T0.ravel() + rng.integers(0, 256, T0.size), w.M - 1)
+    t_cols = np.minimum(T1.ravel() + rng.integers(0, 256, T1.size), w.N - 1)
     S = 3000
     edges = [r for r in (0, 255, 256, w.M - 1) if r < w.M]
-    rows = np.concatenate([rng.integers(0, w.M, S), edges])
-    pick = rng.integers(0, len(ns), len(rows))
-    colsel = ns[pick]
-    acc_o, Y64 = O.int8_linear_entries(X, Wq_r[pick], sw_r[pick], W, w.threshold, rows, colsel,
-                                       act=act)
+    r_cols = np.concatenate([rng.integers(0, w.N, 48), [0, 255, 256, w.N - 1]])
+    r_cols = r_cols[r_cols < w.N]
+    ns = np.unique(np.concatenate([r_cols, t_cols]))
+    say(f"workload {name}: {len(ns)} weight rows, {T0.size} output tiles")
+    Wq_r, sw_r = O.quantize_weight_rows(W, ns)
+    nsd = torch.as_tensor(ns, device="cuda:0")
+    np.testing.assert_array_equal(host(Wq[nsd]), Wq_r)
+    np.testing.assert_array_equal(host(sw[nsd]).view(np.uint32), sw_r.view(np.uint32))
+    rr = np.concatenate([rng.integers(0, w.M, S), edges])
+    rows = np.concatenate([rr, t_rows])
+    colsel = np.concatenate([r_cols[rng.integers(0, len(r_cols), len(rr))], t_cols])
+    pick = np.searchsorted(ns, colsel)
+    acc_o = np.empty(len(rows), np.int32)
+    Y64 = np.empty(len(rows))
+    for a in range(0, len(rows), 512):        # bounded host memory at K = 57344
+        b = slice(a, a + 512)
+        acc_o[b], Y64[b] = O.int8_linear_entries(X, Wq_r[pick[b]], sw_r[pick[b]], W,
+                                                 w.threshold, rows[b], colsel[b], act=act)
     ri = torch.as_tensor(rows, device="cuda:0")
     ci = torch.as_tensor(colsel, device="cuda:0")
     assert_y(host(Y[ri, ci]), Y64, what=name)
-    assert torch.isfinite(Y).all().item()
-    # exact int32 accumulators at the same entries via the GEMM stage
+    # exact int32 accumulators at the same entries via the GEMM stage, split
+    # along K as in the layer
     v = lib.workspace_views(ws, w.M, w.K)
-    acc = lib.gemm_i32(v["Xq"].contiguous(), Wq)
+    ws2 = lib.new_workspace(w.M, w.K, w.N, Xd.device)
+    acc = lib.gemm_i32(v["Xq"].contiguous(), Wq, workspace=ws2)
     np.testing.assert_array_equal(host(acc[ri, ci]), acc_o)
-    del acc, Y, Wq, ws, Xd, Wd
+    del acc, Y, Wq, ws, ws2, Xd, Wd
     torch.cuda.empty_cache()
 
 
