@@ -55,6 +55,14 @@ its reason in the design notes of the repository):
       Codes are kept as q - 128 (int8) and the weight stays absmax per
       column, so sum_k (q - zp) w = sum_k (q - 128) w + (128 - zp) S[n] with
       S[n] = sum_k Wq[n][k]; K <= 66304 keeps every such sum inside int32.
+  r13 mixed int8/fp16 training mode ([blog, "Usage"]: has_fp16_weights=True,
+      the default, is for training in mixed Int8/FP16 precision; the pages
+      describe no gradient path).  Reading: the fp16 weight is the trained
+      parameter; every forward call re-quantizes it (its codes follow each
+      update) and runs the layer as above; the backward pass treats the
+      quantization as the identity, so the gradients are those of the exact
+      product X @ W: dX = dY @ W^T, dW = X^T @ dY, dbias = sum over rows of dY,
+      each formed in fp64 here and rounded once to fp16.
   r12 non-finite X (outside the layer's contract, but the outlier set is still
       defined once): a column is an outlier when some entry has |x| >= t; a
       NaN entry never satisfies that (NaN >= t is false), so it neither makes
@@ -93,6 +101,10 @@ __all__ = [
     "quantize_activation_zp",
     "weight_code_sums",
     "int8_linear_zp",
+    "train_forward",
+    "linear_backward_input",
+    "linear_backward_weight",
+    "linear_backward_bias",
 ]
 
 
@@ -406,3 +418,46 @@ def int8_linear_zp_entries(act_zp, Wq_rows, sw_rows, W16, rows, cols, bias=None)
     if bias is not None:
         Y64 = Y64 + np.asarray(bias, dtype=np.float16).astype(np.float64)[cols]
     return acc.astype(np.int64), Y64
+
+
+# ---------------------------------------------------------------------------
+# Mixed int8/fp16 training mode (r13)
+# ---------------------------------------------------------------------------
+def train_forward(X16, W16, threshold, bias=None):
+    """Forward pass of the training mode (r13): the current fp16 weight is
+    quantized afresh ([blog, "Usage"]: the codes are made from the fp16 weight)
+    and the layer runs with that weight's own rows for the outlier product."""
+    Wq, sw = quantize_weight(W16)
+    r = int8_linear(X16, Wq, sw, W16, threshold, bias=bias)
+    r["Wq"], r["sw"] = Wq, sw
+    return r
+
+
+def _to_fp16(Y64):
+    with np.errstate(over="ignore"):
+        return Y64.astype(np.float16)
+
+
+def linear_backward_input(dY16, W16):
+    """dX = dY @ W^T (r13): dY fp16 [M][N], W fp16 [K][N] (math layout).
+
+    Returns (dX64 fp64 [M][K], dX fp16)."""
+    dY = np.asarray(dY16, dtype=np.float16).astype(np.float64)
+    W = np.asarray(W16, dtype=np.float16).astype(np.float64)
+    dX64 = dY @ W.T
+    return dX64, _to_fp16(dX64)
+
+
+def linear_backward_weight(X16, dY16):
+    """dW = X^T @ dY (r13): X fp16 [M][K], dY fp16 [M][N] -> [K][N], the
+    weight's math layout.  Returns (dW64 fp64, dW fp16)."""
+    X = np.asarray(X16, dtype=np.float16).astype(np.float64)
+    dY = np.asarray(dY16, dtype=np.float16).astype(np.float64)
+    dW64 = X.T @ dY
+    return dW64, _to_fp16(dW64)
+
+
+def linear_backward_bias(dY16):
+    """dbias[n] = sum_i dY[i, n] (r13).  Returns (db64 fp64 [N], db fp16)."""
+    db64 = np.asarray(dY16, dtype=np.float16).astype(np.float64).sum(axis=0)
+    return db64, _to_fp16(db64)
