@@ -46,10 +46,14 @@ PEAK_INT8_TOPS = 5000.0
 # steps than the headline.
 DECODE_STEPS, DECODE_WARMUP = 200, 20
 
-# HBM traffic per call of the dominant kernels from rocprofv3 FETCH_SIZE /
-# WRITE_SIZE counter runs, scaled by the copy-kernel calibration factor; valid
-# only for the kernel sources it was measured on (sha256 of the listed files).
-TRAFFIC = {}
+# HBM traffic per call (every kernel of the timed unit) from rocprofv3
+# FETCH_SIZE / WRITE_SIZE counter runs, scaled by the copy-kernel calibration
+# factor (profiles/traffic-mlp_down_prefill_and_decode.md); valid only for the
+# kernel sources it was measured on (sha256 of the listed files).
+TRAFFIC = {
+    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 6731568715, "src": "ac63a428c46c33e7"},
+    ("decode_kernel", "decode"): {"bytes": 68511876, "src": "fb75e3d64f2e27d6"},
+}
 
 
 def kernel_source_hash(files):
