@@ -152,6 +152,27 @@ i8l_status int8_linear_bias(const uint16_t *X, int64_t M, int64_t K,
                             float threshold, uint16_t *Y, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* int8_linear_bias without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The intermediates go to a static scratch
+ * array of I8L_STATIC_SCRATCH_BYTES inside the library, one copy per GPU,
+ * allocated when the library's code is loaded on that GPU and held until the
+ * process ends; the call itself allocates nothing.  Every call on a GPU uses
+ * that GPU's one array, so calls that overlap on one GPU (other streams, other
+ * host threads) race and must be serialized by the caller; the array keeps the
+ * last call's intermediates, and nothing in it needs to start at zero.
+ * Arguments, results and errors as for int8_linear_bias, except: a shape
+ * whose workspace (i8l_linear_workspace_bytes, less the GEMM's split-K partial
+ * tiles if only that makes it fit, in which case every output tile is
+ * computed whole) exceeds I8L_STATIC_SCRATCH_BYTES gives I8L_ERR_WORKSPACE
+ * with nothing enqueued.  Fits, for example: every M <= 64 with K <= 133136,
+ * and M = 2048 with K = 4096. */
+#define I8L_STATIC_SCRATCH_BYTES (32u << 20)
+i8l_status int8_linear_static(const uint16_t *X, int64_t M, int64_t K,
+                              const int8_t *Wq, const float *sw, int64_t N,
+                              const uint16_t *W_outlier_rows, const uint16_t *bias,
+                              float threshold, uint16_t *Y, void *stream);
+
 /* Activation stage on its own ([blog, "A gentle summary of LLM.int8()"],
  * step 1, and the row-wise quantization of [blog, "A closer look at the
  * MatMul"]); the same kernels int8_linear runs for M > 16.

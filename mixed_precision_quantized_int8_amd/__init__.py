@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     Int8LinError,
     MAX_K,
     MAX_K_ZP,
+    STATIC_SCRATCH_BYTES,
     build_info,
     check,
     last_error,
@@ -25,6 +26,7 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "quantize_weight",
     "linear",
+    "linear_static",
     "quantize_activation",
     "gemm_i32",
     "weight_code_sums",
@@ -81,7 +83,7 @@ def new_workspace(M, K, N, device):
     return torch.empty((max(workspace_bytes(M, K, N), 1),), dtype=torch.uint8, device=device)
 
 
-def _linear_args(X, Wq, sw, W, bias, workspace, out):
+def _linear_args(X, Wq, sw, W, bias, workspace, out, need_workspace=True):
     torch = _torch()
     _require(X, torch.float16, "X")
     _require(Wq, torch.int8, "Wq")
@@ -98,7 +100,9 @@ def _linear_args(X, Wq, sw, W, bias, workspace, out):
         _require(bias, torch.float16, "bias")
         if tuple(bias.shape) != (N,):
             raise ValueError(f"bias must be [{N}], got {tuple(bias.shape)}")
-    if workspace is None:
+    if not need_workspace:
+        workspace = None
+    elif workspace is None:
         workspace = new_workspace(M, K, N, X.device)
     else:
         _require(workspace, torch.uint8, "workspace")
@@ -127,6 +131,22 @@ def linear(X, Wq, sw, W=None, threshold=6.0, workspace=None, out=None, bias=None
             W.data_ptr() if W is not None else None,
             bias.data_ptr() if bias is not None else None, float(threshold),
             out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(X)))
+    return out
+
+
+def linear_static(X, Wq, sw, W=None, threshold=6.0, out=None, bias=None):
+    """``linear`` without a workspace: the intermediates go to the library's
+    static scratch array on the current GPU (``STATIC_SCRATCH_BYTES``), so the
+    call allocates nothing when ``out`` is given.  Calls that overlap on one
+    GPU race on that array; shapes whose workspace does not fit it raise."""
+    torch = _torch()
+    M, K, N, _, out = _linear_args(X, Wq, sw, W, bias, None, out, need_workspace=False)
+    with torch.cuda.device(X.device):
+        check(lib().int8_linear_static(
+            X.data_ptr(), M, K, Wq.data_ptr(), sw.data_ptr(), N,
+            W.data_ptr() if W is not None else None,
+            bias.data_ptr() if bias is not None else None, float(threshold),
+            out.data_ptr(), _stream(X)))
     return out
 
 
@@ -249,3 +269,4 @@ def gemm_i32(Xq, Wq, workspace=None):
         check(lib().int8_gemm_i32(Xq.data_ptr(), Wq.data_ptr(), M, N, K, acc.data_ptr(),
                                   ws_ptr, ws_bytes, _stream(Xq)))
     return acc
+

@@ -22,6 +22,7 @@ STATUS_NAMES = {
 }
 MAX_K = 133136
 MAX_K_ZP = 66304
+STATIC_SCRATCH_BYTES = 32 << 20   # I8L_STATIC_SCRATCH_BYTES
 
 # Every symbol include/int8lin.h declares.
 EXPORTS = (
@@ -30,6 +31,7 @@ EXPORTS = (
     "int8_quantize_weight",
     "int8_linear",
     "int8_linear_bias",
+    "int8_linear_static",
     "int8_quantize_activation",
     "int8_gemm_i32",
     "int8_weight_code_sums",
@@ -88,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.int8_linear.restype = ctypes.c_int
     L.int8_linear_bias.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp, f32, vp, vp, sz, vp]
     L.int8_linear_bias.restype = ctypes.c_int
+    L.int8_linear_static.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp, f32, vp, vp]
+    L.int8_linear_static.restype = ctypes.c_int
     L.int8_quantize_activation.argtypes = [vp, i64, i64, f32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.int8_quantize_activation.restype = ctypes.c_int
     L.int8_gemm_i32.argtypes = [vp, vp, i64, i64, i64, vp, vp, sz, vp]

@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 
 #include "../../include/int8lin.h"
@@ -67,8 +68,9 @@ i8l_status check_zp_k(const char* fn, int64_t K) {
 
 // The GEMM's split-K tail (M > 64, the only shapes that reach the GEMM) needs
 // int32 partial tiles, sized for a device with up to kGemmMaxSlices compute
-// units; the counters region before them is reserved.
-i8l_workspace_layout layout_of(int64_t M, int64_t K, int64_t N) {
+// units; the counters region before them is reserved.  split == false lays out
+// no partial tiles (the GEMM then computes every tile whole).
+i8l_workspace_layout layout_of(int64_t M, int64_t K, int64_t N, bool split = true) {
   i8l_workspace_layout L;
   size_t off = 0;
   L.n_outliers = off; off += up(sizeof(int32_t));
@@ -84,7 +86,7 @@ i8l_workspace_layout layout_of(int64_t M, int64_t K, int64_t N) {
       (M >= 1 && M <= i8l::kActSmallRows) ? (size_t)i8l::act_slices((int)K) * (1 + 2 * i8l::kActSmallRows) : 0;
   L.act_partials = off; off += up(act_words * sizeof(uint32_t));
   int slices = 0;
-  if (M > i8l::kStreamMaxM && N > 0) {
+  if (split && M > i8l::kStreamMaxM && N > 0) {
     const i8l::GemmSplit p = i8l::gemm_split_plan((int)M, (int)N, (int)K, i8l::kGemmMaxSlices);
     slices = p.split_tiles * p.S;
   }
@@ -167,13 +169,51 @@ I8L_API i8l_status int8_weight_code_sums(const int8_t* Wq, int64_t N, int64_t K,
                                                      static_cast<hipStream_t>(stream)));
 }
 
+// ---- Static scratch of int8_linear_static ----------------------------------
+// The workspace of callers that cannot allocate device memory: a file-scope
+// device array, one copy per GPU the library runs on, held until the process
+// ends.  Its host-side name is not a device address: host code uses only the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[I8L_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+// Device address of `scratch` per device, looked up on the first call made
+// with that device current (0: not yet).
+std::atomic<uintptr_t> g_scratch_addr[kMaxDevices];
+
+i8l_status scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(I8L_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(I8L_ERR_INVALID_ARG, "%s: device %d outside the %d the library tracks", fn, dev,
+                kMaxDevices);
+  uintptr_t a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (a == 0) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(I8L_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    a = reinterpret_cast<uintptr_t>(p);
+    g_scratch_addr[dev].store(a, std::memory_order_release);   // the same value on every race
+  }
+  *out = reinterpret_cast<void*>(a);
+  return I8L_OK;
+}
+}  // namespace
+
 namespace {
 // zp: zero-point codes for X and the corrected epilogue (wsum required).
+// use_scratch: the workspace is the static scratch array (workspace and
+// workspace_bytes are ignored); shapes whose workspace does not fit it are
+// rejected, after dropping the GEMM's split-K partials if that makes it fit.
 i8l_status linear_impl(const char* fn, const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,
                        const float* sw, const int32_t* wsum, int64_t N,
                        const uint16_t* W_outlier_rows, const uint16_t* bias, float threshold,
                        uint16_t* Y, void* workspace, size_t workspace_bytes, void* stream,
-                       bool zp) {
+                       bool zp, bool use_scratch = false) {
   i8l_status s = check_shape(fn, M, K, N);
   if (s != I8L_OK) return s;
   if (zp && (s = check_zp_k(fn, K)) != I8L_OK) return s;
@@ -185,13 +225,24 @@ i8l_status linear_impl(const char* fn, const uint16_t* X, int64_t M, int64_t K, 
   REQUIRE_PTR(fn, sw, 4);
   if (zp) REQUIRE_PTR(fn, wsum, 4);
   REQUIRE_PTR(fn, Y, 16);
-  REQUIRE_PTR(fn, workspace, 16);
+  if (!use_scratch) REQUIRE_PTR(fn, workspace, 16);
   // NULL W_outlier_rows: the outlier rows are rebuilt from Wq and sw
   if (W_outlier_rows && !aligned(W_outlier_rows, 2))
     return fail(I8L_ERR_INVALID_ARG, "%s: W_outlier_rows must be 2-byte aligned", fn);
   if (bias && !aligned(bias, 2))
     return fail(I8L_ERR_INVALID_ARG, "%s: bias must be 2-byte aligned", fn);
-  const i8l_workspace_layout L = layout_of(M, K, N);
+  i8l_workspace_layout L = layout_of(M, K, N);
+  if (use_scratch) {
+    if (L.total > (size_t)I8L_STATIC_SCRATCH_BYTES) L = layout_of(M, K, N, false);
+    if (L.total > (size_t)I8L_STATIC_SCRATCH_BYTES)
+      return fail(I8L_ERR_WORKSPACE,
+                  "%s: M=%lld K=%lld N=%lld needs %zu bytes of scratch; the static scratch "
+                  "holds %zu (use int8_linear_bias with a workspace)",
+                  fn, (long long)M, (long long)K, (long long)N, L.total,
+                  (size_t)I8L_STATIC_SCRATCH_BYTES);
+    if ((s = scratch_address(fn, &workspace)) != I8L_OK) return s;
+    workspace_bytes = I8L_STATIC_SCRATCH_BYTES;
+  }
   if (workspace_bytes < L.total)
     return fail(I8L_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn,
                 workspace_bytes, L.total);
@@ -229,6 +280,14 @@ I8L_API i8l_status int8_linear_bias(const uint16_t* X, int64_t M, int64_t K, con
                                     void* workspace, size_t workspace_bytes, void* stream) {
   return linear_impl("int8_linear_bias", X, M, K, Wq, sw, nullptr, N, W_outlier_rows, bias,
                      threshold, Y, workspace, workspace_bytes, stream, false);
+}
+
+I8L_API i8l_status int8_linear_static(const uint16_t* X, int64_t M, int64_t K,
+                                      const int8_t* Wq, const float* sw, int64_t N,
+                                      const uint16_t* W_outlier_rows, const uint16_t* bias,
+                                      float threshold, uint16_t* Y, void* stream) {
+  return linear_impl("int8_linear_static", X, M, K, Wq, sw, nullptr, N, W_outlier_rows, bias,
+                     threshold, Y, nullptr, 0, stream, false, true);
 }
 
 I8L_API i8l_status int8_linear_zp(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq,

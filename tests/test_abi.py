@@ -19,6 +19,7 @@ P16 = 0x10000      # fake, 16-byte aligned, never dereferenced: every call below
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"^#.*$", "", src, flags=re.M)        # preprocessor lines
     return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", src)))
 
 
@@ -199,3 +200,25 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_binding, "LIB_PATH", "/nonexistent/libint8lin.so")
     with pytest.raises(RuntimeError, match="missing"):
         _binding.lib()
+
+
+def test_static_entry_point_validates(i8l):
+    """int8_linear_static checks its arguments and the scratch size on the host,
+    before it looks up the scratch array or enqueues anything."""
+    L = i8l.lib()
+    hdr = open(HEADER).read()
+    m = re.search(r"#define I8L_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == i8l.STATIC_SCRATCH_BYTES
+
+    def call(X=P16, M=8, K=64, N=32, Y=P16, t=6.0):
+        return L.int8_linear_static(X, M, K, P16, P16, N, None, None, t, Y, None)
+
+    assert call(X=None) == INVALID and "X is NULL" in i8l.last_error()
+    assert call(Y=None) == INVALID
+    assert call(K=24) == INVALID
+    assert call(t=math.nan) == INVALID
+    assert call(M=0) == OK and call(N=0) == OK
+    # 3 * 4096 * 4096 bytes of codes and outlier values: beyond the scratch
+    assert call(M=4096, K=4096, N=256) == WORKSPACE
+    assert "static scratch" in i8l.last_error()
+    assert call(M=64, K=200000) == K_TOO_LARGE
