@@ -16,6 +16,11 @@ outlier columns, bound by the int8 matrix cores.  The same line carries, under
 columns (bound by HBM), timed the same way in the same process
 (--no-decode skips it).
 
+Under "train" it also carries one step of the mixed int8/fp16 training mode
+on the headline layer (re-quantize the fp16 weight, the forward, the
+gradients dX, dW and dbias), whose fp16 GEMMs are priced against the fp16
+matrix-core peak (--no-train skips it).
+
 The K timed steps are captured into one HIP graph and replayed (--no-graph
 launches each step from Python instead).  To keep the 256 MB Infinity Cache
 from serving the weight, steps rotate over several copies of (X, Wq, sw, W, Y,
@@ -79,6 +84,16 @@ def dominant_kernel(w):
     return "gemm_i8_kernel", "mfma", ["gemm.hip", "act.hip", "common.h"]
 
 
+def blas_threads():
+    """Threads the host BLAS (which carries the oracle's matrix products) uses."""
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        return max((i.get("num_threads") or 0) for i in info) if info else None
+    except Exception:
+        return None
+
+
 def cpu_baseline(w, X, W, budget_s=12.0):
     """Time the CPU oracle (as it stands) on a bounded sample of the workload.
 
@@ -89,13 +104,7 @@ def cpu_baseline(w, X, W, budget_s=12.0):
     import numpy as np
     from oracle import int8_oracle as O
 
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        info = threadpool_info()
-        threads = max((i.get("num_threads") or 0) for i in info) if info else None
-    except Exception:
-        pass
+    threads = blas_threads()
     whole = w.M * w.N * w.K <= 2**31
     rows = w.M if whole else min(w.M, 64)
     cols = w.N if whole else min(w.N, 2048)
@@ -325,6 +334,134 @@ def measure(torch, pkg, workloads, w, args, steps, warmup, with_fp16_context):
     return res, X, W, Y0, Wq0
 
 
+def graph_ms(torch, fn, K):
+    """Per-call time of `fn` captured K times into one HIP graph and replayed
+    (events around the replay, after an untimed replay)."""
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_cap):
+        fn()
+    torch.cuda.current_stream().wait_stream(s_cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(K):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    del g
+    return t0.elapsed_time(t1) / K
+
+
+PEAK_FP16_TFLOPS = 2500.0
+
+
+def measure_train(torch, pkg, w, X, W, steps, warmup, with_cpu):
+    """One step of the mixed int8/fp16 training mode on the workload's layer,
+    the fp16 weight being the trained parameter: re-quantize it, the int8
+    forward with its fp16 rows for the outlier columns and a bias, then the
+    gradients dX = dY W^T, dW = X^T dY and dbias.  Each part is also timed on
+    its own (one graph per part)."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(1000 + w.seed)
+    dY = rng.standard_normal((w.M, w.N), dtype=np.float32).astype(np.float16)
+    bias = (rng.standard_normal(w.N) * 0.1).astype(np.float16)
+    Xd, Wd = torch.from_numpy(X).to(dev), torch.from_numpy(W).to(dev)
+    dYd, bd = torch.from_numpy(dY).to(dev), torch.from_numpy(bias).to(dev)
+    Wq = torch.empty((w.N, w.K), dtype=torch.int8, device=dev)
+    sw = torch.empty((w.N,), dtype=torch.float32, device=dev)
+    Y = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    dX = torch.empty((w.M, w.K), dtype=torch.float16, device=dev)
+    ws = pkg.new_workspace(w.M, w.K, w.N, dev)
+    nbw = int(pkg.lib().i8l_backward_weight_workspace_bytes(w.M, w.K, w.N))
+    wsb = torch.empty((nbw,), dtype=torch.uint8, device=dev)
+
+    def forward():
+        pkg.quantize_weight(Wd, Wq, sw)
+        pkg.linear(Xd, Wq, sw, Wd, w.threshold, workspace=ws, out=Y, bias=bd)
+
+    def back_in():
+        pkg.backward_input(dYd, Wd, out=dX)
+
+    def back_w():
+        return pkg.backward_weight(Xd, dYd, with_bias=True, workspace=wsb)
+
+    def step():
+        forward()
+        back_in()
+        back_w()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = {"step": graph_ms(torch, step, steps), "forward": graph_ms(torch, forward, steps),
+          "backward_input": graph_ms(torch, back_in, steps),
+          "backward_weight": graph_ms(torch, back_w, steps)}
+    mnk2 = 2.0 * w.M * w.N * w.K
+    back_ms = ms["backward_input"] + ms["backward_weight"]
+    achieved = 2 * mnk2 / (back_ms * 1e-3) / 1e12
+    res = {
+        "value": round(3 * mnk2 / (ms["step"] * 1e-3) / 1e12, 3),
+        "unit": "TOPS (2MNK int8 forward + 4MNK fp16 backward per step)",
+        "ms_per_step": round(ms["step"], 5),
+        "steps": steps,
+        "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "bias": True,
+                   "weight": "fp16 parameter, re-quantized every step",
+                   "step": "quantize_weight, linear, backward_input, backward_weight (+bias)"},
+        "parts_ms": {k: round(v, 5) for k, v in ms.items() if k != "step"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                     "traffic": None, "kernel": "gemm_i8_kernel (fp16 instantiation)",
+                     "timed": "backward_input + backward_weight: the two fp16 GEMMs, the "
+                              "two transposes and the bias sum",
+                     "backward_input_frac": round(mnk2 / (ms["backward_input"] * 1e-3) / 1e12
+                                                  / PEAK_FP16_TFLOPS, 4),
+                     "backward_weight_frac": round(mnk2 / (ms["backward_weight"] * 1e-3) / 1e12
+                                                   / PEAK_FP16_TFLOPS, 4)},
+    }
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline_train(w, X, W, dY, bias)
+    del Xd, Wd, dYd, Wq, Y, dX, ws, wsb
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_train(w, X, W, dY, bias, budget_s=10.0):
+    """The oracle's training step (forward with fresh codes, the three
+    gradients) on a bounded sample: the first 64 rows and the first 2048
+    output features of the layer; the rate is scaled by the op share."""
+    from oracle import int8_oracle as O
+    import numpy as np
+
+    rows, cols = min(w.M, 64), min(w.N, 2048)
+    Xs = X[:rows]
+    Ws = np.ascontiguousarray(W[:, :cols])
+    dYs = np.ascontiguousarray(dY[:rows, :cols])
+    reps, t_total = 0, 0.0
+    t0 = time.perf_counter()
+    while reps < 100 and (time.perf_counter() - t0) < budget_s:
+        s = time.perf_counter()
+        O.train_forward(Xs, Ws, w.threshold, bias=bias[:cols])
+        O.linear_backward_input(dYs, Ws)
+        O.linear_backward_weight(Xs, dYs)
+        O.linear_backward_bias(dYs)
+        t_total += time.perf_counter() - s
+        reps += 1
+    per = t_total / reps
+    return {"value": round(3 * 2.0 * rows * cols * w.K / per / 1e12, 6), "unit": "TOPS",
+            "cores": blas_threads() or os.cpu_count(), "kind": "oracle",
+            "sample": f"first {rows} rows x first {cols} output features of the {w.name} "
+                      f"layer ({rows}x{w.K}x{cols}), {reps} steps, {per * 1e3:.1f} ms/step"}
+
+
 def parity_of(w, y_dev, wq_dev, ref, Wq_o, rows, cols):
     """The benchmark's own output against the oracle on the sampled block."""
     import numpy as np
@@ -345,6 +482,8 @@ def main():
     ap.add_argument("--workload", default="mlp_down_prefill")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the secondary decode measurement")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the training-mode step (fp16 weight, backward pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: auto, >512 MB)")
     ap.add_argument("--rebuilt-rows", action="store_true",
@@ -412,8 +551,12 @@ def main():
         cb, ref, Wq_o, rows, cols = cpu_baseline(w, X, W)
         result["cpu_baseline"] = cb
         result["parity"] = parity_of(w, Y0, Wq0, ref, Wq_o, rows, cols)
-    del X, W, Y0, Wq0
+    del Y0, Wq0
     torch.cuda.empty_cache()
+    if not args.no_train and default_layer:
+        result["train"] = measure_train(torch, pkg, w, X, W, args.steps, args.warmup,
+                                        not args.no_cpu_baseline)
+    del X, W
 
     if not args.no_decode and w.name != "decode":
         wd = workloads.WORKLOADS["decode"]

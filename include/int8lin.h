@@ -256,6 +256,41 @@ i8l_status int8_quantize_activation_zp(const uint16_t *X, int64_t M, int64_t K, 
                                        uint16_t *X_outliers, void *workspace,
                                        size_t workspace_bytes, void *stream);
 
+/* ---- Mixed int8/fp16 training mode -----------------------------------------
+ * [blog, "Usage"]: has_fp16_weights=True (the default) keeps the fp16 weight
+ * for training in mixed int8/fp16 precision.  The pages describe no gradient
+ * path; the one provided here treats the quantization as the identity: the
+ * forward pass is int8_quantize_weight on the current fp16 weight followed by
+ * int8_linear_bias with that weight as W_outlier_rows, and the gradients are
+ * those of Y = X . W + bias, formed from fp16 operands with fp32 accumulation
+ * and rounded once to fp16 (round to nearest even, overflow to +/-inf).
+ * Shapes: M >= 0, K as for int8_linear, N >= 0 with N % 8 == 0. */
+
+/* Workspace bytes int8_linear_backward_weight needs (0 on a bad shape):
+ * X^T and dY^T with their rows padded to a multiple of 8, and the bias
+ * gradient's partial sums. */
+size_t i8l_backward_weight_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/* dX = dY . W^T.
+ *   dY  fp16 [M][N]  gradient of the layer's output, 16-byte aligned
+ *   W   fp16 [K][N]  the fp16 weight in math layout, 16-byte aligned
+ *   dX  fp16 [M][K]  out, 16-byte aligned
+ * M == 0: no-op.  N == 0: dX = 0 (dY and W may then be NULL). */
+i8l_status int8_linear_backward_input(const uint16_t *dY, const uint16_t *W, int64_t M,
+                                      int64_t K, int64_t N, uint16_t *dX, void *stream);
+
+/* dW = X^T . dY and dbias[n] = sum_i dY[i][n].
+ *   X       fp16 [M][K]  the layer's input, 16-byte aligned
+ *   dY      fp16 [M][N]  16-byte aligned
+ *   dW      fp16 [K][N]  out (the weight's math layout), 16-byte aligned
+ *   dbias   fp16 [N]     out, 4-byte aligned, or NULL (not computed)
+ *   workspace  at least i8l_backward_weight_workspace_bytes(M, K, N) bytes,
+ *              16-byte aligned (may be NULL when M == 0)
+ * M == 0: dW = 0 and dbias = 0.  N == 0: no-op. */
+i8l_status int8_linear_backward_weight(const uint16_t *X, const uint16_t *dY, int64_t M,
+                                       int64_t K, int64_t N, uint16_t *dW, uint16_t *dbias,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *i8l_last_error(void);
 

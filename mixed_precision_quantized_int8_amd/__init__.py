@@ -32,6 +32,8 @@ __all__ = [
     "weight_code_sums",
     "linear_zp",
     "quantize_activation_zp",
+    "backward_input",
+    "backward_weight",
     "workspace_layout",
     "workspace_bytes",
     "workspace_views",
@@ -270,3 +272,47 @@ def gemm_i32(Xq, Wq, workspace=None):
                                   ws_ptr, ws_bytes, _stream(Xq)))
     return acc
 
+
+def backward_input(dY, W, out=None):
+    """Training mode: dX = dY . W^T; dY fp16 [M][N], W fp16 [K][N] -> fp16 [M][K]."""
+    torch = _torch()
+    _require(dY, torch.float16, "dY")
+    _require(W, torch.float16, "W")
+    M, N = dY.shape
+    K = W.shape[0]
+    if W.shape[1] != N:
+        raise ValueError(f"W must be [K][{N}], got {tuple(W.shape)}")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float16, device=dY.device)
+    else:
+        _require(out, torch.float16, "out")
+        if tuple(out.shape) != (M, K):
+            raise ValueError(f"out must be [{M}][{K}], got {tuple(out.shape)}")
+    with torch.cuda.device(dY.device):
+        check(lib().int8_linear_backward_input(dY.data_ptr(), W.data_ptr(), M, K, N,
+                                               out.data_ptr(), _stream(dY)))
+    return out
+
+
+def backward_weight(X, dY, with_bias=False, workspace=None):
+    """Training mode: (dW = X^T . dY fp16 [K][N], dbias fp16 [N] or None)."""
+    torch = _torch()
+    _require(X, torch.float16, "X")
+    _require(dY, torch.float16, "dY")
+    M, K = X.shape
+    if dY.shape[0] != M:
+        raise ValueError(f"dY must have {M} rows, got {tuple(dY.shape)}")
+    N = dY.shape[1]
+    dW = torch.empty((K, N), dtype=torch.float16, device=X.device)
+    db = torch.empty((N,), dtype=torch.float16, device=X.device) if with_bias else None
+    if workspace is None:
+        nbytes = int(lib().i8l_backward_weight_workspace_bytes(M, K, N))
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=X.device)
+    else:
+        _require(workspace, torch.uint8, "workspace")
+    with torch.cuda.device(X.device):
+        check(lib().int8_linear_backward_weight(
+            X.data_ptr(), dY.data_ptr(), M, K, N, dW.data_ptr(),
+            db.data_ptr() if db is not None else None, workspace.data_ptr(), workspace.numel(),
+            _stream(X)))
+    return dW, db

@@ -37,6 +37,9 @@ EXPORTS = (
     "int8_weight_code_sums",
     "int8_linear_zp",
     "int8_quantize_activation_zp",
+    "i8l_backward_weight_workspace_bytes",
+    "int8_linear_backward_input",
+    "int8_linear_backward_weight",
     "i8l_last_error",
     "i8l_build_info",
 )
@@ -103,6 +106,12 @@ def lib() -> ctypes.CDLL:
     L.int8_quantize_activation_zp.argtypes = [vp, i64, i64, f32, vp, vp, vp, vp, vp, vp, vp, sz,
                                               vp]
     L.int8_quantize_activation_zp.restype = ctypes.c_int
+    L.i8l_backward_weight_workspace_bytes.argtypes = [i64, i64, i64]
+    L.i8l_backward_weight_workspace_bytes.restype = sz
+    L.int8_linear_backward_input.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+    L.int8_linear_backward_input.restype = ctypes.c_int
+    L.int8_linear_backward_weight.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
+    L.int8_linear_backward_weight.restype = ctypes.c_int
     L.i8l_last_error.argtypes = []
     L.i8l_last_error.restype = ctypes.c_char_p
     L.i8l_build_info.argtypes = []

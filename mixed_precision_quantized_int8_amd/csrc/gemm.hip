@@ -55,6 +55,7 @@
 // zero-point limit, and are dequantized by sx * sw / 127.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -123,8 +124,13 @@ __device__ __forceinline__ int d_row(int r, int lane) {
 // visible to it without a fence per workgroup (a device-wide release writes
 // the XCD's L2 back: ~60 us per split workgroup, measured).  Separate
 // instantiations, so that the whole-tile kernel carries none of this.  ZP:
-// zero-point epilogue.
-template <bool OUT_I32, bool SPLIT, bool ZP, bool FIX = false>
+// zero-point epilogue.  F16: the operands are fp16 instead of int8 (a.K is
+// then the row length in BYTES, twice the element count); the same panels,
+// ring and fragments feed v_mfma_f32_32x32x16_f16, whose operand layout per
+// lane (16 bytes of one row, the two half-waves on consecutive 16-byte
+// chunks) is that of the int8 instruction, into fp32 accumulators, stored as
+// fp16 (round to nearest even) to a.Y.
+template <bool OUT_I32, bool SPLIT, bool ZP, bool FIX = false, bool F16 = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) int8_t smem[kSlots * kSlot];
 
@@ -202,11 +208,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     }
   };
 
-  v16i acc[4][2];
+  typedef typename std::conditional<F16, v16f, v16i>::type acc_t;
+  acc_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v16i{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = acc_t{};
   if constexpr (ZP && !SPLIT) {
     // Zero-point correction as the accumulators' starting value: the MFMAs then
     // add sum_k (q - 128) w on top.  Every prefix sum stays within
@@ -230,7 +237,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   }
   auto mfma_one = [&](const v4i (&fa)[4], const v4i (&fb)[2], int q) {
     const int i = q & 3, j = q >> 2;
-    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    if constexpr (F16)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fa[i]),
+                                                        __builtin_bit_cast(v8h, fb[j]), acc[i][j],
+                                                        0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
   // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
   constexpr int kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100;
@@ -332,6 +344,48 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   wait_lgkmcnt0();
   }   // !FIX
   __syncthreads();   // all waves done with the ring before the epilogue reuses it
+
+  if constexpr (F16) {
+    // fp16 output, one 32x32 block at a time: through 2.5 KB of LDS per wave
+    // in row order and out as 16-byte row pieces when N % 8 == 0, else
+    // element by element
+    constexpr int kTS = 40;
+    uint16_t* sT = reinterpret_cast<uint16_t*>(&smem[0]) + wave * 32 * kTS;
+    const bool vec_store = (N & 7) == 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn + j * 32 + l32;
+        if (vec_store) {   // uniform
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sT[d_row(r, lane) * kTS + l32] = f2h(acc[i][j][r]);
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int row = lane >> 1, c0 = (lane & 1) * 16;
+          const v4i p0 = *reinterpret_cast<const v4i*>(&sT[row * kTS + c0]);
+          const v4i p1 = *reinterpret_cast<const v4i*>(&sT[row * kTS + c0 + 8]);
+          const int m = m0 + wm + i * 32 + row;
+          const int nb = n0 + wn + j * 32 + c0;
+          if (m < M) {
+            if (nb < N) *reinterpret_cast<v4i*>(&a.Y[(size_t)m * N + nb]) = p0;
+            if (nb + 8 < N) *reinterpret_cast<v4i*>(&a.Y[(size_t)m * N + nb + 8]) = p1;
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        } else if (n < N) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm + i * 32 + d_row(r, lane);
+            if (m < M) a.Y[(size_t)m * N + n] = f2h(acc[i][j][r]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    return;
+  }
 
   if constexpr (SPLIT && !FIX) {
     // Split tile: store this K range's int32 partial and end; the fix-up
@@ -690,6 +744,23 @@ hipError_t launch_gemm(const GemmArgs& in, hipStream_t stream) {
                          dim3(kGemmThreads), 0, stream, a);
     }
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f16(const uint16_t* A, const uint16_t* B, int M, int N, int K,
+                           uint16_t* C, hipStream_t stream) {
+  GemmArgs a{};
+  a.Xq = reinterpret_cast<const int8_t*>(A);
+  a.Wq = reinterpret_cast<const int8_t*>(B);
+  a.M = M;
+  a.N = N;
+  a.K = 2 * K;   // bytes per row
+  a.Y = C;
+  const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  a.full_tiles = tiles;
+  a.split_S = 1;
+  hipLaunchKernelGGL((gemm_i8_kernel<false, false, false, false, true>), dim3(tiles),
+                     dim3(kGemmThreads), 0, stream, a);
   return hipGetLastError();
 }
 

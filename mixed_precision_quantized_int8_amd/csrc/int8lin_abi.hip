@@ -396,6 +396,73 @@ I8L_API i8l_status int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, 
   return hip_status(fn, i8l::launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 
+// ---- Training mode: backward pass ------------------------------------------------
+
+namespace {
+// Shape rules of the backward entry points: the layer's rules for M, K, plus
+// N % 8 == 0 (the products run along N and along rows padded to 8, in whole
+// 16-byte chunks).
+i8l_status check_backward_shape(const char* fn, int64_t M, int64_t K, int64_t N) {
+  i8l_status s = check_shape(fn, M, K, N);
+  if (s != I8L_OK) return s;
+  if (N % 8 != 0)
+    return fail(I8L_ERR_INVALID_ARG, "%s: N=%lld must be a multiple of 8", fn, (long long)N);
+  if ((uint64_t)K * (uint64_t)N > (1ull << 40) || (uint64_t)M + 8 > (uint64_t)INT32_MAX)
+    return fail(I8L_ERR_INVALID_ARG, "%s: tensor sizes exceed the supported range", fn);
+  return I8L_OK;
+}
+}  // namespace
+
+I8L_API size_t i8l_backward_weight_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  if (check_backward_shape("i8l_backward_weight_workspace_bytes", M, K, N) != I8L_OK) return 0;
+  size_t a, b, c;
+  return i8l::backward_weight_workspace((int)M, (int)K, (int)N, &a, &b, &c);
+}
+
+I8L_API i8l_status int8_linear_backward_input(const uint16_t* dY, const uint16_t* W, int64_t M,
+                                              int64_t K, int64_t N, uint16_t* dX,
+                                              void* stream) {
+  const char* fn = "int8_linear_backward_input";
+  i8l_status s = check_backward_shape(fn, M, K, N);
+  if (s != I8L_OK) return s;
+  if (M == 0) return ok();
+  REQUIRE_PTR(fn, dX, 16);
+  (void)hipGetLastError();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (N == 0)   // empty sums: dX = 0 (K % 16 == 0: whole words)
+    return hip_status(fn, i8l::launch_fill_u32(reinterpret_cast<uint32_t*>(dX),
+                                               (int)((uint64_t)M * K / 2), 0u, st));
+  REQUIRE_PTR(fn, dY, 16);
+  REQUIRE_PTR(fn, W, 16);
+  return hip_status(fn, i8l::launch_backward_input(dY, W, (int)M, (int)K, (int)N, dX, st));
+}
+
+I8L_API i8l_status int8_linear_backward_weight(const uint16_t* X, const uint16_t* dY, int64_t M,
+                                               int64_t K, int64_t N, uint16_t* dW,
+                                               uint16_t* dbias, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
+  const char* fn = "int8_linear_backward_weight";
+  i8l_status s = check_backward_shape(fn, M, K, N);
+  if (s != I8L_OK) return s;
+  if (N == 0) return ok();
+  REQUIRE_PTR(fn, dW, 16);
+  if (dbias && !aligned(dbias, 4))
+    return fail(I8L_ERR_INVALID_ARG, "%s: dbias must be 4-byte aligned", fn);
+  if (M > 0) {
+    REQUIRE_PTR(fn, X, 16);
+    REQUIRE_PTR(fn, dY, 16);
+    REQUIRE_PTR(fn, workspace, 16);
+    size_t a, b, c;
+    const size_t need = i8l::backward_weight_workspace((int)M, (int)K, (int)N, &a, &b, &c);
+    if (workspace_bytes < need)
+      return fail(I8L_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu required", fn,
+                  workspace_bytes, need);
+  }
+  (void)hipGetLastError();
+  return hip_status(fn, i8l::launch_backward_weight(X, dY, (int)M, (int)K, (int)N, dW, dbias,
+                                                    workspace, static_cast<hipStream_t>(stream)));
+}
+
 I8L_API const char* i8l_last_error(void) { return g_err; }
 
 I8L_API const char* i8l_build_info(void) {

@@ -107,6 +107,25 @@ hipError_t launch_decode_zp(const uint16_t* X, int M, int K, const int8_t* Wq, c
                             const uint16_t* bias, float threshold, bool enabled, uint16_t* Y,
                             const Workspace& ws, hipStream_t stream);
 
+// C [M][N] = A [M][K] . B [N][K]^T, fp16 operands (K-contiguous, K % 8 == 0,
+// 16-byte aligned rows), fp32 accumulation, fp16 result (round to nearest
+// even); the int8 GEMM's tiles and pipeline on the fp16 matrix cores.
+hipError_t launch_gemm_f16(const uint16_t* A, const uint16_t* B, int M, int N, int K,
+                           uint16_t* C, hipStream_t stream);
+
+// Training-mode backward (train.hip).  N % 8 == 0; 16-byte aligned operands.
+// dX [M][K] = dY [M][N] . W^T  (W [K][N]).
+hipError_t launch_backward_input(const uint16_t* dY, const uint16_t* W, int M, int K, int N,
+                                 uint16_t* dX, hipStream_t stream);
+// dW [K][N] = X^T . dY, dbias [N] = column sums of dY (optional); the
+// workspace holds X^T, dY^T (rows padded to a multiple of 8) and the bias
+// partial sums, laid out by backward_weight_workspace.
+size_t backward_weight_workspace(int M, int K, int N, size_t* off_xt, size_t* off_dyt,
+                                 size_t* off_part);
+hipError_t launch_backward_weight(const uint16_t* X, const uint16_t* dY, int M, int K, int N,
+                                  uint16_t* dW, uint16_t* dbias, void* workspace,
+                                  hipStream_t stream);
+
 const char* gemm_tile_info();
 
 }  // namespace i8l

@@ -105,6 +105,7 @@ __all__ = [
     "linear_backward_input",
     "linear_backward_weight",
     "linear_backward_bias",
+    "linear_backward_entries",
 ]
 
 
@@ -461,3 +462,23 @@ def linear_backward_bias(dY16):
     """dbias[n] = sum_i dY[i, n] (r13).  Returns (db64 fp64 [N], db fp16)."""
     db64 = np.asarray(dY16, dtype=np.float16).astype(np.float64).sum(axis=0)
     return db64, _to_fp16(db64)
+
+
+def linear_backward_entries(A16, B16, rows, cols, transpose_a=False):
+    """Entries (rows[j], cols[j]) of the two gradient products (r13), each one
+    dot product in fp64, with the matching dot product of magnitudes:
+      transpose_a False: dX[i, k] = sum_n dY[i, n] W[k, n]    (A = dY, B = W)
+      transpose_a True:  dW[k, n] = sum_i X[i, k] dY[i, n]     (A = X,  B = dY)
+    Returns (values fp64, magnitudes fp64)."""
+    A = np.asarray(A16, dtype=np.float16)
+    B = np.asarray(B16, dtype=np.float16)
+    vals = np.empty(len(rows))
+    mags = np.empty(len(rows))
+    for j, (r, c) in enumerate(zip(rows, cols)):
+        if transpose_a:
+            a, b = A[:, r].astype(np.float64), B[:, c].astype(np.float64)
+        else:
+            a, b = A[r].astype(np.float64), B[c].astype(np.float64)
+        vals[j] = a @ b
+        mags[j] = np.abs(a) @ np.abs(b)
+    return vals, mags

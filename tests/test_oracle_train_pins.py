@@ -108,3 +108,20 @@ def test_train_forward_requantizes_the_current_weight():
     assert not np.array_equal(Wq1, Wq0)
     # the outlier column's product uses the new fp16 rows
     np.testing.assert_array_equal(r1["Y64"], O.int8_linear(X, Wq1, sw1, W1, 6.0)["Y64"])
+
+
+def test_backward_entries_match_full():
+    rng = np.random.default_rng(21)
+    M, K, N = 9, 24, 16
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    W = rng.standard_normal((K, N)).astype(np.float16)
+    dY = rng.standard_normal((M, N)).astype(np.float16)
+    r, c = rng.integers(0, M, 30), rng.integers(0, K, 30)
+    v, mag = O.linear_backward_entries(dY, W, r, c)
+    np.testing.assert_allclose(v, O.linear_backward_input(dY, W)[0][r, c], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(mag, (np.abs(dY.astype(np.float64)) @
+                                     np.abs(W.astype(np.float64)).T)[r, c], rtol=1e-13)
+    r, c = rng.integers(0, K, 30), rng.integers(0, N, 30)
+    v, _ = O.linear_backward_entries(X, dY, r, c, transpose_a=True)
+    np.testing.assert_allclose(v, O.linear_backward_weight(X, dY)[0][r, c], rtol=1e-13,
+                               atol=1e-13)
