@@ -284,6 +284,32 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     }
   }
   const int found = wcount < kDecOutPre ? wcount : kDecOutPre;
+  // More than kDecOutPre outlier columns in the chunk (rare): their columns are
+  // found by rank from the per-step masks, kept in scalar registers, and their
+  // values are read kDecOutBatch columns per memory round trip.
+  constexpr int kDecOutBatch = 8;
+  uint64_t msk[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) msk[t] = 0;
+  if (wcount > kDecOutPre) {
+#pragma unroll
+    for (int t = 0; t < KS; ++t) msk[t] = step_mask(t);
+  }
+  // column of the r-th outlier of this chunk, ascending (uniform), -1 past the last
+  auto nth_outlier = [&](int r) -> int {
+    int k = -1;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const int cnt = __popcll(msk[t]);
+      if (k < 0 && r >= 0 && r < cnt) {
+        uint64_t m = msk[t];
+        for (int i = 0; i < r; ++i) m &= m - 1;
+        k = (s0 + t) * 64 + __builtin_ctzll(m);
+      }
+      r -= cnt;
+    }
+    return k;
+  };
   // X values (lane = row) and weight-row values (lane = feature) of the first
   // kDecOutPre outlier columns, loaded now and used after the product
   // Without an fp16 weight (W_rows NULL) the value is rebuilt from the code
@@ -416,24 +442,29 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
           if (m < M) yo[m] += h2f((uint16_t)__builtin_amdgcn_readlane((int)xo[j], m)) * wv;
       }
     }
-    if (wcount > kDecOutPre) {   // the rest, straight from memory
-      int j = 0;
-      for (int s = 0; s < KS; ++s) {
-        uint64_t w = step_mask(s);
-        while (w) {
-          const int k = (s0 + s) * 64 + __builtin_ctzll(w);
-          w &= w - 1;
-          if (j++ < kDecOutPre) continue;
-          float wv = 0.0f;
-          if (n0 + lane < N)
-            wv = rebuild ? h2f(dequant_w16(d.Wq[(size_t)(n0 + lane) * K + k], swl))
-                         : h2f(d.W_rows[(size_t)k * N + n0 + lane]);
-          const int xv = lane < M ? (int)d.X[(size_t)lane * K + k] : 0;
+    // the rest, straight from memory: all loads of a batch go out before any
+    // of their values is used
+    for (int j0 = kDecOutPre; j0 < wcount; j0 += kDecOutBatch) {   // uniform
+      int kk[kDecOutBatch], xv[kDecOutBatch];
+      float wv[kDecOutBatch];
 #pragma unroll
-          for (int m = 0; m < 16; ++m)
-            if (m < M) yo[m] += h2f((uint16_t)__builtin_amdgcn_readlane(xv, m)) * wv;
+      for (int u = 0; u < kDecOutBatch; ++u) kk[u] = nth_outlier(j0 + u);
+#pragma unroll
+      for (int u = 0; u < kDecOutBatch; ++u) {
+        wv[u] = 0.0f;
+        xv[u] = 0;
+        if (kk[u] >= 0) {   // uniform
+          if (n0 + lane < N)
+            wv[u] = rebuild ? h2f(dequant_w16(d.Wq[(size_t)(n0 + lane) * K + kk[u]], swl))
+                            : h2f(d.W_rows[(size_t)kk[u] * N + n0 + lane]);
+          if (lane < M) xv[u] = (int)d.X[(size_t)lane * K + kk[u]];
         }
       }
+#pragma unroll
+      for (int u = 0; u < kDecOutBatch; ++u)
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+          if (m < M) yo[m] += h2f((uint16_t)__builtin_amdgcn_readlane(xv[u], m)) * wv[u];
     }
 #pragma unroll
     for (int m = 0; m < 16; ++m) sYo[wave][m][lane] = yo[m];
@@ -461,18 +492,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
         if (lane < M) d.X_O[(size_t)lane * K + rank + j] = xo[j];
       }
     }
-    if (wcount > kDecOutPre) {
-      int j = 0;
-      for (int s = 0; s < KS; ++s) {
-        uint64_t w = step_mask(s);
-        while (w) {
-          const int k = (s0 + s) * 64 + __builtin_ctzll(w);
-          w &= w - 1;
-          if (j >= kDecOutPre) {
-            if (lane == 0) d.idx[rank + j] = k;
-            if (lane < M) d.X_O[(size_t)lane * K + rank + j] = d.X[(size_t)lane * K + k];
-          }
-          ++j;
+    for (int j0 = kDecOutPre; j0 < wcount; j0 += kDecOutBatch) {   // uniform, batched as above
+      int kk[kDecOutBatch];
+      uint16_t xv[kDecOutBatch];
+#pragma unroll
+      for (int u = 0; u < kDecOutBatch; ++u) {
+        kk[u] = nth_outlier(j0 + u);
+        xv[u] = kk[u] >= 0 && lane < M ? d.X[(size_t)lane * K + kk[u]] : (uint16_t)0;
+      }
+#pragma unroll
+      for (int u = 0; u < kDecOutBatch; ++u) {
+        if (kk[u] >= 0) {
+          if (lane == 0) d.idx[rank + j0 + u] = kk[u];
+          if (lane < M) d.X_O[(size_t)lane * K + rank + j0 + u] = xv[u];
         }
       }
     }

@@ -6,116 +6,162 @@
 // weight keeps nn.Linear's [out][in] layout, here Wq[N][K] (K contiguous),
 // which is also the layout the int8 matrix cores read.
 //
-// One workgroup owns a strip of 64 output features over all of K:
-//   pass 1 reads the strip and reduces |W| down K (sw),
-//   pass 2 re-reads it in 64x64 tiles, transposes through LDS and writes
-//   16-byte runs of codes along K.
-// The strip is re-read from L2/MALL, not HBM, on the second pass for the
-// weight sizes used here.  Runs once per layer, off the timed path.
+// Two launches after clearing sw (a fill kernel, safe under graph capture):
+//   wabsmax  the column maxima: each workgroup reduces |W| over a chunk of
+//            1024 rows of a strip of 512 output features (16-byte loads,
+//            whole 128-byte lines per 8 lanes) and merges its maxima into sw
+//            with an integer atomicMax on the fp32 bits (the order of
+//            non-negative floats is that of their bit patterns);
+//   wcode    the codes: each workgroup takes a tile of 128 rows (k) x 64
+//            output features, reads it once (128-byte row pieces), holds it
+//            in LDS and writes Wq[n][k0 .. k0+128) as whole 128-byte runs.
+// The weight is read twice (every code needs its column's absmax over all K)
+// and the codes written once: 2.5 bytes of traffic per weight element.
 #include "common.h"
 #include "launch.h"
 
 namespace i8l {
 
-constexpr int kWqStrip = 64;   // output features per workgroup
-constexpr int kWqTileK = 64;   // K rows per transpose tile
-constexpr int kWqThreads = 256;
+constexpr int kWaStrip = 512;    // wabsmax: output features per workgroup (8 per lane)
+constexpr int kWaRows = 1024;    // wabsmax: rows per workgroup
+constexpr int kWaThreads = 256;
+constexpr int kWcK = 128;        // wcode: rows (k) per tile
+constexpr int kWcN = 64;         // wcode: output features per tile
+constexpr int kWcThreads = 256;
 
+// grid = (ceil(N / 512), ceil(K / 1024)); sw cleared beforehand.
+// VEC: N % 8 == 0 and W 16-byte aligned (whole 16-byte pieces per lane).
 template <bool VEC>
-__global__ __launch_bounds__(kWqThreads) void wquant_kernel(const uint16_t* __restrict__ W, int K,
-                                                           int N, int8_t* __restrict__ Wq,
-                                                           float* __restrict__ sw) {
-  __shared__ uint32_t red[32][kWqStrip + 1];
-  __shared__ float inv_s[kWqStrip];
-  __shared__ float tile[kWqTileK][kWqStrip + 1];
-
-  const int t = threadIdx.x;
-  const int n0 = blockIdx.x * kWqStrip;
-  const int rg = t >> 3;         // 0..31: row group
-  const int cc = (t & 7) * 8;    // first of 8 columns owned by this thread
-
-  // ---- pass 1: column absmax ------------------------------------------------
+__global__ __launch_bounds__(kWaThreads) void wabsmax_kernel(const uint16_t* __restrict__ W,
+                                                            int K, int N,
+                                                            float* __restrict__ sw) {
+  __shared__ uint32_t red[kWaThreads / 64][kWaStrip];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * kWaStrip + lane * 8;
+  const int k0 = blockIdx.y * kWaRows;
+  const int k1 = min(K, k0 + kWaRows);
   uint32_t mx[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) mx[e] = 0;
-  for (int k = rg; k < K; k += 32) {
-    const uint16_t* row = W + (size_t)k * N + n0 + cc;
-    if (VEC && n0 + cc + 8 <= N) {
-      v4i raw = *reinterpret_cast<const v4i*>(row);
+  if (VEC && c < N) {
+    // four rows in flight per lane
+    int k = k0 + wave;
+    for (; k + 12 < k1; k += 16) {
+      v4i r[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        r[u] = *reinterpret_cast<const v4i*>(W + (size_t)(k + 4 * u) * N + c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t b = habs_bits(((uint32_t)r[u][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+          mx[e] = b > mx[e] ? b : mx[e];
+        }
+    }
+    for (; k < k1; k += 4) {
+      const v4i r = *reinterpret_cast<const v4i*>(W + (size_t)k * N + c);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint32_t b = habs_bits(((uint32_t)raw[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+        const uint32_t b = habs_bits(((uint32_t)r[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
         mx[e] = b > mx[e] ? b : mx[e];
+      }
+    }
+  } else if (!VEC) {
+    for (int k = k0 + wave; k < k1; k += 4) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c + e < N) {
+          const uint32_t b = habs_bits(W[(size_t)k * N + c + e]);
+          mx[e] = b > mx[e] ? b : mx[e];
+        }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[wave][lane * 8 + e] = mx[e];
+  __syncthreads();
+  for (int j = threadIdx.x; j < kWaStrip; j += kWaThreads) {
+    uint32_t m = red[0][j];
+#pragma unroll
+    for (int w = 1; w < kWaThreads / 64; ++w) m = red[w][j] > m ? red[w][j] : m;
+    const int n = blockIdx.x * kWaStrip + j;
+    if (n < N && m != 0)
+      atomicMax(reinterpret_cast<unsigned int*>(sw) + n, __float_as_uint(h2f((uint16_t)m)));
+  }
+}
+
+// grid = (ceil(N / 64), ceil(K / 128)).  Tile: rows k0 .. k0+127 (K % 16 == 0,
+// so a row is either wholly inside or past K in 16-code pieces) x output
+// features n0 .. n0+63.
+template <bool VEC>
+__global__ __launch_bounds__(kWcThreads) void wcode_kernel(const uint16_t* __restrict__ W, int K,
+                                                          int N, const float* __restrict__ sw,
+                                                          int8_t* __restrict__ Wq) {
+  __shared__ uint16_t tile[kWcK][kWcN + 2];   // 33 dwords per row: column reads spread banks
+  __shared__ float inv_s[kWcN];
+  const int t = threadIdx.x;
+  const int n0 = blockIdx.x * kWcN, k0 = blockIdx.y * kWcK;
+  if (t < kWcN) inv_s[t] = n0 + t < N ? quant_scale(sw[n0 + t]) : 0.0f;
+  // load: 128 rows x 8 pieces of 8 values, four pieces per thread
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = t + i * kWcThreads, row = q >> 3, ch = q & 7;
+    const int k = k0 + row, c = n0 + ch * 8;
+    uint32_t v[4] = {0, 0, 0, 0};
+    if (VEC) {
+      if (k < K && c < N) {
+        const v4i r = *reinterpret_cast<const v4i*>(W + (size_t)k * N + c);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) v[d] = (uint32_t)r[d];
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (n0 + cc + e < N) {
-          uint32_t b = habs_bits(row[e]);
-          mx[e] = b > mx[e] ? b : mx[e];
-        }
-      }
+      for (int e = 0; e < 8; ++e)
+        if (k < K && c + e < N) v[e >> 1] |= (uint32_t)W[(size_t)k * N + c + e] << ((e & 1) * 16);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      tile[row][ch * 8 + 2 * d] = (uint16_t)(v[d] & 0xffffu);
+      tile[row][ch * 8 + 2 * d + 1] = (uint16_t)(v[d] >> 16);
     }
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) red[rg][cc + e] = mx[e];
   __syncthreads();
-  if (t < kWqStrip) {
-    uint32_t m = 0;
-    for (int r = 0; r < 32; ++r) m = red[r][t] > m ? red[r][t] : m;
-    const float a = h2f((uint16_t)m);
-    inv_s[t] = quant_scale(a);
-    if (n0 + t < N) sw[n0 + t] = a;
-  }
-  __syncthreads();
-
-  // ---- pass 2: codes, transposed through LDS ----------------------------------
-  const int nl = t >> 2;          // output feature inside the strip
-  const int kc = (t & 3) * 16;    // 16 consecutive k of that feature
-  for (int k0 = 0; k0 < K; k0 += kWqTileK) {
+  // store: 64 output features x 8 pieces of 16 codes, two pieces per thread
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kr = rg + 32 * h;
-      const int k = k0 + kr;
-      const uint16_t* row = W + (size_t)k * N + n0 + cc;
-      if (k < K && VEC && n0 + cc + 8 <= N) {
-        v4i raw = *reinterpret_cast<const v4i*>(row);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          tile[kr][cc + e] = h2f((uint16_t)(((uint32_t)raw[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          tile[kr][cc + e] = (k < K && n0 + cc + e < N) ? h2f(row[e]) : 0.0f;
-      }
-    }
-    __syncthreads();
-    const int n = n0 + nl;
-    const int k = k0 + kc;
+  for (int i = 0; i < 2; ++i) {
+    const int q = t + i * kWcThreads, nl = q >> 3, ch = q & 7;
+    const int n = n0 + nl, k = k0 + ch * 16;
     if (n < N && k < K) {
       const float inv = inv_s[nl];
       uint32_t w[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        w[g] = pack4_i8(quant_code(tile[kc + 4 * g + 0][nl], inv),
-                        quant_code(tile[kc + 4 * g + 1][nl], inv),
-                        quant_code(tile[kc + 4 * g + 2][nl], inv),
-                        quant_code(tile[kc + 4 * g + 3][nl], inv));
-      v4i out = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-      *reinterpret_cast<v4i*>(Wq + (size_t)n * K + k) = out;
+        w[g] = pack4_i8(quant_code(h2f(tile[ch * 16 + 4 * g + 0][nl]), inv),
+                        quant_code(h2f(tile[ch * 16 + 4 * g + 1][nl]), inv),
+                        quant_code(h2f(tile[ch * 16 + 4 * g + 2][nl]), inv),
+                        quant_code(h2f(tile[ch * 16 + 4 * g + 3][nl]), inv));
+      *reinterpret_cast<v4i*>(Wq + (size_t)n * K + k) =
+          v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     }
-    __syncthreads();
   }
 }
 
 hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, float* sw,
                                   hipStream_t stream) {
-  const dim3 grid((N + kWqStrip - 1) / kWqStrip);
+  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(sw), N, 0u, stream);
+  if (e != hipSuccess) return e;
   const bool vec = (N % 8 == 0) && ((uintptr_t)W % 16 == 0);
-  if (vec)
-    hipLaunchKernelGGL(wquant_kernel<true>, grid, dim3(kWqThreads), 0, stream, W, K, N, Wq, sw);
-  else
-    hipLaunchKernelGGL(wquant_kernel<false>, grid, dim3(kWqThreads), 0, stream, W, K, N, Wq, sw);
+  const dim3 ga((N + kWaStrip - 1) / kWaStrip, (K + kWaRows - 1) / kWaRows);
+  const dim3 gc((N + kWcN - 1) / kWcN, (K + kWcK - 1) / kWcK);
+  if (vec) {
+    hipLaunchKernelGGL(wabsmax_kernel<true>, ga, dim3(kWaThreads), 0, stream, W, K, N, sw);
+    hipLaunchKernelGGL(wcode_kernel<true>, gc, dim3(kWcThreads), 0, stream, W, K, N,
+                       (const float*)sw, Wq);
+  } else {
+    hipLaunchKernelGGL(wabsmax_kernel<false>, ga, dim3(kWaThreads), 0, stream, W, K, N, sw);
+    hipLaunchKernelGGL(wcode_kernel<false>, gc, dim3(kWcThreads), 0, stream, W, K, N,
+                       (const float*)sw, Wq);
+  }
   return hipGetLastError();
 }
 

@@ -74,6 +74,13 @@ WORKLOADS = {
         # a batch of 32 tokens on the decode layer: the weight-bound path for
         # 16 < M <= 64
         Workload("decode_m32", 32, 4096, 16384, 1.0, 0.02, 4, 6.5, 40.0, seed=8),
+        # the decode layer with 1 % of its hidden columns outliers (41 of
+        # 4096): the fused kernel's path for many outlier columns per wave
+        Workload("decode_1pct", 8, 4096, 16384, 1.0, 0.02, 41, 6.5, 40.0, seed=9),
+        # batches of 128 and 256 tokens on the decode layer: weight-bound shapes
+        # above the streaming kernel's 64 rows
+        Workload("decode_m128", 128, 4096, 16384, 1.0, 0.02, 4, 6.5, 40.0, seed=10),
+        Workload("decode_m256", 256, 4096, 16384, 1.0, 0.02, 4, 6.5, 40.0, seed=11),
     ]
 }
 

@@ -230,6 +230,10 @@ def _linear_cases():
     yield "stream_m64", 64, 2048, 520, 4, 6.0, 1.0
     yield "stream_m64_many_outliers", 64, 1024, 200, 90, 6.0, 1.0
     yield "decode_many_outliers", 4, 1024, 130, 70, 6.0, 1.0
+    # the fused kernel with many outlier columns per wave (batched reads)
+    yield "decode_m16_300_outliers", 16, 4096, 320, 300, 6.0, 1.0
+    yield "decode_m1_100_outliers", 1, 512, 200, 100, 6.0, 1.0
+    yield "decode_m8_41_outliers", 8, 4096, 520, 41, 6.0, 1.0
     yield "prefill_m17", 17, 1024, 600, 2, 6.0, 1.0
     yield "prefill_ragged", 300, 272, 520, 5, 6.0, 1.0
     yield "prefill_tiles", 513, 1040, 769, 8, 6.0, 1.0
@@ -339,7 +343,7 @@ def test_linear_concurrent_host_threads(lib):
 # ---------------------------------------------------------------------------------
 # the benchmark workloads at full size, in the launch configuration bench.py times
 # ---------------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["tiny", "decode"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "decode_1pct", "decode_m128"])
 def test_workload_full_oracle(lib, name):
     w = wl.WORKLOADS[name]
     say(f"workload {name} (full oracle)")
@@ -356,7 +360,7 @@ def test_workload_full_oracle(lib, name):
 
 @pytest.mark.parametrize("name", ["qkv_prefill", "mlp_down_prefill", "square_0pct",
                                   "square_0.1pct", "square_1pct", "decode_qkv",
-                                  "decode_mlp_down", "decode_m32"])
+                                  "decode_mlp_down", "decode_m32", "decode_m256"])
 def test_workload_full_sampled(lib, name):
     w = wl.WORKLOADS[name]
     say(f"workload {name} (sampled): generating inputs")
