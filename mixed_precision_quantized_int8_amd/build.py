@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libint8lin.so")
 
 ARCH = "gfx950"
-SOURCES = ["wquant.hip", "act.hip", "gemm.hip", "decode.hip", "train.hip", "int8lin_abi.hip"]
+SOURCES = ["wquant.hip", "act.hip", "gemm.hip", "skinny.hip", "decode.hip", "train.hip",
+           "int8lin_abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

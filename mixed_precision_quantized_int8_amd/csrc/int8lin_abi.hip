@@ -66,7 +66,7 @@ i8l_status check_zp_k(const char* fn, int64_t K) {
   return I8L_OK;
 }
 
-// The GEMM's split-K tail (M > 64, the only shapes that reach the GEMM) needs
+// The GEMM's split-K tail (M > 256, the only shapes that reach it) needs
 // int32 partial tiles, sized for a device with up to kGemmMaxSlices compute
 // units; the counters region before them is reserved.  split == false lays out
 // no partial tiles (the GEMM then computes every tile whole).
@@ -86,7 +86,7 @@ i8l_workspace_layout layout_of(int64_t M, int64_t K, int64_t N, bool split = tru
       (M >= 1 && M <= i8l::kActSmallRows) ? (size_t)i8l::act_slices((int)K) * (1 + 2 * i8l::kActSmallRows) : 0;
   L.act_partials = off; off += up(act_words * sizeof(uint32_t));
   int slices = 0;
-  if (split && M > i8l::kStreamMaxM && N > 0) {
+  if (split && M > i8l::kSkinnyMaxM && N > 0) {
     const i8l::GemmSplit p = i8l::gemm_split_plan((int)M, (int)N, (int)K, i8l::kGemmMaxSlices);
     slices = p.split_tiles * p.S;
   }
@@ -262,6 +262,7 @@ i8l_status linear_impl(const char* fn, const uint16_t* X, int64_t M, int64_t K, 
   i8l::GemmArgs g{w.Xq, Wq, m, n, k, w.sx, sw, w.n_out, w.idx, w.X_O, W_outlier_rows, Y, nullptr,
                   bias, zp ? w.zp : nullptr, zp ? wsum : nullptr, w.gemm_cnt, w.gemm_part,
                   w.gemm_slices, 0, 1};
+  if (m <= i8l::kSkinnyMaxM) return hip_status(fn, i8l::launch_gemm_skinny(g, st));
   return hip_status(fn, i8l::launch_gemm(g, st));
 }
 }  // namespace
@@ -393,6 +394,9 @@ I8L_API i8l_status int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, 
   (void)hipGetLastError();
   i8l::GemmArgs g{Xq, Wq, (int)M, (int)N, (int)K, nullptr, nullptr, nullptr, nullptr, nullptr,
                   nullptr, nullptr, acc, nullptr, nullptr, nullptr, nullptr, part, slices, 0, 1};
+  // the kernel int8_linear runs for this M: 256 x 64 tiles up to 256 rows
+  if (M <= i8l::kSkinnyMaxM)
+    return hip_status(fn, i8l::launch_gemm_skinny(g, static_cast<hipStream_t>(stream)));
   return hip_status(fn, i8l::launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 

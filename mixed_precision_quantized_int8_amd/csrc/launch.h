@@ -90,6 +90,12 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
+// The same product and epilogue with 256 x 64 tiles and no split along K
+// (skinny.hip), for kStreamMaxM < M <= kSkinnyMaxM: weight-bound batches,
+// where 256 x 256 tiles would leave most compute units idle.
+constexpr int kSkinnyMaxM = 256;
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
+
 // Small-M (decode) path, M <= kStreamMaxM: when decode_fits(M, K) (M <= 16,
 // K <= 4096) one fused kernel does the activation stage, the int8 product,
 // the outlier product and the epilogue; otherwise the activation kernels run

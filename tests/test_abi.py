@@ -184,10 +184,13 @@ def test_workspace_layout(i8l):
     assert i8l.workspace_layout(4096, 57344, 14336)["gemm_slices"] == 128 * 2  # 896 tiles
     assert i8l.workspace_layout(8192, 8192, 8192)["gemm_slices"] == 0         # 1024 tiles
     assert i8l.workspace_layout(520, 2048, 1300)["gemm_slices"] == 18 * 2     # 18 tiles
-    # M <= 64 never reaches the GEMM, so no partial tiles are reserved there
+    # M <= 256 never reaches the 256 x 256 GEMM (M <= 64: the small-M kernels;
+    # 64 < M <= 256: 256 x 64 tiles, never split), so no partial tiles there
     assert i8l.workspace_layout(32, 4096, 16384)["gemm_slices"] == 0
     assert i8l.workspace_layout(64, 4096, 16384)["gemm_slices"] == 0
-    assert i8l.workspace_layout(65, 4096, 16384)["gemm_slices"] == 64 * 4     # 64 tiles
+    assert i8l.workspace_layout(65, 4096, 16384)["gemm_slices"] == 0
+    assert i8l.workspace_layout(256, 4096, 16384)["gemm_slices"] == 0
+    assert i8l.workspace_layout(257, 4096, 16384)["gemm_slices"] == 128 * 2   # 128 tiles
     assert i8l.workspace_bytes(4, 70, 4) == 0
     with pytest.raises(i8l.Int8LinError):
         i8l.workspace_layout(4, 70)

@@ -235,10 +235,17 @@ def _linear_cases():
     yield "decode_m1_100_outliers", 1, 512, 200, 100, 6.0, 1.0
     yield "decode_m8_41_outliers", 8, 4096, 520, 41, 6.0, 1.0
     yield "prefill_m17", 17, 1024, 600, 2, 6.0, 1.0
+    # 64 < M <= 256: the 256 x 64 tiles (one or two outlier staging rounds,
+    # ragged N with element stores)
+    yield "skinny_m65", 65, 1040, 520, 5, 6.0, 1.0
+    yield "skinny_m128", 128, 4096, 1000, 3, 6.0, 1.0
+    yield "skinny_m200_ragged_n", 200, 272, 70, 2, 6.0, 1.0
+    yield "skinny_m256_40_outliers", 256, 2048, 264, 40, 6.0, 1.0
     yield "prefill_ragged", 300, 272, 520, 5, 6.0, 1.0
     yield "prefill_tiles", 513, 1040, 769, 8, 6.0, 1.0
     yield "prefill_chunks", 64, 512, 300, 45, 6.0, 1.0
-    yield "prefill_many_outliers", 70, 1024, 300, 130, 6.0, 1.0   # > 96: unstaged path
+    yield "prefill_many_outliers", 70, 1024, 300, 130, 6.0, 1.0   # 256 x 64 tiles
+    yield "prefill_many_outliers_big", 300, 1024, 300, 130, 6.0, 1.0   # > 96: unstaged path
     yield "prefill_split_k", 520, 2048, 1300, 6, 6.0, 1.0         # 18 tiles, K split in 2
     yield "prefill_no_outliers", 260, 512, 512, 0, 6.0, 1.0
     yield "prefill_disabled", 260, 512, 512, 3, math.inf, 1.0
@@ -502,7 +509,8 @@ def test_linear_split_tail_sampled(lib):
     ("stream_m32", 32, 4096, 520, 3),        # streaming kernel, 2 row groups
     ("stream_m64_many", 64, 1024, 200, 70),  # 4 row groups, outliers past the LDS copy
     ("prefill", 300, 1040, 520, 5),          # GEMM, staged outlier rows
-    ("prefill_many", 70, 1024, 300, 130),    # GEMM, rows straight from memory
+    ("prefill_many", 300, 1024, 300, 130),   # GEMM, rows straight from memory
+    ("skinny_many", 70, 1024, 300, 130),     # 256 x 64 tiles, five staging rounds
     ("prefill_split", 520, 2048, 1300, 6),   # GEMM split-K tail
 ])
 def test_linear_rebuilt_outlier_rows(lib, name, M, K, N, n_out):

@@ -168,6 +168,8 @@ def _linear_cases():
     yield "decode_m1_k16", 1, 16, 64, 0, 6.0, "offset", False, True
     yield "decode_m2_k3088", 2, 3088, 70, 1, 6.0, "offset", True, True
     yield "prefill_m17", 17, 1024, 600, 2, 6.0, "positive", True, True
+    yield "skinny_m100", 100, 1024, 520, 3, 6.0, "offset", True, True
+    yield "skinny_m256_rebuilt", 256, 2048, 264, 40, 6.0, "negative", False, False
     yield "prefill_ragged", 300, 272, 520, 5, 6.0, "offset", True, True
     yield "prefill_tiles", 513, 1040, 769, 8, 6.0, "offset", False, False
     yield "prefill_split_k", 520, 2048, 1300, 6, 6.0, "positive", True, True
