@@ -49,9 +49,12 @@ constexpr int kDecP = 4;                      // 16-feature blocks per workgroup
 constexpr int kDecCols = 16 * kDecP;
 constexpr int kDecMaxKS = 8;                  // fused kernel: k-steps per wave
 constexpr int kDecOutPre = 4;                 // outlier columns per wave preloaded
+constexpr int kDecOutDma = 4;                 // further ones fetched into LDS behind the stream
 constexpr int kDecMaxOutLds = 64;             // stream kernel: outlier values in LDS
 constexpr int kDecStreamRows = 64;            // stream kernel: rows of X (4 row groups)
 constexpr int kDecOutReg = 8;                 // stream kernel: outlier weights per lane
+
+#define I8L_DEC_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Zero bytes for lanes whose load is out of range (loads stay unconditional,
 // so the number of loads in flight is fixed and waits stay exact).
@@ -155,6 +158,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   __shared__ int sHasOut[kDecWaves];
   __shared__ float sSx[16];
   __shared__ v4i sQ[16][KS * kDecWaves * 4 + 4];    // codes [m][16-byte chunk] + spare
+  // outlier columns kDecOutPre .. kDecOutPre + kDecOutDma - 1 of each wave:
+  // weight values (lane = feature: the fp16 weight, or the code when no fp16
+  // weight is kept) and X values (lane = row), written by LDS-DMA loads, which
+  // give every lane a dword (the value zero-extended) whatever the load size
+  __shared__ uint32_t sOw[kDecWaves][kDecOutDma][64];
+  __shared__ uint32_t sOx[kDecWaves][kDecOutDma][64];
 
   const int M = d.M, K = d.K, N = d.N;
   const int lane = threadIdx.x & 63;
@@ -351,6 +360,29 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   // the rest of the weight stream goes out before the barrier: a wave waiting
   // there for the slowest wave of its workgroup keeps its loads in flight
   load_b(kPre, kLoads);
+  // the next kDecOutDma outlier columns of this wave (rare) follow the stream
+  // into LDS: they arrive with the weight, not one round trip after it
+  int kx[kDecOutDma];
+#pragma unroll
+  for (int u = 0; u < kDecOutDma; ++u) kx[u] = -1;
+  if (wcount > kDecOutPre) {   // uniform
+#pragma unroll
+    for (int u = 0; u < kDecOutDma; ++u) {
+      kx[u] = nth_outlier(kDecOutPre + u);
+      if (kx[u] >= 0) {
+        // X[lane][k]: lanes >= M read 0 from the range check
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, I8L_DEC_LDS(&sOx[wave][u][0]), 2,
+                                                 (int)((uint32_t)(lane * K + kx[u]) * 2u), 0, 0, 0);
+        if (rebuild)   // the code Wq[n0 + lane][k]
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, I8L_DEC_LDS(&sOw[wave][u][0]), 1,
+                                                   (int)(uint32_t)(lane * K + kx[u]), 0, 0, 0);
+        else           // the fp16 weight W[k][n0 + lane]
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              make_rsrc(d.W_rows + (size_t)kx[u] * N + n0, (uint32_t)nrows * 2u),
+              I8L_DEC_LDS(&sOw[wave][u][0]), 2, (int)((uint32_t)lane * 2u), 0, 0, 0);
+      }
+    }
+  }
   if (lane < MR) sRowMax[kc][lane] = rm;
   if (ZP && lane < MR) sRowMin[ZP ? kc : 0][lane] = rn;
   if (lane == 0) sCnt[kc] = wcount;
@@ -442,9 +474,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
           if (m < M) yo[m] += h2f((uint16_t)__builtin_amdgcn_readlane((int)xo[j], m)) * wv;
       }
     }
-    // the rest, straight from memory: all loads of a batch go out before any
-    // of their values is used
-    for (int j0 = kDecOutPre; j0 < wcount; j0 += kDecOutBatch) {   // uniform
+    if (wcount > kDecOutPre) {   // the columns fetched into LDS behind the stream
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA has landed
+#pragma unroll
+      for (int u = 0; u < kDecOutDma; ++u) {
+        if (kx[u] >= 0) {   // uniform
+          const uint32_t wb = sOw[wave][u][lane];
+          const float wv = n0 + lane >= N ? 0.0f
+                           : rebuild ? h2f(dequant_w16((int)(int8_t)(wb & 0xffu), swl))
+                                     : h2f((uint16_t)(wb & 0xffffu));
+#pragma unroll
+          for (int m = 0; m < 16; ++m)
+            if (m < M) yo[m] += h2f((uint16_t)(sOx[wave][u][m] & 0xffffu)) * wv;
+        }
+      }
+    }
+    // the rest (beyond kDecOutPre + kDecOutDma), straight from memory: all
+    // loads of a batch go out before any of their values is used
+    for (int j0 = kDecOutPre + kDecOutDma; j0 < wcount; j0 += kDecOutBatch) {   // uniform
       int kk[kDecOutBatch], xv[kDecOutBatch];
       float wv[kDecOutBatch];
 #pragma unroll
@@ -492,7 +539,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
         if (lane < M) d.X_O[(size_t)lane * K + rank + j] = xo[j];
       }
     }
-    for (int j0 = kDecOutPre; j0 < wcount; j0 += kDecOutBatch) {   // uniform, batched as above
+    if (wcount > kDecOutPre) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < kDecOutDma; ++u) {
+        if (kx[u] >= 0) {
+          if (lane == 0) d.idx[rank + kDecOutPre + u] = kx[u];
+          if (lane < M)
+            d.X_O[(size_t)lane * K + rank + kDecOutPre + u] = (uint16_t)(sOx[wave][u][lane] & 0xffffu);
+        }
+      }
+    }
+    for (int j0 = kDecOutPre + kDecOutDma; j0 < wcount; j0 += kDecOutBatch) {   // uniform, batched as above
       int kk[kDecOutBatch];
       uint16_t xv[kDecOutBatch];
 #pragma unroll
