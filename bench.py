@@ -56,8 +56,8 @@ DECODE_STEPS, DECODE_WARMUP = 200, 20
 # factor (profiles/traffic-mlp_down_prefill_and_decode.md); valid only for the
 # kernel sources it was measured on (sha256 of the listed files).
 TRAFFIC = {
-    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 6731568715, "src": "ac63a428c46c33e7"},
-    ("decode_kernel", "decode"): {"bytes": 68511876, "src": "fb75e3d64f2e27d6"},
+    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 6731347104, "src": "4464f0fddb958b4a"},
+    ("decode_kernel", "decode"): {"bytes": 68534577, "src": "00f2fed7b24adf76"},
 }
 
 
