@@ -160,9 +160,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   __shared__ v4i sQ[16][KS * kDecWaves * 4 + 4];    // codes [m][16-byte chunk] + spare
   // outlier columns kDecOutPre .. kDecOutPre + kDecOutDma - 1 of each wave:
   // weight values (lane = feature: the fp16 weight, or the code when no fp16
-  // weight is kept) and X values (lane = row), written by LDS-DMA loads, which
-  // give every lane a dword (the value zero-extended) whatever the load size
-  __shared__ uint32_t sOw[kDecWaves][kDecOutDma][64];
+  // weight is kept; slots kDecOutPre ..) and X values (lane = row), written by
+  // LDS-DMA loads, which give every lane a dword (the value zero-extended)
+  // whatever the load size.  Slots 0 .. kDecOutPre - 1 of sOw take the fp16
+  // weight values of the first columns (held in registers until then) for the
+  // matrix-core product of the outlier columns.
+  __shared__ uint32_t sOw[kDecWaves][kDecOutPre + kDecOutDma][64];
   __shared__ uint32_t sOx[kDecWaves][kDecOutDma][64];
 
   const int M = d.M, K = d.K, N = d.N;
@@ -337,9 +340,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     wo[j] = buf_load_u16(ro, (uint32_t)lane * 2u);
     wc[j] = buf_load_u8(rw, ok && rebuild ? (uint32_t)(lane * K + ko[j]) : kBufOff);
   }
-  auto wval = [&](int j) -> float {
-    return rebuild ? h2f(dequant_w16((int)(int8_t)wc[j], swl)) : h2f(wo[j]);
-  };
 
   uint32_t rm, rn = 0;
   if constexpr (ZP) {
@@ -360,29 +360,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   // the rest of the weight stream goes out before the barrier: a wave waiting
   // there for the slowest wave of its workgroup keeps its loads in flight
   load_b(kPre, kLoads);
-  // the next kDecOutDma outlier columns of this wave (rare) follow the stream
-  // into LDS: they arrive with the weight, not one round trip after it
+  // columns kDecOutPre .. kDecOutPre + kDecOutDma - 1 of this wave (many
+  // outliers only): fetched into LDS right after the codes, below
   int kx[kDecOutDma];
 #pragma unroll
   for (int u = 0; u < kDecOutDma; ++u) kx[u] = -1;
-  if (wcount > kDecOutPre) {   // uniform
-#pragma unroll
-    for (int u = 0; u < kDecOutDma; ++u) {
-      kx[u] = nth_outlier(kDecOutPre + u);
-      if (kx[u] >= 0) {
-        // X[lane][k]: lanes >= M read 0 from the range check
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, I8L_DEC_LDS(&sOx[wave][u][0]), 2,
-                                                 (int)((uint32_t)(lane * K + kx[u]) * 2u), 0, 0, 0);
-        if (rebuild)   // the code Wq[n0 + lane][k]
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, I8L_DEC_LDS(&sOw[wave][u][0]), 1,
-                                                   (int)(uint32_t)(lane * K + kx[u]), 0, 0, 0);
-        else           // the fp16 weight W[k][n0 + lane]
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              make_rsrc(d.W_rows + (size_t)kx[u] * N + n0, (uint32_t)nrows * 2u),
-              I8L_DEC_LDS(&sOw[wave][u][0]), 2, (int)((uint32_t)lane * 2u), 0, 0, 0);
-      }
-    }
-  }
   if (lane < MR) sRowMax[kc][lane] = rm;
   if (ZP && lane < MR) sRowMin[ZP ? kc : 0][lane] = rn;
   if (lane == 0) sCnt[kc] = wcount;
@@ -453,6 +435,31 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
       sQ[lr][s0 + t < s1 ? (s0 + t) * 4 + g : KS * kDecWaves * 4 + g] = a[t];
     }
   }
+  // The further outlier columns follow the stream into LDS: issued behind this
+  // wave's weight loads, they land with them, not one round trip after them.
+  // They go out only now, after the codes' LDS writes: the compiler makes an
+  // LDS write that it cannot tell apart from an LDS-DMA destination wait for
+  // every load issued so far, which would hold the codes (and the products
+  // after them) until the whole weight had landed.
+  __builtin_amdgcn_sched_barrier(0);
+  if (wcount > kDecOutPre) {   // uniform
+#pragma unroll
+    for (int u = 0; u < kDecOutDma; ++u) {
+      kx[u] = nth_outlier(kDecOutPre + u);
+      if (kx[u] >= 0) {
+        // X[lane][k]: lanes >= M read 0 from the range check
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, I8L_DEC_LDS(&sOx[wave][u][0]), 2,
+                                                 (int)((uint32_t)(lane * K + kx[u]) * 2u), 0, 0, 0);
+        if (rebuild)   // the code Wq[n0 + lane][k]
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, I8L_DEC_LDS(&sOw[wave][kDecOutPre + u][0]), 1,
+                                                   (int)(uint32_t)(lane * K + kx[u]), 0, 0, 0);
+        else           // the fp16 weight W[k][n0 + lane]
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              make_rsrc(d.W_rows + (size_t)kx[u] * N + n0, (uint32_t)nrows * 2u),
+              I8L_DEC_LDS(&sOw[wave][kDecOutPre + u][0]), 2, (int)((uint32_t)lane * 2u), 0, 0, 0);
+      }
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int c = 0; c < kDecP; ++c)
@@ -460,61 +467,87 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     for (int t = 0; t < KS; ++t)
       acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], fb[t][c], acc[c], 0, 0, 0);
 
-  // ---- outlier product of this chunk's columns (lane = feature n0 + lane) ----------
+  // ---- outlier product of this chunk's columns ----------------------------------
+  // Up to kDecOutPre + kDecOutDma columns on the matrix cores: X_O (16 rows x
+  // the columns, zero-padded to 16) times their fp16 weight rows (the columns x
+  // 64 features) with v_mfma_f32_16x16x16_f16, one product per 16-feature
+  // block, into fp32.  Lane l holds operand row (or feature) l % 16 and
+  // columns 4 (l / 16) .. 4 (l / 16) + 3 of the wave's outlier list; columns
+  // past the list are zero in both operands (an unwritten slot could hold a
+  // NaN pattern).  The result has the layout of the int8 partials: lane l,
+  // feature l % 16 of the block, rows 4 (l / 16) .. + 3.
   if (wcount > 0) {
-    float yo[16];
+    constexpr int kDecOutMfma = kDecOutPre + kDecOutDma;   // 8: two of the four groups
+    const int nv = wcount < kDecOutMfma ? wcount : kDecOutMfma;   // uniform
+    if (wcount > kDecOutPre) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // DMA landed
+    // weight values of the first columns into their slots, fp16 (lane = feature)
 #pragma unroll
-    for (int m = 0; m < 16; ++m) yo[m] = 0.0f;
+    for (int j = 0; j < kDecOutPre; ++j)
+      if (j < found)
+        sOw[wave][j][lane] = rebuild ? dequant_w16((int)(int8_t)wc[j], swl) : wo[j];
+    if (rebuild && wcount > kDecOutPre) {   // the fetched codes become fp16 values
 #pragma unroll
-    for (int j = 0; j < kDecOutPre; ++j) {
-      if (j < found) {
-        const float wv = wval(j);
-#pragma unroll
-        for (int m = 0; m < 16; ++m)
-          if (m < M) yo[m] += h2f((uint16_t)__builtin_amdgcn_readlane((int)xo[j], m)) * wv;
-      }
+      for (int u = 0; u < kDecOutDma; ++u)
+        if (kx[u] >= 0)
+          sOw[wave][kDecOutPre + u][lane] =
+              dequant_w16((int)(int8_t)(sOw[wave][kDecOutPre + u][lane] & 0xffu), swl);
     }
-    if (wcount > kDecOutPre) {   // the columns fetched into LDS behind the stream
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA has landed
+    const int jb = 4 * g;   // this lane's first column
+    uint32_t ax[4];
 #pragma unroll
-      for (int u = 0; u < kDecOutDma; ++u) {
-        if (kx[u] >= 0) {   // uniform
-          const uint32_t wb = sOw[wave][u][lane];
-          const float wv = n0 + lane >= N ? 0.0f
-                           : rebuild ? h2f(dequant_w16((int)(int8_t)(wb & 0xffu), swl))
-                                     : h2f((uint16_t)(wb & 0xffffu));
+    for (int i = 0; i < 4; ++i) {
+      // column i (registers, lane = row) for lanes 0-15, column 4 + i (LDS) for 16-31
+      const uint32_t xr0 = (uint32_t)__shfl((int)xo[i], lr, 64);
+      const uint32_t xr1 = sOx[wave][i][lr];
+      ax[i] = jb + i < nv ? (g == 0 ? xr0 : xr1) & 0xffffu : 0u;
+    }
+    const v4h av = __builtin_bit_cast(v4h, v2i{(int)(ax[0] | (ax[1] << 16)), (int)(ax[2] | (ax[3] << 16))});
+    v4f po[kDecP];
+#pragma unroll
+    for (int c = 0; c < kDecP; ++c) {
+      uint32_t bw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bw[i] = jb + i < nv ? sOw[wave][(jb + i) & (kDecOutMfma - 1)][c * 16 + lr] & 0xffffu : 0u;
+      const v4h bv = __builtin_bit_cast(v4h, v2i{(int)(bw[0] | (bw[1] << 16)), (int)(bw[2] | (bw[3] << 16))});
+      po[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kDecP; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sYo[wave][4 * g + r][c * 16 + lr] = po[c][r];
+    // the rest (beyond kDecOutMfma, rare), straight from memory on the vector
+    // units (lane = feature n0 + lane): all loads of a batch go out before any
+    // of their values is used
+    if (wcount > kDecOutMfma) {   // uniform
+      float yo[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) yo[m] = 0.0f;
+      for (int j0 = kDecOutMfma; j0 < wcount; j0 += kDecOutBatch) {   // uniform
+        int kk[kDecOutBatch], xv[kDecOutBatch];
+        float wv[kDecOutBatch];
+#pragma unroll
+        for (int u = 0; u < kDecOutBatch; ++u) kk[u] = nth_outlier(j0 + u);
+#pragma unroll
+        for (int u = 0; u < kDecOutBatch; ++u) {
+          wv[u] = 0.0f;
+          xv[u] = 0;
+          if (kk[u] >= 0) {   // uniform
+            if (n0 + lane < N)
+              wv[u] = rebuild ? h2f(dequant_w16(d.Wq[(size_t)(n0 + lane) * K + kk[u]], swl))
+                              : h2f(d.W_rows[(size_t)kk[u] * N + n0 + lane]);
+            if (lane < M) xv[u] = (int)d.X[(size_t)lane * K + kk[u]];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kDecOutBatch; ++u)
 #pragma unroll
           for (int m = 0; m < 16; ++m)
-            if (m < M) yo[m] += h2f((uint16_t)(sOx[wave][u][m] & 0xffffu)) * wv;
-        }
-      }
-    }
-    // the rest (beyond kDecOutPre + kDecOutDma), straight from memory: all
-    // loads of a batch go out before any of their values is used
-    for (int j0 = kDecOutPre + kDecOutDma; j0 < wcount; j0 += kDecOutBatch) {   // uniform
-      int kk[kDecOutBatch], xv[kDecOutBatch];
-      float wv[kDecOutBatch];
-#pragma unroll
-      for (int u = 0; u < kDecOutBatch; ++u) kk[u] = nth_outlier(j0 + u);
-#pragma unroll
-      for (int u = 0; u < kDecOutBatch; ++u) {
-        wv[u] = 0.0f;
-        xv[u] = 0;
-        if (kk[u] >= 0) {   // uniform
-          if (n0 + lane < N)
-            wv[u] = rebuild ? h2f(dequant_w16(d.Wq[(size_t)(n0 + lane) * K + kk[u]], swl))
-                            : h2f(d.W_rows[(size_t)kk[u] * N + n0 + lane]);
-          if (lane < M) xv[u] = (int)d.X[(size_t)lane * K + kk[u]];
-        }
+            if (m < M) yo[m] += h2f((uint16_t)__builtin_amdgcn_readlane(xv[u], m)) * wv[u];
       }
 #pragma unroll
-      for (int u = 0; u < kDecOutBatch; ++u)
-#pragma unroll
-        for (int m = 0; m < 16; ++m)
-          if (m < M) yo[m] += h2f((uint16_t)__builtin_amdgcn_readlane(xv[u], m)) * wv[u];
+      for (int m = 0; m < 16; ++m) sYo[wave][m][lane] += yo[m];
     }
-#pragma unroll
-    for (int m = 0; m < 16; ++m) sYo[wave][m][lane] = yo[m];
   }
   if (lane == 0) sHasOut[wave] = wcount > 0;
 

@@ -505,6 +505,7 @@ def test_linear_split_tail_sampled(lib):
     ("decode", 8, 4096, 1000, 3),            # fused decode kernel
     ("decode_m1", 1, 1040, 300, 2),
     ("decode_many", 4, 1024, 130, 9),        # more outliers than a wave preloads
+    ("decode_many_lds", 8, 1024, 520, 60),   # columns 5-8 of a wave fetched into LDS, and beyond
     ("decode_bigk", 8, 16384, 256, 4),       # activation kernels + streaming kernel
     ("stream_m32", 32, 4096, 520, 3),        # streaming kernel, 2 row groups
     ("stream_m64_many", 64, 1024, 200, 70),  # 4 row groups, outliers past the LDS copy

@@ -158,6 +158,9 @@ def _linear_cases():
     yield "decode_m16", 16, 4096, 512, 3, 6.0, "offset", True, False
     yield "decode_k8192", 8, 8192, 256, 5, 6.0, "negative", False, True
     yield "decode_bigk_many_outliers", 3, 4112, 200, 90, 6.0, "offset", True, True
+    # the fused kernel with up to and beyond eight outlier columns per wave
+    yield "decode_many_outliers", 8, 2048, 520, 50, 6.0, "offset", True, True
+    yield "decode_many_outliers_rebuilt", 4, 1024, 200, 60, 6.0, "negative", False, False
     yield "stream_m17_bias", 17, 1024, 600, 2, 6.0, "offset", True, True
     yield "stream_m40_k4112", 40, 4112, 300, 3, 6.0, "negative", False, False
     yield "stream_m64", 64, 2048, 520, 4, 6.0, "positive", True, True
