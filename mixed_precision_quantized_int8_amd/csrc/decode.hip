@@ -145,6 +145,64 @@ __device__ __forceinline__ v4i codes16_zp(const v4i (&x)[2], float inv65, int zp
 //    activation stage.
 // ZP: zero-point codes (row minimum and maximum instead of the absmax, codes
 //    minus 128, accumulators corrected by (128 - zp) * wsum, scale range / 255).
+// OR of h over the L lanes of one X row slot (lanes 16 g + L q + r, r < L; L
+// a power of two up to 16) with DPP moves inside a 16-lane row: neighbour
+// and pair swaps within quads, then the mirror image of each 8-lane half and
+// of the row (no LDS round trip).
+template <int L>
+__device__ __forceinline__ uint32_t or_slot(uint32_t h) {
+  if constexpr (L >= 2) h |= (uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0xb1, 0xf, 0xf, false);   // quad_perm 1,0,3,2
+  if constexpr (L >= 4) h |= (uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0x4e, 0xf, 0xf, false);   // quad_perm 2,3,0,1
+  if constexpr (L >= 8) h |= (uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0x141, 0xf, 0xf, false);  // row_half_mirror
+  if constexpr (L >= 16) h |= (uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0x140, 0xf, 0xf, false); // row_mirror
+  return h;
+}
+
+// Maximum (minimum) of v over the lanes lr, lr + L, lr + 2L, ... of each
+// 16-lane row (L a power of two up to 16): DPP row rotations by 8, 4, ..., L.
+template <int OFF>
+__device__ __forceinline__ uint32_t row_ror(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x120 + OFF, 0xf, 0xf, false);
+}
+// v of lane (lr + s) mod 16 of the same 16-lane row (a rotation right by 16 - s
+// moves each value s lanes down); s is a constant once inlined and unrolled
+__device__ __forceinline__ uint32_t row_up(uint32_t v, int s) {
+  switch (s & 15) {
+    case 1: return row_ror<15>(v);
+    case 2: return row_ror<14>(v);
+    case 3: return row_ror<13>(v);
+    case 4: return row_ror<12>(v);
+    case 5: return row_ror<11>(v);
+    case 6: return row_ror<10>(v);
+    case 7: return row_ror<9>(v);
+    case 8: return row_ror<8>(v);
+    case 9: return row_ror<7>(v);
+    case 10: return row_ror<6>(v);
+    case 11: return row_ror<5>(v);
+    case 12: return row_ror<4>(v);
+    case 13: return row_ror<3>(v);
+    case 14: return row_ror<2>(v);
+    case 15: return row_ror<1>(v);
+    default: return v;
+  }
+}
+template <int L>
+__device__ __forceinline__ uint32_t max_rows(uint32_t v) {
+  if constexpr (L <= 8) v = __builtin_elementwise_max(v, row_ror<8>(v));
+  if constexpr (L <= 4) v = __builtin_elementwise_max(v, row_ror<4>(v));
+  if constexpr (L <= 2) v = __builtin_elementwise_max(v, row_ror<2>(v));
+  if constexpr (L <= 1) v = __builtin_elementwise_max(v, row_ror<1>(v));
+  return v;
+}
+template <int L>
+__device__ __forceinline__ uint32_t min_rows(uint32_t v) {
+  if constexpr (L <= 8) v = __builtin_elementwise_min(v, row_ror<8>(v));
+  if constexpr (L <= 4) v = __builtin_elementwise_min(v, row_ror<4>(v));
+  if constexpr (L <= 2) v = __builtin_elementwise_min(v, row_ror<2>(v));
+  if constexpr (L <= 1) v = __builtin_elementwise_min(v, row_ror<1>(v));
+  return v;
+}
+
 template <int KS, int R, int PRE, bool ZP>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   constexpr int MR = 16 / R;         // X rows per slot
@@ -246,8 +304,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
         const uint32_t b = habs_bits(half_at(xr[j], e));
         h |= (b >= T && b <= 0x7c00u ? 1u : 0u) << e;
       }
-#pragma unroll
-      for (int off = 1; off < MR; off <<= 1) h |= __shfl_xor(h, off, 64);
+      h = or_slot<MR>(h);
       hm[j] = h;
       smax = u16x2{0, 0};
 #pragma unroll
@@ -272,22 +329,36 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   }
   // outlier columns of chunk step t as a wave-wide mask: bit l <-> column
   // (s0+t)*64 + l, so ascending column order is (t, bit)
+  // (16-bit group masks read from one lane of each slot: t is a constant
+  // wherever this is called, and so are the lanes)
   auto step_mask = [&](int t) -> uint64_t {
     const int j = t / R, qq = t % R;
     if (!((hitsets >> j) & 1u)) return 0;
-    const uint32_t h = __shfl(hm[j], (lane & ~15) | (qq * MR), 64);
-    return __ballot((h >> lr) & 1u);
-  };
-  int wcount = 0;
-  int ko[kDecOutPre];
+    uint64_t m = 0;
 #pragma unroll
-  for (int j = 0; j < kDecOutPre; ++j) ko[j] = -1;
+    for (int gg = 0; gg < 4; ++gg)
+      m |= (uint64_t)((uint32_t)__builtin_amdgcn_readlane((int)hm[j], 16 * gg + qq * MR) & 0xffffu)
+           << (16 * gg);
+    return m;
+  };
+  // The per-step masks (kept in scalar registers), the number of outlier
+  // columns and the first kDecOutPre + kDecOutDma of them, ascending (uniform).
+  int wcount = 0;
+  uint64_t msk[KS];
+  int ko[kDecOutPre + kDecOutDma];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) msk[t] = 0;
+#pragma unroll
+  for (int j = 0; j < kDecOutPre + kDecOutDma; ++j) ko[j] = -1;
   if (hitsets) {
+#pragma unroll
+    for (int t = 0; t < KS; ++t) msk[t] = step_mask(t);
+#pragma unroll
     for (int t = 0; t < KS; ++t) {
-      uint64_t w = step_mask(t);
+      uint64_t w = msk[t];
       wcount += __popcll(w);
 #pragma unroll
-      for (int j = 0; j < kDecOutPre; ++j) {
+      for (int j = 0; j < kDecOutPre + kDecOutDma; ++j) {
         if (w != 0 && ko[j] < 0) {
           ko[j] = (s0 + t) * 64 + __builtin_ctzll(w);
           w &= w - 1;
@@ -296,17 +367,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     }
   }
   const int found = wcount < kDecOutPre ? wcount : kDecOutPre;
-  // More than kDecOutPre outlier columns in the chunk (rare): their columns are
-  // found by rank from the per-step masks, kept in scalar registers, and their
-  // values are read kDecOutBatch columns per memory round trip.
+  // Beyond kDecOutPre + kDecOutDma columns (rare) the columns are found by rank
+  // from the per-step masks and their values read kDecOutBatch columns per
+  // memory round trip.
   constexpr int kDecOutBatch = 8;
-  uint64_t msk[KS];
-#pragma unroll
-  for (int t = 0; t < KS; ++t) msk[t] = 0;
-  if (wcount > kDecOutPre) {
-#pragma unroll
-    for (int t = 0; t < KS; ++t) msk[t] = step_mask(t);
-  }
   // column of the r-th outlier of this chunk, ascending (uniform), -1 past the last
   auto nth_outlier = [&](int r) -> int {
     int k = -1;
@@ -348,8 +412,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   } else {
     rm = rmv[0] > rmv[1] ? rmv[0] : rmv[1];
   }
+  // over the slots (DPP rotations inside a 16-lane row: lanes lr, lr + MR, ...
+  // hold the same row), then over the column groups
+  rm = max_rows<MR>(rm);
+  if constexpr (ZP) rn = min_rows<MR>(rn);
 #pragma unroll
-  for (int off = MR; off < 64; off <<= 1) {   // over the slots, then the column groups
+  for (int off = 16; off < 64; off <<= 1) {
     const uint32_t o = __shfl_xor(rm, off, 64);
     rm = o > rm ? o : rm;
     if constexpr (ZP) {
@@ -357,6 +425,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
       rn = o2 < rn ? o2 : rn;
     }
   }
+
   // the rest of the weight stream goes out before the barrier: a wave waiting
   // there for the slowest wave of its workgroup keeps its loads in flight
   load_b(kPre, kLoads);
@@ -424,9 +493,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
       if (qq == 0) {
         a[t] = cj;
       } else {
-        const int src = (lane & ~15) | ((lr + qq * MR) & 15);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[t][i] = __shfl(cj[i], src, 64);
+        for (int i = 0; i < 4; ++i) a[t][i] = (int)row_up((uint32_t)cj[i], qq * MR);
       }
       if (R > 1 && lr >= MR) a[t] = v4i{0, 0, 0, 0};
       // codes also go to LDS (all workgroups: no branch near the loads); workgroup
@@ -445,7 +513,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   if (wcount > kDecOutPre) {   // uniform
 #pragma unroll
     for (int u = 0; u < kDecOutDma; ++u) {
-      kx[u] = nth_outlier(kDecOutPre + u);
+      kx[u] = ko[kDecOutPre + u];
       if (kx[u] >= 0) {
         // X[lane][k]: lanes >= M read 0 from the range check
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, I8L_DEC_LDS(&sOx[wave][u][0]), 2,
@@ -493,23 +561,38 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
               dequant_w16((int)(int8_t)(sOw[wave][kDecOutPre + u][lane] & 0xffu), swl);
     }
     const int jb = 4 * g;   // this lane's first column
-    uint32_t ax[4];
+    // every operand value is read unconditionally and pinned in a register
+    // (so the compiler cannot sink the reads into branches, one LDS round
+    // trip each); the columns past the list are masked afterwards
+    uint32_t xv0[4], xv1[4], bw[kDecP][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // column i (registers, lane = row) for lanes 0-15, column 4 + i (LDS) for 16-31
-      const uint32_t xr0 = (uint32_t)__shfl((int)xo[i], lr, 64);
-      const uint32_t xr1 = sOx[wave][i][lr];
-      ax[i] = jb + i < nv ? (g == 0 ? xr0 : xr1) & 0xffffu : 0u;
+      xv0[i] = (uint32_t)__shfl((int)xo[i], lr, 64);   // column i, lanes 0-15
+      xv1[i] = sOx[wave][i][lr];                        // column 4 + i, lanes 16-31
     }
+#pragma unroll
+    for (int c = 0; c < kDecP; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bw[c][i] = sOw[wave][(jb + i) & (kDecOutMfma - 1)][c * 16 + lr];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(xv0[i]), "+v"(xv1[i]));
+#pragma unroll
+    for (int c = 0; c < kDecP; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(bw[c][i]));
+    uint32_t keep[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) keep[i] = jb + i < nv ? 0xffffu : 0u;
+    uint32_t ax[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ax[i] = (g == 0 ? xv0[i] : xv1[i]) & keep[i];
     const v4h av = __builtin_bit_cast(v4h, v2i{(int)(ax[0] | (ax[1] << 16)), (int)(ax[2] | (ax[3] << 16))});
     v4f po[kDecP];
 #pragma unroll
     for (int c = 0; c < kDecP; ++c) {
-      uint32_t bw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        bw[i] = jb + i < nv ? sOw[wave][(jb + i) & (kDecOutMfma - 1)][c * 16 + lr] & 0xffffu : 0u;
-      const v4h bv = __builtin_bit_cast(v4h, v2i{(int)(bw[0] | (bw[1] << 16)), (int)(bw[2] | (bw[3] << 16))});
+      const v4h bv = __builtin_bit_cast(
+          v4h, v2i{(int)((bw[c][0] & keep[0]) | ((bw[c][1] & keep[1]) << 16)),
+                   (int)((bw[c][2] & keep[2]) | ((bw[c][3] & keep[3]) << 16))});
       po[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
     }
 #pragma unroll
