@@ -297,21 +297,37 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     hm[j] = 0;
     if (__ballot(lmax >= T) != 0) {
       // a column is an outlier when some entry has |x| >= T; a NaN (pattern
-      // above 0x7c00) never does
+      // above 0x7c00) never does.  Per pair of magnitude patterns m (packed
+      // u16): with d = m - T (mod 2^16) and L = 0x7c01 - T, min(d, L) - L has
+      // its top bit set exactly when T <= m <= 0x7c00.
+      const u16x2 tt = {(unsigned short)T, (unsigned short)T};
+      const u16x2 ll = {(unsigned short)(0x7c01u - T), (unsigned short)(0x7c01u - T)};
+      uint32_t fl[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const u16x2 m = __builtin_bit_cast(u16x2, (uint32_t)xr[j][i >> 2][i & 3] & 0x7fff7fffu);
+        fl[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(m - tt, ll) - ll);
+      }
+      // the 16 flags (bits 15 and 31 of each pair) into bits 0..15: the four
+      // flag bytes of two pairs side by side (byte permute), then their top
+      // bits (7, 15, 23, 31) gathered into bits 28..31 by one multiplication
+      // (the partial products land on distinct bits: no carries)
       uint32_t h = 0;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t b = habs_bits(half_at(xr[j], e));
-        h |= (b >= T && b <= 0x7c00u ? 1u : 0u) << e;
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t p = __builtin_amdgcn_perm(fl[2 * k + 1], fl[2 * k], 0x07050301u) & 0x80808080u;
+        h |= ((p * 0x00204081u) >> 28) << (4 * k);
       }
       h = or_slot<MR>(h);
       hm[j] = h;
       smax = u16x2{0, 0};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t b0 = (h >> (2 * i)) & 1u, b1 = (h >> (2 * i + 1)) & 1u;
-        const uint32_t keep = ((b0 - 1u) & 0xffffu) | ((b1 - 1u) << 16);
-        xr[j][i >> 2][i & 3] &= (int)keep;
+        // 0xffff over each outlier half of the pair (its flag bit sign-extended)
+        const uint32_t z0 = (uint32_t)((int)(h << (31 - 2 * i)) >> 31);
+        const uint32_t z1 = (uint32_t)((int)(h << (30 - 2 * i)) >> 31);
+        const uint32_t z = __builtin_amdgcn_perm(z1, z0, 0x05040100u);
+        xr[j][i >> 2][i & 3] &= (int)~z;
         smax = __builtin_elementwise_max(
             smax, __builtin_bit_cast(u16x2, (uint32_t)xr[j][i >> 2][i & 3] & 0x7fff7fffu));
       }
@@ -937,7 +953,7 @@ kfn fused_decode_kernel(int M, int K) {
   int r = 1;   // k-steps packed per register set: M <= 16 / r, r <= ks
   while (r < ks && M <= 16 / (2 * r)) r *= 2;
   kfn f = nullptr;
-#define I8L_DEC(KS_, R_) if (ks == KS_ && r == R_) f = decode_kernel<KS_, R_, 4, ZP>;
+#define I8L_DEC(KS_, R_) if (ks == KS_ && r == R_) f = decode_kernel<KS_, R_, 8, ZP>;
   I8L_DEC(1, 1) I8L_DEC(2, 1) I8L_DEC(2, 2) I8L_DEC(4, 1) I8L_DEC(4, 2) I8L_DEC(4, 4)
   I8L_DEC(8, 1) I8L_DEC(8, 2) I8L_DEC(8, 4) I8L_DEC(8, 8)
 #undef I8L_DEC
