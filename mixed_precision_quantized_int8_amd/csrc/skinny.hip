@@ -96,8 +96,14 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_skinny_kernel(GemmArgs a) {
   const uint32_t rowB = (uint32_t)(min(rowb, lastB) * K);
   const int8_t* tileA = a.Xq + (size_t)m0 * K;
   const int8_t* tileB = a.Wq + (size_t)n0 * K;
+  // The K loop starts at a step rotated by the workgroup's place on its XCD
+  // (workgroup b runs on XCD b % 8): the XCD's compute units then read
+  // different steps of the activation codes at any time instead of the same
+  // lines at once.  Integer sums: the order does not change the result.
+  const int rot = (int)((long long)(blockIdx.x >> 3) * nk / 32 % nk);
   auto load_step = [&](int kt) {   // kt may run past the end: clamped to the last step
-    const int ks = min(kt, nk - 1), sl = kt % kSStages;
+    const int kc = min(kt, nk - 1) + rot, sl = kt % kSStages;
+    const int ks = kc < nk ? kc : kc - nk;
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int kk = ks * kSBK + cofA[i];
