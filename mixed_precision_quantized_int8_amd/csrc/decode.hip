@@ -803,7 +803,35 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
         for (int g = 0; g < MG; ++g)
           acc[g][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[g][u], fb[b][u][c], acc[g][c], 0, 0, 0);
   };
+  // Epilogue operands: the outlier count and the first kDecOutReg indices
+  // (scalars) now; the outlier weight values of this wave's epilogue features
+  // and the first X_O values of the LDS copy are loaded right behind the last
+  // weight loads, so that they land with them instead of one memory round
+  // trip after the stream.
+  // (The scalar loads go out after the first weight loads and are read
+  // unconditionally, K >= kDecOutReg entries: no wait for the count holds up
+  // the stream.)
+  const int c = wave & (kDecP - 1);
+  const int n = n0 + c * 16 + lr;
+  int nout, nl, oidx[kDecOutReg];
+  uint32_t wraw[kDecOutReg];   // fp16 weight value, or the code (W_rows NULL)
+  uint32_t xraw = 0;           // X_O element t of the LDS copy (row t / nl, column t % nl)
+  auto load_epi = [&]() {
+#pragma unroll
+    for (int j = 0; j < kDecOutReg; ++j) {
+      wraw[j] = 0;
+      if (j < nout && n < N)
+        wraw[j] = d.W_rows ? (uint32_t)d.W_rows[(size_t)oidx[j] * N + n]
+                           : (uint32_t)(uint8_t)d.Wq[(size_t)n * K + oidx[j]];
+    }
+    if (t < nl * M) xraw = d.X_O[(size_t)(t / nl) * K + t % nl];
+  };
   load_b(0, s0);
+  __builtin_amdgcn_sched_barrier(0);
+  nout = *d.n_out;
+  nl = min(nout, kDecMaxOutLds);
+#pragma unroll
+  for (int j = 0; j < kDecOutReg; ++j) oidx[j] = d.idx[j];
   int s = s0;
   for (; s + 2 * KU < s1; s += 2 * KU) {
     v4i fa0[MG][KU], fa1[MG][KU];
@@ -832,22 +860,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
     mma(0, fa0);
     __builtin_amdgcn_sched_barrier(0);
     load_a(s + KU, fa1);
+    load_epi();
     __builtin_amdgcn_sched_barrier(0);
     mma(1, fa1);
     __builtin_amdgcn_sched_barrier(0);
   } else {
     v4i fa0[MG][KU];
     load_a(s, fa0);
+    load_epi();
     __builtin_amdgcn_sched_barrier(0);
     mma(0, fa0);
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  const int nout = *d.n_out;
   // every wave finishes features c * 16 + lr of its block (c = wave % 4), for
   // row groups wave / 4, wave / 4 + 2, ...
-  const int c = wave & (kDecP - 1);
-  const int n = n0 + c * 16 + lr;
   // outlier weight value: the fp16 row, or rebuilt from the code (W_rows NULL)
   const float swn_raw = d.sw[n < N ? n : N - 1];
   auto wval = [&](int k) -> float {
@@ -856,9 +883,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
   };
   float wo[kDecOutReg];
 #pragma unroll
-  for (int j = 0; j < kDecOutReg; ++j) wo[j] = (j < nout && n < N) ? wval(d.idx[j]) : 0.0f;
-  const int nl = min(nout, kDecMaxOutLds);
-  for (int e = t; e < nl * M; e += kDecThreads) {
+  for (int j = 0; j < kDecOutReg; ++j)
+    wo[j] = j < nout && n < N ? (d.W_rows ? h2f((uint16_t)wraw[j])
+                                          : h2f(dequant_w16((int8_t)(uint8_t)wraw[j], swn_raw)))
+                              : 0.0f;
+  if (t < nl * M) sXO[t / nl][t % nl] = h2f((uint16_t)xraw);
+  for (int e = t + kDecThreads; e < nl * M; e += kDecThreads) {   // beyond the first 512 (rare)
     const int m = e / nl, j = e % nl;
     sXO[m][j] = h2f(d.X_O[(size_t)m * K + j]);
   }
