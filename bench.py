@@ -57,7 +57,7 @@ DECODE_STEPS, DECODE_WARMUP = 200, 20
 # kernel sources it was measured on (sha256 of the listed files).
 TRAFFIC = {
     ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 6731347104, "src": "4464f0fddb958b4a"},
-    ("decode_kernel", "decode"): {"bytes": 68534577, "src": "00f2fed7b24adf76"},
+    ("decode_kernel", "decode"): {"bytes": 68463165, "src": "bf78f4288aa5c646"},
 }
 
 
