@@ -215,7 +215,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   __shared__ int sCnt[kDecWaves];                   // outliers per K chunk
   __shared__ int sHasOut[kDecWaves];
   __shared__ float sSx[16];
-  __shared__ v4i sQ[16][KS * kDecWaves * 4 + 4];    // codes [m][16-byte chunk] + spare
   // outlier columns kDecOutPre .. kDecOutPre + kDecOutDma - 1 of each wave:
   // weight values (lane = feature: the fp16 weight, or the code when no fp16
   // weight is kept; slots kDecOutPre ..) and X values (lane = row), written by
@@ -513,10 +512,37 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
         for (int i = 0; i < 4; ++i) a[t][i] = (int)row_up((uint32_t)cj[i], qq * MR);
       }
       if (R > 1 && lr >= MR) a[t] = v4i{0, 0, 0, 0};
-      // codes also go to LDS (all workgroups: no branch near the loads); workgroup
-      // 0 copies them to the workspace at the end (steps past this wave's chunk
-      // land in a spare slot, not the next chunk's)
-      sQ[lr][s0 + t < s1 ? (s0 + t) * 4 + g : KS * kDecWaves * 4 + g] = a[t];
+    }
+  }
+  // ---- workspace intermediates (workgroup 0), behind the weight loads ------------
+  // Written now rather than after the products, so that workgroup 0 does not end
+  // last: the codes from registers (lane: row lr, 16 columns of k-step s0 + t),
+  // the first kDecOutPre outlier columns of this chunk at their rank, and the row
+  // scales, zero points and outlier count.  The LDS-fetched and further columns
+  // (many outliers only) are written after the products.
+  if (blockIdx.x == 0) {   // uniform
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const int k = (s0 + t) * 64 + 16 * g;
+      if (lr < M && s0 + t < s1 && k < K) *reinterpret_cast<v4i*>(d.Xq + (size_t)lr * K + k) = a[t];
+    }
+    int rank = 0;
+    for (int w = 0; w < kc; ++w) rank += sCnt[w];
+#pragma unroll
+    for (int j = 0; j < kDecOutPre; ++j) {
+      if (j < found) {
+        if (lane == 0) d.idx[rank + j] = ko[j];
+        if (lane < M) d.X_O[(size_t)lane * K + rank + j] = xo[j];
+      }
+    }
+    if (wave == 0) {   // lane = row for lanes < M (M <= 16 / R)
+      if (lane < M) d.sx[lane] = rowscale;
+      if (ZP && lane < M) d.zp[lane] = zpv;
+      if (lane == 0) {
+        int tot = 0;
+        for (int w = 0; w < kDecWaves; ++w) tot += sCnt[w];
+        *d.n_out = tot;
+      }
     }
   }
   // The further outlier columns follow the stream into LDS: issued behind this
@@ -655,31 +681,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   for (int c = 0; c < kDecP; ++c) sRed[wave][c][lane] = acc[c];
   lds_sync();
 
-  // ---- workspace intermediates (workgroup 0) ----------------------------------------
-  if (blockIdx.x == 0) {
-    // codes: Xq[m][k] for the k-steps of this wave's chunk
-    for (int i = lane; i < M * (s1 - s0) * 4; i += 64) {
-      const int m = i / ((s1 - s0) * 4), q = (s0 * 4) + i % ((s1 - s0) * 4);
-      if (q * 16 < K) *reinterpret_cast<v4i*>(d.Xq + (size_t)m * K + q * 16) = sQ[m][q];
-    }
+  // ---- workspace intermediates of the further outlier columns (workgroup 0) --------
+  if (blockIdx.x == 0 && wcount > kDecOutPre) {   // uniform
     int rank = 0;
     for (int w = 0; w < kc; ++w) rank += sCnt[w];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int j = 0; j < kDecOutPre; ++j) {
-      if (j < found) {
-        if (lane == 0) d.idx[rank + j] = ko[j];
-        if (lane < M) d.X_O[(size_t)lane * K + rank + j] = xo[j];
-      }
-    }
-    if (wcount > kDecOutPre) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int u = 0; u < kDecOutDma; ++u) {
-        if (kx[u] >= 0) {
-          if (lane == 0) d.idx[rank + kDecOutPre + u] = kx[u];
-          if (lane < M)
-            d.X_O[(size_t)lane * K + rank + kDecOutPre + u] = (uint16_t)(sOx[wave][u][lane] & 0xffffu);
-        }
+    for (int u = 0; u < kDecOutDma; ++u) {
+      if (kx[u] >= 0) {
+        if (lane == 0) d.idx[rank + kDecOutPre + u] = kx[u];
+        if (lane < M)
+          d.X_O[(size_t)lane * K + rank + kDecOutPre + u] = (uint16_t)(sOx[wave][u][lane] & 0xffffu);
       }
     }
     for (int j0 = kDecOutPre + kDecOutDma; j0 < wcount; j0 += kDecOutBatch) {   // uniform, batched as above
@@ -696,15 +708,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
           if (lane == 0) d.idx[rank + j0 + u] = kk[u];
           if (lane < M) d.X_O[(size_t)lane * K + rank + j0 + u] = xv[u];
         }
-      }
-    }
-    if (wave == 0) {
-      if (lane < M) d.sx[lane] = sSx[lane];
-      if (ZP && lane < M) d.zp[lane] = sZp[lane];
-      if (lane == 0) {
-        int tot = 0;
-        for (int w = 0; w < kDecWaves; ++w) tot += sCnt[w];
-        *d.n_out = tot;
       }
     }
   }
