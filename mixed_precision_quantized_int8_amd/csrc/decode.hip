@@ -208,12 +208,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   constexpr int MR = 16 / R;         // X rows per slot
   constexpr int NSET = KS / R;       // register sets
   __shared__ v4i sRed[kDecWaves][kDecP][64];        // int32 partials, D layout
-  __shared__ float sYo[kDecWaves][16][kDecCols];    // fp32 outlier partials [m][col]
+  // fp32 outlier partials [col][m] (zero for a wave without outlier columns):
+  // the epilogue reads a lane's four rows with one 16-byte read per wave
+  __shared__ v4f sYo[kDecWaves][kDecCols][4];
   __shared__ uint32_t sRowMax[kDecWaves][16];       // per chunk, per row
   __shared__ uint32_t sRowMin[ZP ? kDecWaves : 1][16];   // zero-point mode: minimum key
   __shared__ int sZp[16];
   __shared__ int sCnt[kDecWaves];                   // outliers per K chunk
-  __shared__ int sHasOut[kDecWaves];
   __shared__ float sSx[16];
   // outlier columns kDecOutPre .. kDecOutPre + kDecOutDma - 1 of each wave:
   // weight values (lane = feature: the fp16 weight, or the code when no fp16
@@ -638,9 +639,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
       po[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
     }
 #pragma unroll
-    for (int c = 0; c < kDecP; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sYo[wave][4 * g + r][c * 16 + lr] = po[c][r];
+    for (int c = 0; c < kDecP; ++c) sYo[wave][c * 16 + lr][g] = po[c];   // rows 4g .. 4g+3
     // the rest (beyond kDecOutMfma, rare), straight from memory on the vector
     // units (lane = feature n0 + lane): all loads of a batch go out before any
     // of their values is used
@@ -671,10 +670,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
             if (m < M) yo[m] += h2f((uint16_t)__builtin_amdgcn_readlane(xv[u], m)) * wv[u];
       }
 #pragma unroll
-      for (int m = 0; m < 16; ++m) sYo[wave][m][lane] += yo[m];
+      for (int i = 0; i < 4; ++i)
+        sYo[wave][lane][i] += v4f{yo[4 * i], yo[4 * i + 1], yo[4 * i + 2], yo[4 * i + 3]};
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sYo[wave][lane][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  if (lane == 0) sHasOut[wave] = wcount > 0;
 
   // ---- sum the partials of the 8 waves ------------------------------------------------
 #pragma unroll
@@ -715,16 +717,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   if (wave >= kDecP) return;
   const int c = wave;
   v4i tot = {0, 0, 0, 0};
-  float yo4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  v4f yo4 = {0.0f, 0.0f, 0.0f, 0.0f};
   const int mb = g * 4;   // D rows of this lane: mb .. mb + 3
 #pragma unroll
   for (int w = 0; w < kDecWaves; ++w) {
     const v4i p = sRed[w][c][lane];
     tot[0] += p[0]; tot[1] += p[1]; tot[2] += p[2]; tot[3] += p[3];
-    if (sHasOut[w]) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) yo4[r] += sYo[w][mb + r][c * 16 + lr];
-    }
+    yo4 += sYo[w][c * 16 + lr][g];
   }
 
   // ---- epilogue ----------------------------------------------------------------------
