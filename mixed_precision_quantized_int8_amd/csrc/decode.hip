@@ -213,9 +213,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   __shared__ v4f sYo[kDecWaves][kDecCols][4];
   __shared__ uint32_t sRowMax[kDecWaves][16];       // per chunk, per row
   __shared__ uint32_t sRowMin[ZP ? kDecWaves : 1][16];   // zero-point mode: minimum key
-  __shared__ int sZp[16];
   __shared__ int sCnt[kDecWaves];                   // outliers per K chunk
-  __shared__ float sSx[16];
   // outlier columns kDecOutPre .. kDecOutPre + kDecOutDma - 1 of each wave:
   // weight values (lane = feature: the fp16 weight, or the code when no fp16
   // weight is kept; slots kDecOutPre ..) and X values (lane = row), written by
@@ -478,11 +476,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
     rowscale = h2f((uint16_t)mx);
     inv65 = quant_scale(rowscale) * 65536.0f;
   }
-  if (wave == 0 && lane < 16) {
-    sSx[lane] = lane < MR ? rowscale : 0.0f;
-    sZp[lane] = lane < MR ? zpv : 0;
-  }
   const int zpc = 0x8000 + (zpv - 128) * 65536;   // zero-point codes: see codes16_zp
+  // the row scales (and zero points) of this lane's epilogue rows 4 g .. 4 g + 3,
+  // from the lanes that hold those rows (lane m holds row m for m < M), now
+  // rather than from LDS in the tail
+  float sxe[4];
+  int zpe[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sxe[r] = __shfl(rowscale, 4 * g + r, 64);
+    zpe[r] = ZP ? __shfl(zpv, 4 * g + r, 64) : 0;
+  }
   v4i acc[kDecP];
 #pragma unroll
   for (int c = 0; c < kDecP; ++c) acc[c] = v4i{0, 0, 0, 0};
@@ -733,12 +737,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs d) {
   if constexpr (ZP) {   // sum (q - zp) w = sum (q - 128) w + (128 - zp) S[n], mod 2^32
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (mb + r < M) tot[r] = (int)((uint32_t)tot[r] + (uint32_t)(128 - sZp[mb + r]) * (uint32_t)wsn);
+      if (mb + r < M) tot[r] = (int)((uint32_t)tot[r] + (uint32_t)(128 - zpe[r]) * (uint32_t)wsn);
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = mb + r;
-    if (m < M) d.Y[(size_t)m * N + n] = f2h((float)tot[r] * (sSx[m] * swn) + yo4[r] + h2f(bvb));
+    if (m < M) d.Y[(size_t)m * N + n] = f2h((float)tot[r] * (sxe[r] * swn) + yo4[r] + h2f(bvb));
   }
 }
 
