@@ -56,8 +56,8 @@ DECODE_STEPS, DECODE_WARMUP = 200, 20
 # factor (profiles/traffic-mlp_down_prefill_and_decode.md); valid only for the
 # kernel sources it was measured on (sha256 of the listed files).
 TRAFFIC = {
-    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 6731347104, "src": "4464f0fddb958b4a"},
-    ("decode_kernel", "decode"): {"bytes": 68463165, "src": "bf78f4288aa5c646"},
+    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 6731175776, "src": "4464f0fddb958b4a"},
+    ("decode_kernel", "decode"): {"bytes": 68493233, "src": "3d2a5c2aa0bdac72"},
 }
 
 
