@@ -822,6 +822,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
   int nout, nl, oidx[kDecOutReg];
   uint32_t wraw[kDecOutReg];   // fp16 weight value, or the code (W_rows NULL)
   uint32_t xraw = 0;           // X_O element t of the LDS copy (row t / nl, column t % nl)
+  // row scales and zero points of this lane's epilogue rows (row groups
+  // wave / 4 and wave / 4 + 2), the bias and the weight code sum of its feature
+  constexpr int GE = (MG + 1) / 2;   // row groups per wave in the epilogue
+  float sxr[GE][4];
+  int zpr[GE][4];
+  uint32_t braw = 0, wsraw = 0;
   auto load_epi = [&]() {
 #pragma unroll
     for (int j = 0; j < kDecOutReg; ++j) {
@@ -831,6 +837,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
                            : (uint32_t)(uint8_t)d.Wq[(size_t)n * K + oidx[j]];
     }
     if (t < nl * M) xraw = d.X_O[(size_t)(t / nl) * K + t % nl];
+#pragma unroll
+    for (int gi = 0; gi < GE; ++gi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * (wave / kDecP + 2 * gi) + (lane >> 4) * 4 + r;
+        sxr[gi][r] = m < M ? d.sx[m] : 0.0f;
+        zpr[gi][r] = d.zp && m < M ? d.zp[m] : 0;
+      }
+    if (n < N) {
+      if (d.bias) braw = d.bias[n];
+      if (d.zp) wsraw = (uint32_t)d.wsum[n];
+    }
   };
   load_b(0, s0);
   __builtin_amdgcn_sched_barrier(0);
@@ -905,9 +923,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
   lds_sync();
   if (n >= N) return;
   const float swn = swn_raw * (d.zp ? 1.0f / 127.0f : 1.0f / 16129.0f);
-  const float bv = d.bias ? h2f(d.bias[n]) : 0.0f;
-  const uint32_t wsv = d.zp ? (uint32_t)d.wsum[n] : 0u;
-  for (int g = wave / kDecP; g < MG; g += kDecWaves / kDecP) {   // uniform per wave
+  const float bv = d.bias ? h2f((uint16_t)braw) : 0.0f;
+  const uint32_t wsv = wsraw;
+#pragma unroll
+  for (int gi = 0; gi < GE; ++gi) {   // row group g = wave / 4 + 2 gi (uniform per wave)
+    const int g = wave / kDecP + 2 * gi;
+    if (g >= MG) continue;
     const int mb = 16 * g + (lane >> 4) * 4;   // D rows of this lane: mb .. mb + 3
     if (mb >= M) continue;
     v4i tot = {0, 0, 0, 0};
@@ -919,13 +940,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_stream_kernel(DecodeArgs d
     if (d.zp) {   // sum (q - zp) w = sum (q - 128) w + (128 - zp) S[n], mod 2^32
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (mb + r < M) tot[r] = (int)((uint32_t)tot[r] + (uint32_t)(128 - d.zp[mb + r]) * wsv);
+        if (mb + r < M) tot[r] = (int)((uint32_t)tot[r] + (uint32_t)(128 - zpr[gi][r]) * wsv);
     }
     float y[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = mb + r;
-      y[r] = m < M ? (float)tot[r] * (d.sx[m] * swn) : 0.0f;
+      y[r] = m < M ? (float)tot[r] * (sxr[gi][r] * swn) : 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < kDecOutReg; ++j)
