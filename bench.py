@@ -57,7 +57,7 @@ DECODE_STEPS, DECODE_WARMUP = 200, 20
 # kernel sources it was measured on (sha256 of the listed files).
 TRAFFIC = {
     ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 6731175776, "src": "4464f0fddb958b4a"},
-    ("decode_kernel", "decode"): {"bytes": 68493233, "src": "3d2a5c2aa0bdac72"},
+    ("decode_kernel", "decode"): {"bytes": 68493233, "src": "0cc9611719cb8aeb"},
 }
 
 

@@ -11,25 +11,26 @@
 // the operand layout of v_mfma_i32_16x16x64_i8 (lane = row lr, 16-column
 // group g).  Consequences:
 //   * the outlier test of a column needs only the wave's own registers: an OR
-//     of hit masks over the 16 lanes of a column group;
+//     of hit masks over the lanes of a row slot (DPP moves, no LDS);
 //   * the row absmax over the regular columns is the only workgroup-wide
 //     dependency: one LDS exchange and one barrier;
 //   * the codes are computed in registers, already in MFMA operand layout;
-//   * each wave adds the fp16 product of its own outlier columns (weight rows
-//     of up to four columns loaded as soon as the columns are known, long
-//     before they are needed; a fifth and later ones are read at the end);
+//   * each wave adds the fp16 product of its own outlier columns on the matrix
+//     cores (up to eight: the first four loaded into registers as soon as the
+//     columns are known, the next four fetched into LDS behind the weight
+//     stream; any further ones are read at the end);
 //   * a second barrier sums the 8 waves' int32 partials (exact) and fp32
 //     outlier partials, then the epilogue dequantizes and stores fp16.
 // The weight is streamed with 16-byte buffer loads (default cache policy:
 // measured faster here than the nontemporal hint), one 16-feature block after
 // the other, all k-steps of a block back to back (~8 % more bandwidth than
-// k-step by k-step across the blocks); the first PRE (4) loads of a wave are
+// k-step by k-step across the blocks); the first PRE (8) loads of a wave are
 // issued before the activation stage and the rest as soon as the wave's own
 // row reduction is done, before the workgroup barrier.
 // The K chunk a wave streams is rotated by the workgroup index (measured ~15%
 // more HBM bandwidth than all starting at chunk 0).
 // Workgroup 0 also writes the intermediates (Xq, sx, outlier list, X_O) to the
-// workspace.
+// workspace, right after its codes (behind its weight loads).
 //
 // Stream kernel (K > 4096): reads the intermediates written by the activation
 // kernels and does the product and epilogue the same way, with the weight
