@@ -234,6 +234,10 @@ def _linear_cases():
     yield "decode_m16_300_outliers", 16, 4096, 320, 300, 6.0, 1.0
     yield "decode_m1_100_outliers", 1, 512, 200, 100, 6.0, 1.0
     yield "decode_m8_41_outliers", 8, 4096, 520, 41, 6.0, 1.0
+    # many outlier columns per wave with 4 and 8 k-steps packed per register set
+    yield "decode_m4_70_outliers", 4, 4096, 520, 70, 6.0, 1.0
+    yield "decode_m2_60_outliers", 2, 4096, 300, 60, 6.0, 1.0
+    yield "decode_m3_k2048_40_outliers", 3, 2048, 260, 40, 6.0, 1.0
     yield "prefill_m17", 17, 1024, 600, 2, 6.0, 1.0
     # 64 < M <= 256: the 256 x 64 tiles (one or two outlier staging rounds,
     # ragged N with element stores)
@@ -506,6 +510,7 @@ def test_linear_split_tail_sampled(lib):
     ("decode_m1", 1, 1040, 300, 2),
     ("decode_many", 4, 1024, 130, 9),        # more outliers than a wave preloads
     ("decode_many_lds", 8, 1024, 520, 60),   # columns 5-8 of a wave fetched into LDS, and beyond
+    ("decode_m2_many", 2, 4096, 300, 60),    # 8 k-steps per register set
     ("decode_bigk", 8, 16384, 256, 4),       # activation kernels + streaming kernel
     ("stream_m32", 32, 4096, 520, 3),        # streaming kernel, 2 row groups
     ("stream_m64_many", 64, 1024, 200, 70),  # 4 row groups, outliers past the LDS copy

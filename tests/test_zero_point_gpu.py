@@ -161,6 +161,8 @@ def _linear_cases():
     # the fused kernel with up to and beyond eight outlier columns per wave
     yield "decode_many_outliers", 8, 2048, 520, 50, 6.0, "offset", True, True
     yield "decode_many_outliers_rebuilt", 4, 1024, 200, 60, 6.0, "negative", False, False
+    yield "decode_m4_many_outliers", 4, 4096, 520, 70, 6.0, "offset", True, True
+    yield "decode_m2_many_outliers", 2, 4096, 300, 60, 6.0, "positive", False, True
     yield "stream_m17_bias", 17, 1024, 600, 2, 6.0, "offset", True, True
     yield "stream_m40_k4112", 40, 4112, 300, 3, 6.0, "negative", False, False
     yield "stream_m64", 64, 2048, 520, 4, 6.0, "positive", True, True
