@@ -22,7 +22,10 @@ gradients dX, dW and dbias), whose fp16 GEMMs are priced against the fp16
 matrix-core peak (--no-train skips it).
 
 The K timed steps are captured into one HIP graph and replayed (--no-graph
-launches each step from Python instead).  To keep the 256 MB Infinity Cache
+launches each step from Python instead).  `value` is the whole call's rate;
+`roofline` prices the call's dominant kernel: for the GEMM paths, the call's
+time less that of its activation stage, which is timed alone (the same
+kernels, in a graph of its own, on the same inputs).  To keep the 256 MB Infinity Cache
 from serving the weight, steps rotate over several copies of (X, Wq, sw, W, Y,
 workspace) totalling more than 512 MB.
 
@@ -51,12 +54,13 @@ PEAK_INT8_TOPS = 5000.0
 # steps than the headline.
 DECODE_STEPS, DECODE_WARMUP = 200, 20
 
-# HBM traffic per call (every kernel of the timed unit) from rocprofv3
-# FETCH_SIZE / WRITE_SIZE counter runs, scaled by the copy-kernel calibration
-# factor (profiles/traffic-mlp_down_prefill_and_decode.md); valid only for the
-# kernel sources it was measured on (sha256 of the listed files).
+# HBM traffic per call of the priced kernel (the GEMM's three launches; the
+# fused decode kernel's one) from rocprofv3 FETCH_SIZE / WRITE_SIZE counter
+# runs, scaled by the copy-kernel calibration factor
+# (profiles/traffic-mlp_down_prefill_and_decode.md); valid only for the kernel
+# sources it was measured on (sha256 of the listed files).
 TRAFFIC = {
-    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 6731175776, "src": "4464f0fddb958b4a"},
+    ("gemm_i8_kernel", "mlp_down_prefill"): {"bytes": 5555913273, "src": "4464f0fddb958b4a"},
     ("decode_kernel", "decode"): {"bytes": 68493233, "src": "0cc9611719cb8aeb"},
 }
 
@@ -77,10 +81,13 @@ def algorithmic_bytes(w):
 
 def dominant_kernel(w):
     """The kernel that carries the call: the fused small-M kernel (M <= 16,
-    K <= 4096), the streaming kernel (M <= 64 otherwise) or the GEMM."""
+    K <= 4096), the streaming kernel (M <= 64 otherwise), the skinny GEMM
+    (M <= 256) or the GEMM."""
     if w.M <= 64:
         name = "decode_kernel" if w.M <= 16 and w.K <= 4096 else "decode_stream_kernel"
         return name, "hbm", ["decode.hip", "common.h"]
+    if w.M <= 256:
+        return "gemm_skinny_kernel", "mfma", ["skinny.hip", "act.hip", "common.h"]
     return "gemm_i8_kernel", "mfma", ["gemm.hip", "act.hip", "common.h"]
 
 
@@ -187,10 +194,11 @@ def copy_calibration(mib):
                       "copy_calibration_bytes_written": mib << 20, "launches": 3}))
 
 
-def time_steps(torch, step, K, graph):
+def time_steps(torch, step, K, graph, eager=True):
     """Time exactly K steps: captured once into a HIP graph and replayed
     (events around the replay), or launched eagerly with events per step.
-    Returns (ms per step, eager ms per step or None, per-step ms array or None)."""
+    Returns (ms per step, eager ms per step or None, per-step ms array or None);
+    eager=False skips the reference eager timing after a graph replay."""
     import numpy as np
     if graph:
         # The K steps are captured once into a HIP graph and replayed: the
@@ -217,6 +225,9 @@ def time_steps(torch, step, K, graph):
         t1.record()
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / K
+        if not eager:
+            del g
+            return ms, None, None
         # eager launches, for reference (Python launch path included)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -292,11 +303,23 @@ def measure(torch, pkg, workloads, w, args, steps, warmup, with_fp16_context):
         launch = ("one launch of decode_kernel per call" if kname == "decode_kernel" else
                   "activation kernels + decode_stream_kernel per call")
     else:
-        achieved = w.int_ops / (ms * 1e-3) / 1e12
+        # The GEMM's own launches: the call's time less that of its activation
+        # stage (flag clear, column scan, row quantization), which runs the very
+        # same kernels when timed alone, in a graph of its own, on the same
+        # rotated inputs and workspaces.
+        act_ms = activation_ms(torch, pkg, w, sets, R, steps, args)
+        kernel_ms = ms - act_ms
+        achieved = w.int_ops / (kernel_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
-                "unit": "TOPS", "frac": round(achieved / PEAK_INT8_TOPS, 4)}
-        launch = ("whole call: flag clear, colflags_kernel, rowquant_kernel, then "
-                  "gemm_i8_kernel whole tiles, split-K tail and fix-up")
+                "unit": "TOPS", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                "kernel_ms": round(kernel_ms, 5), "activation_ms": round(act_ms, 5)}
+        if kname == "gemm_skinny_kernel":
+            launch = ("gemm_skinny_kernel (one launch per call): the call's time less its "
+                      "activation stage timed alone")
+        else:
+            launch = ("gemm_i8_kernel whole tiles, split-K tail and fix-up: the call's time "
+                      "less its activation stage (flag clear, colflags_kernel, "
+                      "rowquant_kernel) timed alone")
     # counter figures were taken on the default layer (fp16 outlier rows, absmax codes)
     tr = None if (args.zero_point or args.rebuilt_rows or args.bias) else TRAFFIC.get((kname, w.name))
     roof["traffic"] = tr["bytes"] if tr and tr["src"] == src_hash else None
@@ -332,6 +355,24 @@ def measure(torch, pkg, workloads, w, args, steps, warmup, with_fp16_context):
     Y0, Wq0 = sets[0][5], sets[0][1]
     del sets, Xd, Wd
     return res, X, W, Y0, Wq0
+
+
+def activation_ms(torch, pkg, w, sets, R, K, args):
+    """Per-call time of the layer's activation stage alone (the kernels the call
+    runs before its GEMM), K calls over the same rotated buffer sets captured
+    into one HIP graph; the outputs go to buffers allocated once."""
+    import numpy as np
+    x0, ws0 = sets[0][0], sets[0][4]
+    if args.zero_point:
+        out = pkg.quantize_activation_zp(x0, w.threshold, workspace=ws0)
+        fn = lambda x, ws: pkg.quantize_activation_zp(x, w.threshold, workspace=ws, out=out)
+    else:
+        out = pkg.quantize_activation(x0, w.threshold, workspace=ws0)
+        fn = lambda x, ws: pkg.quantize_activation(x, w.threshold, workspace=ws, out=out)
+    ms, _, _ = time_steps(torch, lambda i: fn(sets[i % R][0], sets[i % R][4]), K,
+                          not args.no_graph, eager=False)
+    del out
+    return ms
 
 
 def graph_ms(torch, fn, K):

@@ -201,18 +201,34 @@ def workspace_views(workspace, M, K):
     }
 
 
-def quantize_activation(X, threshold=6.0, workspace=None):
+def _act_outputs(M, K, dev, out, zp):
+    """The activation stage's output tensors: ``out``'s (checked) or new ones."""
+    torch = _torch()
+    spec = [("Xq", (M, K), torch.int8)]
+    spec += [("zp", (M,), torch.int32), ("xscale", (M,), torch.float32)] if zp else \
+        [("sx", (M,), torch.float32)]
+    spec += [("idx", (K,), torch.int32), ("n_out", (1,), torch.int32),
+             ("X_O", (M, K), torch.float16)]
+    if out is None:
+        return {name: torch.empty(shape, dtype=dt, device=dev) for name, shape, dt in spec}
+    for name, shape, dt in spec:
+        t = out[name]
+        _require(t, dt, name)
+        if tuple(t.shape) != shape or t.device != dev:
+            raise ValueError(f"out[{name!r}] must be {shape} on {dev}")
+    return {name: out[name] for name, _, _ in spec}
+
+
+def quantize_activation(X, threshold=6.0, workspace=None, out=None):
     """Activation stage alone: dict of Xq [M][K], sx [M], idx [K] (first n_out
-    valid), n_out [1], X_O [M][K] (first n_out columns valid)."""
+    valid), n_out [1], X_O [M][K] (first n_out columns valid).  ``out``: a dict
+    of such tensors from an earlier call, written again instead of new ones."""
     torch = _torch()
     _require(X, torch.float16, "X")
     M, K = X.shape
     dev = X.device
-    Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
-    sx = torch.empty((M,), dtype=torch.float32, device=dev)
-    idx = torch.empty((K,), dtype=torch.int32, device=dev)
-    n_out = torch.empty((1,), dtype=torch.int32, device=dev)
-    X_O = torch.empty((M, K), dtype=torch.float16, device=dev)
+    o = _act_outputs(M, K, dev, out, zp=False)
+    Xq, sx, idx, n_out, X_O = o["Xq"], o["sx"], o["idx"], o["n_out"], o["X_O"]
     if workspace is None:
         workspace = new_workspace(M, K, 0, dev)
     else:
@@ -224,19 +240,17 @@ def quantize_activation(X, threshold=6.0, workspace=None):
     return {"Xq": Xq, "sx": sx, "idx": idx, "n_out": n_out, "X_O": X_O}
 
 
-def quantize_activation_zp(X, threshold=6.0, workspace=None):
+def quantize_activation_zp(X, threshold=6.0, workspace=None, out=None):
     """Zero-point activation stage alone: dict of Xq [M][K] (codes - 128), zp [M],
-    xscale [M], idx [K] (first n_out valid), n_out [1], X_O [M][K]."""
+    xscale [M], idx [K] (first n_out valid), n_out [1], X_O [M][K].  ``out``: a
+    dict of such tensors from an earlier call, written again instead of new ones."""
     torch = _torch()
     _require(X, torch.float16, "X")
     M, K = X.shape
     dev = X.device
-    Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
-    zp = torch.empty((M,), dtype=torch.int32, device=dev)
-    xscale = torch.empty((M,), dtype=torch.float32, device=dev)
-    idx = torch.empty((K,), dtype=torch.int32, device=dev)
-    n_out = torch.empty((1,), dtype=torch.int32, device=dev)
-    X_O = torch.empty((M, K), dtype=torch.float16, device=dev)
+    o = _act_outputs(M, K, dev, out, zp=True)
+    Xq, zp, xscale, idx, n_out, X_O = (o["Xq"], o["zp"], o["xscale"], o["idx"], o["n_out"],
+                                      o["X_O"])
     if workspace is None:
         workspace = new_workspace(M, K, 0, dev)
     else:

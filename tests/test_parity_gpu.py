@@ -180,6 +180,30 @@ def test_quantize_activation_reused_workspace(lib):
         np.testing.assert_array_equal(host(r["Xq"]), Xq_o, err_msg=name)
 
 
+def test_quantize_activation_reused_outputs(lib):
+    """The same output tensors written again by a second call (the `out`
+    argument): the second call's results, bit-exact, nothing left of the first
+    (its outlier set is larger), and an out tensor of the wrong shape raises."""
+    K = 1040
+    ws = lib.new_workspace(64, K, 0, torch.device("cuda:0"))
+    X1 = wl.make_x(40, K, 1.0, 60, 8, 20, 31)[0]
+    X2 = wl.make_x(40, K, 1.0, 3, 8, 20, 32)[0]
+    say(f"quantize_activation reused outputs M=40 K={K}")
+    out = lib.quantize_activation(dev(X1), 6.0, workspace=ws)
+    r = lib.quantize_activation(dev(X2), 6.0, workspace=ws, out=out)
+    assert all(r[k] is out[k] for k in out)
+    Xq_o, sx_o, idx_o, XO_o = O.quantize_activation(X2, 6.0)
+    n = int(host(r["n_out"])[0])
+    assert n == len(idx_o)
+    np.testing.assert_array_equal(host(r["idx"])[:n], idx_o)
+    np.testing.assert_array_equal(host(r["sx"]).view(np.uint32), sx_o.view(np.uint32))
+    np.testing.assert_array_equal(host(r["Xq"]), Xq_o)
+    np.testing.assert_array_equal(host(r["X_O"])[:, :n], XO_o)
+    bad = dict(out, sx=torch.empty(39, dtype=torch.float32, device="cuda:0"))
+    with pytest.raises(ValueError):
+        lib.quantize_activation(dev(X2), 6.0, workspace=ws, out=bad)
+
+
 # ---------------------------------------------------------------------------------
 # exact int8 GEMM (stage export)
 # ---------------------------------------------------------------------------------
