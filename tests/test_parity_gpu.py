@@ -230,6 +230,32 @@ def test_gemm_i32_extremes(lib):
     np.testing.assert_array_equal(host(acc), O.int8_matmul(Xq, Wq))
 
 
+# The largest K the library accepts, every code at +-127: the accumulators
+# reach +-127^2 * K = +-2147350544, just inside int32 (the bound that fixes
+# that K).  One row and one weight row of random codes catch misplaced
+# k-steps.  M = 8 and 100: 128-row skinny tiles; 200: 256-row skinny tiles;
+# 300: the 256 x 256 GEMM, whole tiles or (with a workspace) split along K.
+@pytest.mark.parametrize("M,N,split", [(8, 40, False), (100, 72, False), (200, 64, False),
+                                       (300, 64, False), (300, 64, True)])
+def test_gemm_i32_max_k(lib, M, N, split):
+    K = lib.MAX_K
+    say(f"gemm_i32 max K M={M} K={K} N={N} split={split}")
+    Xq = np.full((M, K), 127, np.int8)
+    Xq[1::2] = -127
+    Wq = np.full((N, K), 127, np.int8)
+    Wq[1::3] = -127
+    Wq[2::3, ::2] = -127
+    rng = np.random.default_rng(M + N)
+    Xq[-1] = rng.integers(-127, 128, K, dtype=np.int8)
+    Wq[-1] = rng.integers(-127, 128, K, dtype=np.int8)
+    ws = lib.new_workspace(M, K, N, torch.device("cuda:0")) if split else None
+    acc = host(lib.gemm_i32(dev(Xq), dev(Wq), workspace=ws))
+    np.testing.assert_array_equal(acc, O.int8_matmul(Xq, Wq))
+    assert acc[0, 0] == 127 * 127 * K == 2147350544
+    assert acc[1, 0] == -2147350544 and acc[0, 1] == -2147350544 and acc[1, 1] == 2147350544
+    assert acc[0, 2] == 0
+
+
 # ---------------------------------------------------------------------------------
 # the whole layer through int8_linear (small M: fused decode kernel; larger M: GEMM)
 # ---------------------------------------------------------------------------------
@@ -245,6 +271,10 @@ def _linear_cases():
     yield "decode_bigk_many_outliers", 3, 4112, 200, 90, 6.0, 1.0
     yield "decode_bigk_m16_ragged_n", 16, 6160, 777, 3, 6.0, 1.0
     yield "decode_bigk_m1", 1, 8192, 1000, 2, 6.0, 1.0
+    # the largest K the library accepts: small-M activation kernels and the
+    # streaming kernel; the 256 x 256 GEMM (two tiles, split along K)
+    yield "decode_max_k", 8, 133136, 300, 5, 6.0, 1.0
+    yield "prefill_max_k", 300, 133136, 64, 5, 6.0, 1.0
     # 17 <= M <= 64: activation kernels + the streaming kernel with 2 or 4 row groups
     yield "stream_m17", 17, 1024, 600, 2, 6.0, 1.0
     yield "stream_m24_k4112", 24, 4112, 300, 3, 6.0, 1.0
