@@ -9,13 +9,15 @@
 //
 // For M > 16, launches on the caller's stream:
 //   clear     zero the column bitmask (a fill kernel, safe under graph capture);
-//             only where several workgroups share a column (M > 64)
+//             only where several workgroups share a column (M > 256)
 //   colflags  one pass over X: per thread 16-byte loads, 8 running column
 //             maxima (NaN entries count as 0: a NaN never reaches the
 //             threshold); a set bit for every column whose maximum reaches the
 //             threshold (atomicOr, issued only for the rare outlier columns;
-//             for M <= 64, or with the threshold off, one workgroup holds
-//             every row of its columns and stores its flag words outright)
+//             with the threshold off, one workgroup holds every row of its
+//             columns and stores its flag words outright).  For M <= 256 the
+//             same test runs in colscan_strip_kernel: 64-column strips, each
+//             workgroup over every row, every flag word stored.
 //   rowquant  one workgroup per row: the bitmask and its prefix popcounts go
 //             to LDS, the row is held in registers while its absmax over the
 //             regular columns is reduced, then codes are written (8 bytes per
@@ -124,6 +126,82 @@ __global__ __launch_bounds__(kColThreads) void colflags_kernel(const uint16_t* _
     } else if (v) {
       atomicOr(flags + word, v);
     }
+  }
+}
+
+// Column scan for batches of up to 32 * RPT rows: one workgroup per strip of
+// 64 columns holds every row of it, so the strip's two flag words are complete
+// there and are stored outright (zeros included: no clear launch).  Thread t
+// reads columns 8 (t % 8) .. +7 of rows t / 8 + 32 i, i < RPT, all loads in
+// flight at once; rows past M and columns past K read 0 from the buffer
+// resource.  Narrow strips give K / 64 workgroups (64 for K = 4096), where the
+// 512-column strips of colflags_kernel give K / 512 with several round trips
+// each.  scan == 0 stores zeros without reading X.
+constexpr int kStripCols = 64;
+template <int RPT>
+__global__ __launch_bounds__(kColThreads) void colscan_strip_kernel(const uint16_t* __restrict__ X,
+                                                                    int M, int K, float threshold,
+                                                                    int scan,
+                                                                    uint32_t* __restrict__ flags) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int g = t & 7;
+  const int c = blockIdx.x * kStripCols + g * 8;
+  uint32_t mx[4] = {0, 0, 0, 0};   // packed pairs of |fp16| bit patterns
+  if (scan) {   // uniform
+    const buf_rsrc rx = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
+    v4i x[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = (t >> 3) + 32 * i;
+      x[i] = buf_load16(rx, r < M && c < K ? (uint32_t)(r * K + c) * 2u : kBufOff);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t v = habs2_nonan((uint32_t)x[i][j]);
+        const uint32_t lo = max(v & 0xffffu, mx[j] & 0xffffu);
+        const uint32_t hi = max(v >> 16, mx[j] >> 16);
+        mx[j] = lo | (hi << 16);
+      }
+    // the 8 row groups of the wave that share a column chunk (lane bits 3-5)
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)mx[j], off, 64);
+        const uint32_t lo = max(o & 0xffffu, mx[j] & 0xffffu);
+        const uint32_t hi = max(o >> 16, mx[j] >> 16);
+        mx[j] = lo | (hi << 16);
+      }
+  }
+  __shared__ uint32_t s_mx[kColThreads / 64][8][4];
+  __shared__ uint32_t s_byte[8];
+  if (lane < 8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_mx[wave][lane][j] = mx[j];
+  }
+  __syncthreads();
+  if (t < 8) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t h = 0;
+#pragma unroll
+      for (int w = 0; w < kColThreads / 64; ++w) {
+        const uint32_t v = (s_mx[w][t][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        h = v > h ? v : h;
+      }
+      if (scan && h2f((uint16_t)h) >= threshold) bits |= 1u << e;
+    }
+    s_byte[t] = bits;
+  }
+  __syncthreads();
+  if (t < kStripCols / 32) {
+    const uint32_t v = s_byte[4 * t] | (s_byte[4 * t + 1] << 8) | (s_byte[4 * t + 2] << 16) |
+                       (s_byte[4 * t + 3] << 24);
+    const int word = blockIdx.x * (kStripCols / 32) + t;
+    if (word < (K + 31) / 32) flags[word] = v;
   }
 }
 
@@ -582,7 +660,23 @@ hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float thr
     return hipGetLastError();
   }
   const int bx = (K + kColStrip - 1) / kColStrip;
-  if (!enabled || M <= kStreamMaxM) {
+  if (M <= 32 * 8) {
+    // narrow strips over every row: every flag word stored, so no clear launch
+    const dim3 grid((K + kStripCols - 1) / kStripCols), block(kColThreads);
+    const int sc = (int)enabled;
+    if (M <= 32)
+      hipLaunchKernelGGL(colscan_strip_kernel<1>, grid, block, 0, stream, X, M, K, threshold, sc,
+                         ws.flags);
+    else if (M <= 64)
+      hipLaunchKernelGGL(colscan_strip_kernel<2>, grid, block, 0, stream, X, M, K, threshold, sc,
+                         ws.flags);
+    else if (M <= 128)
+      hipLaunchKernelGGL(colscan_strip_kernel<4>, grid, block, 0, stream, X, M, K, threshold, sc,
+                         ws.flags);
+    else
+      hipLaunchKernelGGL(colscan_strip_kernel<8>, grid, block, 0, stream, X, M, K, threshold, sc,
+                         ws.flags);
+  } else if (!enabled) {
     // one row block: every flag word is stored, so no clear launch
     hipLaunchKernelGGL(colflags_kernel<true>, dim3(bx, 1), dim3(kColThreads), 0, stream, X, M, K,
                        M, threshold, (int)enabled, ws.flags);

@@ -133,6 +133,17 @@ def _act_cases():
     yield "small_all_outliers", X, c, 2.0 ** -24
     yield "small_disabled", *wl.make_x(10, 1040, 1.0, 3, 8, 20, 17), math.inf
     yield "rows64_wide_k", *wl.make_x(64, 24592, 1.0, 7, 8, 20, 18), 6.0   # 64-row slices
+    # 64-column strip scan, one launch shape per rows-per-thread count (up to 32,
+    # 64, 128, 256 rows): threshold edges in the last row block, a K that ends
+    # inside a strip (K % 64 == 16) and one on a strip edge
+    for M, K, seed in ((32, 1040, 19), (65, 4096, 20), (128, 1104, 21), (255, 2064, 22),
+                       (256, 4096, 23)):
+        X, c = wl.make_x(M, K, 0.5, 3, 8, 20, seed)
+        X[M - 1, K - 1] = 6.0
+        X[M - 2, K - 17] = np.float16(5.99609375)
+        X[M - 1, 63] = -6.0
+        X[M // 2, 64] = np.float16(-5.99609375)
+        yield f"strip_{M}x{K}", X, sorted(set(c) | {K - 1, 63}), 6.0
     X, c = wl.make_x(24, 128, 0.25, 0, 8, 20, 8)
     X[3, 5] = 6.0
     X[7, 9] = np.float16(5.99609375)
@@ -157,7 +168,7 @@ def test_quantize_activation_bitexact(lib, case):
 
 def test_quantize_activation_reused_workspace(lib):
     """One workspace through calls whose outlier sets shrink: no column flag
-    of an earlier call may survive (rows <= 64 store every flag word; more
+    of an earlier call may survive (rows <= 256 store every flag word; more
     rows clear the flags first; the threshold off stores zeros)."""
     K = 1040
     ws = lib.new_workspace(300, K, 0, torch.device("cuda:0"))
@@ -166,6 +177,8 @@ def test_quantize_activation_reused_workspace(lib):
              ("m40_none", wl.make_x(40, K, 1.0, 0, 8, 20, 22)[0], 6.0),
              ("m300_many", wl.make_x(300, K, 1.0, 50, 8, 20, 23)[0], 6.0),
              ("m64_few", wl.make_x(64, K, 1.0, 2, 8, 20, 24)[0], 6.0),
+             ("m200_many", wl.make_x(200, K, 1.0, 40, 8, 20, 27)[0], 6.0),
+             ("m130_none", wl.make_x(130, K, 1.0, 0, 8, 20, 28)[0], 6.0),
              ("m300_off", wl.make_x(300, K, 1.0, 9, 8, 20, 25)[0], math.inf),
              ("m20_off", wl.make_x(20, K, 1.0, 9, 8, 20, 26)[0], math.inf)]
     for name, X, t in calls:
