@@ -26,23 +26,27 @@
 //     barrier, so they stay in flight across it; past the last step they
 //     re-read valid memory into a consumed slot, so the loop body has no
 //     branches and the wait counts are fixed;
-//   * each wave owns a 128 x 64 sub-tile = 4 x 2 blocks of
-//     v_mfma_i32_32x32x32_i8 (128 int32 accumulators per lane); on gfx950 this
-//     shape sustains ~93% of the int8 peak in a bare loop, against ~79% for
-//     v_mfma_i32_16x16x64_i8;
-//   * software pipeline at quarter-step granularity: while the 8 MFMAs of one
-//     32-byte k quarter run, the 6 fragments of the next quarter are read from
-//     LDS into the other of two fixed register sets; reads and loads are
+//   * each wave owns a 128 x 64 sub-tile = 8 x 4 blocks of
+//     v_mfma_i32_16x16x64_i8 (128 int32 accumulators per lane).  Both int8
+//     shapes run at ~99% of the peak in a sustained loop with all-zero
+//     operands, but with random operands the board's power limit holds
+//     32x32x32 to 3.29 POP/s and 16x16x64 to 3.88 POP/s (measured on MI355X),
+//     so the smaller shape does more work per joule;
+//   * software pipeline at quarter-step granularity: a 128-byte k-step is two
+//     64-byte sub-steps; while the 16 MFMAs of one quarter (one sub-step, half
+//     of the A blocks) run, the 4 or 8 fragments of the next quarter are read
+//     from LDS into the other of two fixed register sets; reads and loads are
 //     placed between the MFMAs with sched_group_barrier;
 //   * LDS rows are 128 bytes = eight 16-byte chunks; chunk c of row r is
-//     stored at c ^ (((r >> 1) & 3) | (((r >> 4) & 1) << 2)): the bank-conflict
-//     counter reads 0 for the fragment reads (one chunk of 32 consecutive rows
-//     per half-wave);
+//     stored at c ^ ((r >> 1) & 7): the bank-conflict counter reads 0 for both
+//     fragment patterns (16 consecutive rows per 16 lanes for the int8 loop, 32
+//     per half-wave for the fp16 one);
 //   * tiles are handed out XCD by XCD: workgroup b runs on XCD b % 8, and each
 //     XCD takes a contiguous range of tiles ordered in groups of 8 tile-rows so
 //     that concurrently running tiles share operand panels in that XCD's L2.
-// Epilogue, one 32x32 block of the wave tile at a time: the int32
-// accumulators of the block are dequantized to fp32 (acc * sx * sw / 127^2),
+// Epilogue, one 32x32 block of the wave tile at a time (its four 16x16
+// accumulator blocks rearranged into the 32x32 layout through 5 KB of LDS per
+// wave): the int32 accumulators of the block are dequantized to fp32 (acc * sx * sw / 127^2),
 // then the outlier product is accumulated onto them with
 // v_mfma_f32_32x32x16_f16 from X_O [256 x 96] and the matching weight rows
 // (transposed to [256 x 96]) staged in LDS once per tile (up to 96 outlier
@@ -70,7 +74,7 @@ constexpr int kSlots = 5;                  // LDS slots of one operand panel of 
 constexpr int kSlot = kBM * kBK;           // 32 KB
 constexpr int kGemmThreads = 512;
 constexpr int kGroupM = 8;
-__device__ __forceinline__ int lds_swz(int row) { return ((row >> 1) & 3) | (((row >> 4) & 1) << 2); }
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 7; }
 
 // Tile order: linear tile index -> (tile row, tile column), in groups of
 // kGroupM tile rows so that concurrently running tiles share operand panels.
@@ -116,6 +120,13 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 __device__ __forceinline__ int d_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
+// D layout of a 16x16 MFMA block: lane l holds column l % 16 and, in register
+// r, row 4 * (l / 16) + r.
+// Per-wave LDS area that turns four 16x16 int32 blocks into the 32x32 layout
+// above (rows of kCvS words: lanes 32-63 of a 32x32 read land 32 banks away
+// from lanes 0-31).
+constexpr int kCvS = 40;
+constexpr int kCvWave = 32 * kCvS;   // words per wave
 
 // SPLIT: the workgroups are the split tiles of the tail (S per tile), each on
 // its own range of k-steps; they store their int32 partials and end.  FIX
@@ -190,6 +201,45 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
                                      16, 0, 0);
   };
   // Step kt's A panel sits in slot (2 kt) % 5 and its B panel in (2 kt + 1) % 5.
+
+  // Accumulators.  F16: 4 x 2 blocks of v_mfma_f32_32x32x16_f16 (32 x 32 each).
+  // int8: 8 x 4 blocks of v_mfma_i32_16x16x64_i8 (16 x 16 each; block (ia, jb)
+  // covers rows wm + 16 ia, features wn + 16 jb).  Measured on MI355X with
+  // random operands in a sustained loop: the 16x16x64 shape reaches 3.88 POP/s
+  // against 3.29 POP/s for 32x32x32 (both ~4.97 POP/s with all-zero operands):
+  // under the board's power limit it does more work per joule.
+  constexpr int kAI = F16 ? 4 : 8, kAJ = F16 ? 2 : 4;
+  typedef typename std::conditional<F16, v16f, v4i>::type blk_t;
+  blk_t acc[kAI][kAJ];
+#pragma unroll
+  for (int i = 0; i < kAI; ++i)
+#pragma unroll
+    for (int j = 0; j < kAJ; ++j) acc[i][j] = blk_t{};
+  if constexpr (ZP && !SPLIT && !F16) {
+    // Zero-point correction as the accumulators' starting value: the MFMAs then
+    // add sum_k (q - 128) w on top.  Every prefix sum stays within
+    // 255 * 127 * K < 2^31 in magnitude, so nothing wraps.  Rows past M read 0
+    // from the buffer resource (never stored).
+    const buf_rsrc rz = make_rsrc(a.zp, (uint32_t)M * 4u);
+    uint32_t wsv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + j * 16 + (lane & 15);
+      wsv[j] = n < N ? (uint32_t)a.wsum[n] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const v4i z = buf_load16(rz, (uint32_t)(m0 + wm + i * 16 + 4 * (lane >> 4)) * 4u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = (int)((128u - (uint32_t)z[r]) * wsv[j]);
+    }
+  }
+  // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
+  constexpr int kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100;
+
+  if constexpr (!FIX && F16) {
   // Fragments of the 32-byte k quarter q: 4 A blocks and 2 B blocks of 32
   // rows; lane l reads row l % 32, logical chunk 2q + l / 32.
   auto read_q = [&](int kt, int q, v4i (&fa)[4], v4i (&fb)[2]) {
@@ -207,45 +257,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
       fb[j] = *reinterpret_cast<const v4i*>(&sB[row * kBK + ((c ^ lds_swz(row)) << 4)]);
     }
   };
-
-  typedef typename std::conditional<F16, v16f, v16i>::type acc_t;
-  acc_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = acc_t{};
-  if constexpr (ZP && !SPLIT) {
-    // Zero-point correction as the accumulators' starting value: the MFMAs then
-    // add sum_k (q - 128) w on top.  Every prefix sum stays within
-    // 255 * 127 * K < 2^31 in magnitude, so nothing wraps.  Rows past M read 0
-    // from the buffer resource (never stored).
-    const buf_rsrc rz = make_rsrc(a.zp, (uint32_t)M * 4u);
-    uint32_t wsv[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn + j * 32 + l32;
-      wsv[j] = n < N ? (uint32_t)a.wsum[n] : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {   // one dword per row: each load wholly in or out
-        const uint32_t z = buf_load_u32(rz, (uint32_t)(m0 + wm + i * 32 + d_row(r, lane)) * 4u);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j][r] = (int)((128u - z) * wsv[j]);
-      }
-  }
   auto mfma_one = [&](const v4i (&fa)[4], const v4i (&fb)[2], int q) {
     const int i = q & 3, j = q >> 2;
-    if constexpr (F16)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fa[i]),
-                                                        __builtin_bit_cast(v8h, fb[j]), acc[i][j],
-                                                        0, 0, 0);
-    else
-      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fa[i]),
+                                                      __builtin_bit_cast(v8h, fb[j]), acc[i][j],
+                                                      0, 0, 0);
   };
-  // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
-  constexpr int kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100;
   // One quarter: 8 MFMAs with the 6 fragment reads of the next quarter and 2
   // loads between them.
   auto pattern_quarter = [&]() {
@@ -271,7 +288,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   // barrier at the end of iteration kt needs step kt+1 complete: issued after
   // its last load are only the four A loads of kt+2, so vmcnt(4).  (Measured:
   // ~10 % faster than issuing two of the A loads after the barrier.)
-  if constexpr (!FIX) {
   load(0, 0, false, 0); load(0, 0, false, 1); load(0, 0, false, 2); load(0, 0, false, 3);
   load(1, 0, true, 0); load(1, 0, true, 1); load(1, 0, true, 2); load(1, 0, true, 3);
   {
@@ -342,8 +358,173 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   }
   wait_vmcnt<0>();
   wait_lgkmcnt0();
-  }   // !FIX
+  }   // !FIX && F16
+
+  if constexpr (!FIX && !F16) {
+  // int8 main loop on v_mfma_i32_16x16x64_i8.  A 128-byte k-step is two 64-byte
+  // sub-steps s; the operand of lane l is 16 bytes of row l % 16 at logical
+  // chunk 4 s + l / 16 (the same chunk in A and B, so the products pair the
+  // same k).  Quarter q of a step: sub-step q / 2, A blocks 4 (q % 2) .. +3, all
+  // four B blocks: 16 MFMAs on 4 A and 4 B fragments.  Register sets: A in
+  // fa0 / fa1 (even / odd quarters), B in fb0 / fb1 (sub-step 0 / 1).
+  auto read_a = [&](int kt, int s, int h, v4i (&fa)[4]) {
+    const int8_t* sA = &smem[((2 * kt) % kSlots) * kSlot];
+    const int c = 4 * s + (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm + (4 * h + i) * 16 + (lane & 15);
+      fa[i] = *reinterpret_cast<const v4i*>(&sA[row * kBK + ((c ^ lds_swz(row)) << 4)]);
+    }
+  };
+  auto read_b = [&](int kt, int s, v4i (&fb)[4]) {
+    const int8_t* sB = &smem[((2 * kt + 1) % kSlots) * kSlot];
+    const int c = 4 * s + (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn + j * 16 + (lane & 15);
+      fb[j] = *reinterpret_cast<const v4i*>(&sB[row * kBK + ((c ^ lds_swz(row)) << 4)]);
+    }
+  };
+  // MFMA e (0..15) of a quarter with A set h: A block 4 h + e / 4, B block e % 4
+  auto mfma16 = [&](const v4i (&fa)[4], const v4i (&fb)[4], int h, int e) {
+    const int i = e >> 2, j = e & 3;
+    acc[4 * h + i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[4 * h + i][j], 0, 0, 0);
+  };
+  // 16 MFMAs with 4 fragment reads and 2 loads between them
+  auto pattern_4r = [&]() {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 3, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // 16 MFMAs with 8 fragment reads and 2 loads between them
+  auto pattern_8r = [&]() {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 3, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Slot schedule as in the fp16 loop above: A of kt+1 in flight from the
+  // previous iteration, B of kt+1 issued in quarters 0-1, A of kt+2 in
+  // quarters 2-3, vmcnt(4) before the end-of-step barrier.
+  load(0, 0, false, 0); load(0, 0, false, 1); load(0, 0, false, 2); load(0, 0, false, 3);
+  load(1, 0, true, 0); load(1, 0, true, 1); load(1, 0, true, 2); load(1, 0, true, 3);
+  {
+    const int k1 = min(1, nk - 1);
+    load(2, k1, false, 0); load(2, k1, false, 1); load(2, k1, false, 2); load(2, k1, false, 3);
+  }
+  wait_vmcnt<4>();   // step 0 landed; A of step 1 may be in flight
+  lds_barrier();
+
+  v4i fa0[4], fa1[4], fb0[4], fb1[4];
+  read_a(0, 0, 0, fa0);
+  read_b(0, 0, fb0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slB = (2 * kt + 3) % kSlots, slA = (2 * kt + 4) % kSlots;
+    const int kB = min(kt + 1, nk - 1), kA = min(kt + 2, nk - 1);
+    // ---- quarter 0 (sub-step 0, A 0-3): reads A 4-7 of sub-step 0; B loads 0-1
+    wait_lgkmcnt0();
+    read_a(kt, 0, 1, fa1);
+    load(slB, kB, true, 0);
+    load(slB, kB, true, 1);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mfma16(fa0, fb0, 0, e);
+    pattern_4r();
+    // ---- quarter 1 (sub-step 0, A 4-7): reads A 0-3 and B of sub-step 1; B loads 2-3
+    wait_lgkmcnt0();
+    read_a(kt, 1, 0, fa0);
+    read_b(kt, 1, fb1);
+    load(slB, kB, true, 2);
+    load(slB, kB, true, 3);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mfma16(fa1, fb0, 1, e);
+    pattern_8r();
+    // ---- quarter 2 (sub-step 1, A 0-3): reads A 4-7 of sub-step 1; A loads 0-1 of kt+2
+    wait_lgkmcnt0();
+    read_a(kt, 1, 1, fa1);
+    load(slA, kA, false, 0);
+    load(slA, kA, false, 1);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mfma16(fa0, fb1, 0, e);
+    pattern_4r();
+    // ---- quarter 3 (sub-step 1, A 4-7): half of the MFMAs go out before the
+    // wait and the barrier, so the matrix pipe is busy while the waves
+    // synchronize; then the reads of the next step's first quarter
+    wait_lgkmcnt0();
+    load(slA, kA, false, 2);
+    load(slA, kA, false, 3);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mfma16(fa1, fb1, 1, e);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<4>();
+    lds_barrier();
+    // Step kt+1 is in every wave's view and step kt's slots are free.  On the
+    // last step the fragment reads re-read step kt (landed, unused), so that
+    // the registers keep fixed roles.
+    {
+      const int kn = kt + 1 < nk ? kt + 1 : kt;
+      read_a(kn, 0, 0, fa0);
+      read_b(kn, 0, fb0);
+    }
+#pragma unroll
+    for (int e = 8; e < 16; ++e) mfma16(fa1, fb1, 1, e);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_vmcnt<0>();
+  wait_lgkmcnt0();
+  }   // !FIX && !F16
   __syncthreads();   // all waves done with the ring before the epilogue reuses it
+
+  // int8: the exact int32 values of 32x32 region (i, j) of the wave tile in
+  // the 32x32 D layout, from its four 16x16 blocks (2i + bi, 2j + bj), through
+  // the wave's kCvWave words of LDS at cv (the epilogue below is written for
+  // that layout).
+  auto to32 = [&](int* cv, int i, int j, int (&tot)[16]) {
+    if constexpr (!F16) {
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            cv[(16 * bi + 4 * (lane >> 4) + r) * kCvS + 16 * bj + (lane & 15)] =
+                acc[2 * i + bi][2 * j + bj][r];
+      // the wave's LDS writes before its reads of other lanes' values
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tot[r] = cv[d_row(r, lane) * kCvS + l32];
+      // the reads done before the area is written again
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  };
 
   if constexpr (F16) {
     // fp16 output, one 32x32 block at a time: through 2.5 KB of LDS per wave
@@ -396,14 +577,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     // covers 1 KB contiguous per wave.
     constexpr int kTile = kBM * kBN;
     v4i* mine = reinterpret_cast<v4i*>(a.part + (size_t)(slot * a.split_S + sidx) * kTile);
+    int* cv = reinterpret_cast<int*>(&smem[0]) + wave * kCvWave;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
+        int tot[16];
+        to32(cv, i, j, tot);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           mine[((i * 2 + j) * 4 + q) * kGemmThreads + t] =
-              v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              v4i{tot[4 * q], tot[4 * q + 1], tot[4 * q + 2], tot[4 * q + 3]};
         __builtin_amdgcn_sched_barrier(0);
       }
     return;
@@ -413,7 +597,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   // or, in the fix-up of a split tile, the sum of its S partials, read four at
   // a time with every load unconditional (partials past S read zero from the
   // range check), so that they are in flight together.
-  auto tile_sum = [&](int i, int j, int (&tot)[16]) {
+  auto tile_sum = [&](int* cv, int i, int j, int (&tot)[16]) {
     if constexpr (SPLIT) {
       constexpr int kTile = kBM * kBN;
       const buf_rsrc rp = make_rsrc(a.part + (size_t)slot * a.split_S * kTile,
@@ -437,8 +621,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
             for (int e = 0; e < 4; ++e) tot[4 * q + e] += p[k][q][e];
       }
     } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tot[r] = acc[i][j][r];
+      to32(cv, i, j, tot);
     }
   };
 
@@ -449,7 +632,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
       for (int j = 0; j < 2; ++j) {
         const int n = n0 + wn + j * 32 + l32;
         int tot[16];
-        tile_sum(i, j, tot);
+        tile_sum(reinterpret_cast<int*>(&smem[0]) + wave * kCvWave, i, j, tot);
         if (n >= N) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -478,11 +661,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     float* sBias = sSw + kBN;                                      // [256] (0 without bias)
     int* sZc = reinterpret_cast<int*>(sBias + kBN);                // [256] 128 - zp (ZP)
     int* sWs = sZc + kBM;                                          // [256] wsum (ZP)
-    // Per wave, one 32x32 fp16 block in row order (kTS halves per row), so
-    // that Y goes out in 16-byte row pieces instead of 2-byte column values.
+    // Per wave, kCvWave words: first the int32 conversion of a 32x32 region
+    // (to32), then the same block as fp16 in row order (kTS halves per row),
+    // so that Y goes out in 16-byte row pieces instead of 2-byte column values.
     constexpr int kTS = 40;
-    uint16_t* sT = reinterpret_cast<uint16_t*>(sWs + kBN) + wave * 32 * kTS;
-    static_assert(2 * kBM * kOutG * 2 + 5 * 256 * 4 + kGemmThreads / 64 * 32 * kTS * 2 <=
+    int* cvY = reinterpret_cast<int*>(sWs + kBN) + wave * kCvWave;
+    uint16_t* sT = reinterpret_cast<uint16_t*>(cvY);
+    static_assert(32 * kTS * 2 <= kCvWave * 4, "fp16 staging must fit the conversion area");
+    static_assert(2 * kBM * kOutG * 2 + 5 * 256 * 4 + kGemmThreads / 64 * kCvWave * 4 <=
                       (int)sizeof(smem),
                   "epilogue staging must fit the LDS");
     // N % 8 == 0: every 8-column piece of a row lies wholly inside or outside
@@ -591,7 +777,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
         const int n = n0 + wn + j * 32 + l32;
         const float swv = sSw[wn + j * 32 + l32];
         int tot[16];
-        tile_sum(i, j, tot);
+        tile_sum(cvY, i, j, tot);
         if constexpr (ZP && SPLIT) {   // sum (q - zp) w = sum (q - 128) w + (128 - zp) S[n], mod 2^32
           const uint32_t wsv = (uint32_t)sWs[wn + j * 32 + l32];
 #pragma unroll
@@ -766,7 +952,7 @@ hipError_t launch_gemm_f16(const uint16_t* A, const uint16_t* B, int M, int N, i
 
 const char* gemm_tile_info() {
   return "gemm: 256x256x128 tile, 5-slot LDS-DMA ring, 8 waves of 128x64, "
-         "v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_f16 outlier tail";
+         "v_mfma_i32_16x16x64_i8, v_mfma_f32_32x32x16_f16 outlier tail";
 }
 
 }  // namespace i8l
