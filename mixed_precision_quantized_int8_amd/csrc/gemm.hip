@@ -202,14 +202,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   };
   // Step kt's A panel sits in slot (2 kt) % 5 and its B panel in (2 kt + 1) % 5.
 
-  // Accumulators.  F16: 4 x 2 blocks of v_mfma_f32_32x32x16_f16 (32 x 32 each).
-  // int8: 8 x 4 blocks of v_mfma_i32_16x16x64_i8 (16 x 16 each; block (ia, jb)
-  // covers rows wm + 16 ia, features wn + 16 jb).  Measured on MI355X with
-  // random operands in a sustained loop: the 16x16x64 shape reaches 3.88 POP/s
-  // against 3.29 POP/s for 32x32x32 (both ~4.97 POP/s with all-zero operands):
-  // under the board's power limit it does more work per joule.
-  constexpr int kAI = F16 ? 4 : 8, kAJ = F16 ? 2 : 4;
-  typedef typename std::conditional<F16, v16f, v4i>::type blk_t;
+  // Accumulators: 8 x 4 blocks of v_mfma_i32_16x16x64_i8 (F16:
+  // v_mfma_f32_16x16x32_f16), 16 x 16 each; block (ia, jb) covers rows
+  // wm + 16 ia, features wn + 16 jb.  Measured on MI355X with random operands
+  // in a sustained loop: the 16x16 shapes reach 3.9-4.1 POP/s (int8) and 1.90
+  // PFLOP/s (fp16) against 3.3-3.5 and 1.67 for the 32x32 ones (all ~99 % of
+  // the peak with all-zero operands): under the board's power limit they do
+  // more work per joule.
+  constexpr int kAI = 8, kAJ = 4;
+  typedef typename std::conditional<F16, v4f, v4i>::type blk_t;
   blk_t acc[kAI][kAJ];
 #pragma unroll
   for (int i = 0; i < kAI; ++i)
@@ -239,132 +240,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
   constexpr int kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100;
 
-  if constexpr (!FIX && F16) {
-  // Fragments of the 32-byte k quarter q: 4 A blocks and 2 B blocks of 32
-  // rows; lane l reads row l % 32, logical chunk 2q + l / 32.
-  auto read_q = [&](int kt, int q, v4i (&fa)[4], v4i (&fb)[2]) {
-    const int8_t* sA = &smem[((2 * kt) % kSlots) * kSlot];
-    const int8_t* sB = &smem[((2 * kt + 1) % kSlots) * kSlot];
-    const int c = 2 * q + lh;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm + i * 32 + l32;
-      fa[i] = *reinterpret_cast<const v4i*>(&sA[row * kBK + ((c ^ lds_swz(row)) << 4)]);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = wn + j * 32 + l32;
-      fb[j] = *reinterpret_cast<const v4i*>(&sB[row * kBK + ((c ^ lds_swz(row)) << 4)]);
-    }
-  };
-  auto mfma_one = [&](const v4i (&fa)[4], const v4i (&fb)[2], int q) {
-    const int i = q & 3, j = q >> 2;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fa[i]),
-                                                      __builtin_bit_cast(v8h, fb[j]), acc[i][j],
-                                                      0, 0, 0);
-  };
-  // One quarter: 8 MFMAs with the 6 fragment reads of the next quarter and 2
-  // loads between them.
-  auto pattern_quarter = [&]() {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // Slot schedule (5 slots, steps of two panels).  During iteration kt: step
-  // kt is read from slots 2kt, 2kt+1; A of kt+1 (slot 2kt+2) was issued during
-  // iteration kt-1; B of kt+1 goes to slot 2kt+3 (quarters 0-1) and A of kt+2
-  // to slot 2kt+4 (quarter 2 and the start of quarter 3), all mod 5.  Slots 2kt+3 and 2kt+4 held step
-  // kt-1, which every wave finished reading before the previous barrier.  The
-  // barrier at the end of iteration kt needs step kt+1 complete: issued after
-  // its last load are only the four A loads of kt+2, so vmcnt(4).  (Measured:
-  // ~10 % faster than issuing two of the A loads after the barrier.)
-  load(0, 0, false, 0); load(0, 0, false, 1); load(0, 0, false, 2); load(0, 0, false, 3);
-  load(1, 0, true, 0); load(1, 0, true, 1); load(1, 0, true, 2); load(1, 0, true, 3);
-  {
-    const int k1 = min(1, nk - 1);
-    load(2, k1, false, 0); load(2, k1, false, 1); load(2, k1, false, 2); load(2, k1, false, 3);
-  }
-  wait_vmcnt<4>();   // step 0 landed; A of step 1 may be in flight
-  lds_barrier();
-
-  v4i f0a[4], f0b[2], f1a[4], f1b[2];
-  read_q(0, 0, f0a, f0b);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int slB = (2 * kt + 3) % kSlots, slA = (2 * kt + 4) % kSlots;
-    const int kB = min(kt + 1, nk - 1), kA = min(kt + 2, nk - 1);
-    // ---- quarter 0: MFMAs on f0, reads of quarter 1 into f1, B loads 0-1.
-    // The only outstanding LDS reads are those of f0, so draining lgkmcnt
-    // first costs little.
-    wait_lgkmcnt0();
-    read_q(kt, 1, f1a, f1b);
-    load(slB, kB, true, 0);
-    load(slB, kB, true, 1);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) mfma_one(f0a, f0b, q);
-    pattern_quarter();
-    // ---- quarter 1: B loads 2-3
-    wait_lgkmcnt0();
-    read_q(kt, 2, f0a, f0b);
-    load(slB, kB, true, 2);
-    load(slB, kB, true, 3);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) mfma_one(f1a, f1b, q);
-    pattern_quarter();
-    // ---- quarter 2: A loads 0-1 of step kt+2
-    wait_lgkmcnt0();
-    read_q(kt, 3, f1a, f1b);
-    load(slA, kA, false, 0);
-    load(slA, kA, false, 1);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) mfma_one(f0a, f0b, q);
-    pattern_quarter();
-    // ---- quarter 3: the first four MFMAs go out before the wait and the
-    // barrier, so the matrix pipe is busy while the waves synchronize
-    // (measured: 1, 2, 4, 6, 8 before it; four best, ~2 % over one on QKV).
-    wait_lgkmcnt0();
-    load(slA, kA, false, 2);
-    load(slA, kA, false, 3);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) mfma_one(f1a, f1b, q);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<4>();
-    lds_barrier();
-    // Step kt+1 is in every wave's view and step kt's slots are free.  On the
-    // last step the fragment reads re-read step kt (landed, unused), so that
-    // the registers keep fixed roles.
-    read_q(kt + 1 < nk ? kt + 1 : kt, 0, f0a, f0b);
-#pragma unroll
-    for (int q = 4; q < 8; ++q) mfma_one(f1a, f1b, q);
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  wait_vmcnt<0>();
-  wait_lgkmcnt0();
-  }   // !FIX && F16
-
-  if constexpr (!FIX && !F16) {
-  // int8 main loop on v_mfma_i32_16x16x64_i8.  A 128-byte k-step is two 64-byte
-  // sub-steps s; the operand of lane l is 16 bytes of row l % 16 at logical
-  // chunk 4 s + l / 16 (the same chunk in A and B, so the products pair the
-  // same k).  Quarter q of a step: sub-step q / 2, A blocks 4 (q % 2) .. +3, all
+  if constexpr (!FIX) {
+  // Main loop on v_mfma_i32_16x16x64_i8 (F16: v_mfma_f32_16x16x32_f16, whose
+  // operand is also 16 bytes of one row per lane).  A 128-byte k-step is two
+  // 64-byte sub-steps s; the operand of lane l is 16 bytes of row l % 16 at
+  // logical chunk 4 s + l / 16 (the same chunk in A and B, so the products pair
+  // the same k).  Quarter q of a step: sub-step q / 2, A blocks 4 (q % 2) .. +3, all
   // four B blocks: 16 MFMAs on 4 A and 4 B fragments.  Register sets: A in
   // fa0 / fa1 (even / odd quarters), B in fb0 / fb1 (sub-step 0 / 1).
   auto read_a = [&](int kt, int s, int h, v4i (&fa)[4]) {
@@ -388,7 +269,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   // MFMA e (0..15) of a quarter with A set h: A block 4 h + e / 4, B block e % 4
   auto mfma16 = [&](const v4i (&fa)[4], const v4i (&fb)[4], int h, int e) {
     const int i = e >> 2, j = e & 3;
-    acc[4 * h + i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[4 * h + i][j], 0, 0, 0);
+    if constexpr (F16)
+      acc[4 * h + i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          __builtin_bit_cast(v8h, fa[i]), __builtin_bit_cast(v8h, fb[j]), acc[4 * h + i][j], 0, 0, 0);
+    else
+      acc[4 * h + i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[4 * h + i][j], 0, 0, 0);
   };
   // 16 MFMAs with 4 fragment reads and 2 loads between them
   auto pattern_4r = [&]() {
@@ -423,9 +308,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Slot schedule as in the fp16 loop above: A of kt+1 in flight from the
-  // previous iteration, B of kt+1 issued in quarters 0-1, A of kt+2 in
-  // quarters 2-3, vmcnt(4) before the end-of-step barrier.
+  // Slot schedule (5 slots, steps of two panels).  During iteration kt: step
+  // kt is read from slots 2kt, 2kt+1; A of kt+1 (slot 2kt+2) was issued during
+  // iteration kt-1; B of kt+1 goes to slot 2kt+3 (quarters 0-1) and A of kt+2
+  // to slot 2kt+4 (quarters 2-3), all mod 5.  Slots 2kt+3 and 2kt+4 held step
+  // kt-1, which every wave finished reading before the previous barrier.  The
+  // barrier at the end of iteration kt needs step kt+1 complete: issued after
+  // its last load are only the four A loads of kt+2, so vmcnt(4).  (Measured:
+  // ~10 % faster than issuing two of the A loads after the barrier.)
   load(0, 0, false, 0); load(0, 0, false, 1); load(0, 0, false, 2); load(0, 0, false, 3);
   load(1, 0, true, 0); load(1, 0, true, 1); load(1, 0, true, 2); load(1, 0, true, 3);
   {
@@ -496,23 +386,31 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   }
   wait_vmcnt<0>();
   wait_lgkmcnt0();
-  }   // !FIX && !F16
+  }   // !FIX
   __syncthreads();   // all waves done with the ring before the epilogue reuses it
 
-  // int8: the exact int32 values of 32x32 region (i, j) of the wave tile in
-  // the 32x32 D layout, from its four 16x16 blocks (2i + bi, 2j + bj), through
+  // The values of 32x32 region (i, j) of the wave tile in the 32x32 D layout
+  // (int8: the exact int32 sums), from its four 16x16 blocks (2i + bi, 2j + bj), through
   // the wave's kCvWave words of LDS at cv (the epilogue below is written for
   // that layout).
-  auto to32 = [&](int* cv, int i, int j, int (&tot)[16]) {
-    if constexpr (!F16) {
+  auto to32 = [&](int* cv, int i, int j, int (&tot)[16]) {   // F16: fp32 bit patterns
+    {
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
         for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            cv[(16 * bi + 4 * (lane >> 4) + r) * kCvS + 16 * bj + (lane & 15)] =
-                acc[2 * i + bi][2 * j + bj][r];
+          for (int r = 0; r < 4; ++r) {
+            // (element r taken as a value first: __builtin_bit_cast applied to
+            // the vector subscript itself read element 0 for every r)
+            int* dst = &cv[(16 * bi + 4 * (lane >> 4) + r) * kCvS + 16 * bj + (lane & 15)];
+            if constexpr (F16) {
+              const float v = acc[2 * i + bi][2 * j + bj][r];
+              *dst = __float_as_int(v);
+            } else {
+              *dst = acc[2 * i + bi][2 * j + bj][r];
+            }
+          }
       // the wave's LDS writes before its reads of other lanes' values
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -527,20 +425,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
   };
 
   if constexpr (F16) {
-    // fp16 output, one 32x32 block at a time: through 2.5 KB of LDS per wave
-    // in row order and out as 16-byte row pieces when N % 8 == 0, else
-    // element by element
+    // fp16 output, one 32x32 block at a time (rearranged by to32, then through
+    // the same LDS area in row order) and out as 16-byte row pieces when
+    // N % 8 == 0, else element by element
     constexpr int kTS = 40;
-    uint16_t* sT = reinterpret_cast<uint16_t*>(&smem[0]) + wave * 32 * kTS;
+    int* cv = reinterpret_cast<int*>(&smem[0]) + wave * kCvWave;
+    uint16_t* sT = reinterpret_cast<uint16_t*>(cv);
     const bool vec_store = (N & 7) == 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int n = n0 + wn + j * 32 + l32;
+        int tb[16];
+        to32(cv, i, j, tb);
         if (vec_store) {   // uniform
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sT[d_row(r, lane) * kTS + l32] = f2h(acc[i][j][r]);
+          for (int r = 0; r < 16; ++r)
+            sT[d_row(r, lane) * kTS + l32] = f2h(__int_as_float(tb[r]));
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -560,7 +462,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int m = m0 + wm + i * 32 + d_row(r, lane);
-            if (m < M) a.Y[(size_t)m * N + n] = f2h(acc[i][j][r]);
+            if (m < M) a.Y[(size_t)m * N + n] = f2h(__int_as_float(tb[r]));
           }
         }
         __builtin_amdgcn_sched_barrier(0);
