@@ -356,14 +356,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) mfma16(fa0, fb1, 0, e);
     pattern_4r();
-    // ---- quarter 3 (sub-step 1, A 4-7): half of the MFMAs go out before the
+    // ---- quarter 3 (sub-step 1, A 4-7): 12 of the 16 MFMAs go out before the
     // wait and the barrier, so the matrix pipe is busy while the waves
-    // synchronize; then the reads of the next step's first quarter
+    // synchronize; then the reads of the next step's first quarter between
+    // the last four (swept on MI355X: 4, 8, 12, 14, 16 before the barrier;
+    // 12 best, ~1 % over 8 and ~4 % over 4)
     wait_lgkmcnt0();
     load(slA, kA, false, 2);
     load(slA, kA, false, 3);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mfma16(fa1, fb1, 1, e);
+    for (int e = 0; e < 12; ++e) mfma16(fa1, fb1, 1, e);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<4>();
     lds_barrier();
@@ -376,10 +378,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs a) {
       read_b(kn, 0, fb0);
     }
 #pragma unroll
-    for (int e = 8; e < 16; ++e) mfma16(fa1, fb1, 1, e);
+    for (int e = 12; e < 16; ++e) mfma16(fa1, fb1, 1, e);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+    for (int r = 0; r < 4; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
