@@ -30,8 +30,8 @@
 //     v_mfma_i32_16x16x64_i8 (128 int32 accumulators per lane).  Both int8
 //     shapes run at ~99% of the peak in a sustained loop with all-zero
 //     operands, but with random operands the board's power limit holds
-//     32x32x32 to 3.29 POP/s and 16x16x64 to 3.88 POP/s (measured on MI355X),
-//     so the smaller shape does more work per joule;
+//     32x32x32 to 3.3-3.5 POP/s and 16x16x64 to 3.9-4.1 POP/s (measured on
+//     MI355X), so the smaller shape does more work per joule;
 //   * software pipeline at quarter-step granularity: a 128-byte k-step is two
 //     64-byte sub-steps; while the 16 MFMAs of one quarter (one sub-step, half
 //     of the A blocks) run, the 4 or 8 fragments of the next quarter are read
@@ -137,8 +137,8 @@ constexpr int kCvWave = 32 * kCvS;   // words per wave
 // instantiations, so that the whole-tile kernel carries none of this.  ZP:
 // zero-point epilogue.  F16: the operands are fp16 instead of int8 (a.K is
 // then the row length in BYTES, twice the element count); the same panels,
-// ring and fragments feed v_mfma_f32_32x32x16_f16, whose operand layout per
-// lane (16 bytes of one row, the two half-waves on consecutive 16-byte
+// ring and fragments feed v_mfma_f32_16x16x32_f16, whose operand layout per
+// lane (16 bytes of one row, the four 16-lane groups on consecutive 16-byte
 // chunks) is that of the int8 instruction, into fp32 accumulators, stored as
 // fp16 (round to nearest even) to a.Y.
 template <bool OUT_I32, bool SPLIT, bool ZP, bool FIX = false, bool F16 = false>
