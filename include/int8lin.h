@@ -75,7 +75,8 @@ typedef enum {
  *   flags        uint32 [ceil(K/32)] internal: outlier column bitmask
  *   zero_points  int32 [M]        int8_linear_zp only: the row zero points;
  *                                 sx then holds range / 255 and Xq the codes
- *                                 minus 128 (see int8_quantize_activation_zp)
+ *                                 minus 128 (see int8_quantize_activation_zp);
+ *                                 internal for absmax codes
  *   act_partials uint32           internal (1 <= M <= 16): per 512-column
  *                                 slice of K, its outlier count and per-row
  *                                 partial maxima / minima of the activation

@@ -7,7 +7,8 @@
 // states are quantized row by row.  [blog, "Introduction to model
 // quantization"]: absmax codes are round(x * 127 / absmax) in [-127, 127].
 //
-// For M > 16, launches on the caller's stream:
+// For M > 16, launches on the caller's stream (absmax codes with more than
+// 256 rows: clear, rowpass, rowquant FIX instead; see below):
 //   clear     zero the column bitmask (a fill kernel, safe under graph capture);
 //             only where several workgroups share a column (M > 256)
 //   colflags  one pass over X: per thread 16-byte loads, 8 running column
@@ -30,8 +31,14 @@
 // zp, 0, 255), stored as code - 128 so the int8 matrix cores can take them;
 // outlier columns store zp - 128 (the code of 0).  The row writes
 // fl32(range / 255) to sx and zp to the zero-point array.
-// The column dependency (every row must be seen before any row scale) is why
-// X is read twice; the second read is one coalesced pass per row.
+// The column dependency (every row must be seen before any row scale) would
+// have X read twice.  For more than 256 rows with absmax codes it is read once:
+// rowpass_kernel codes each row with a provisional scale (its largest entry
+// below the threshold) and sets the outlier flags, and the FIX instantiation of
+// rowquant then zeroes and gathers the outlier columns, recomputing only the
+// rows whose provisional scale came from an outlier column.  Zero-point codes
+// and 17-256 rows keep the scan + row pass (two reads; for small M the reads
+// are latency, not bytes).
 // For 1 <= M <= 16 (the small-M path with K > 4096, and the stage export) two
 // launches over 512-column slices do the same work with many workgroups
 // instead of one per row (see the kernels below).
@@ -234,14 +241,21 @@ __device__ __forceinline__ float wave_min(float v) {
 
 // One workgroup per row of X.  NCH 16-byte chunks per thread: K <= BS * 8 * NCH.
 // ZP: zero-point codes (zp != nullptr) instead of absmax codes.
-template <int BS, int NCH, bool ZP>
+// FIX (absmax codes only): the fix-up after rowpass_kernel.  The row's codes
+// and scale are already in Xq and sx; unless the column rowpass recorded for
+// the row (argcol) is an outlier column, the workgroup only zeroes the codes of
+// the outlier columns and copies their values to X_O, without reading the rest
+// of the row; otherwise it recomputes the row as the plain kernel does.
+template <int BS, int NCH, bool ZP, bool FIX = false>
 __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                      const uint32_t* __restrict__ flags,
                                                      int8_t* __restrict__ Xq, float* __restrict__ sx,
                                                      int32_t* __restrict__ zp,
                                                      int32_t* __restrict__ idx,
                                                      int32_t* __restrict__ n_out,
-                                                     uint16_t* __restrict__ X_O) {
+                                                     uint16_t* __restrict__ X_O,
+                                                     const int32_t* __restrict__ argcol) {
+  static_assert(!(FIX && ZP), "the row pass writes absmax codes only");
   __shared__ uint32_t s_flags[kMaxFlagWords];
   __shared__ int s_rank[kMaxFlagWords];
   __shared__ int s_tmp[BS / 64 + 1];
@@ -264,8 +278,10 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
   const buf_rsrc rx = make_rsrc(X + (size_t)row * K, (uint32_t)K * 2u);
   const int nchunks = K >> 3;
   v4i raw[NCH];
+  if constexpr (!FIX) {
 #pragma unroll
-  for (int j = 0; j < NCH; ++j) raw[j] = buf_load16(rx, (uint32_t)(t + j * BS) * 16u);
+    for (int j = 0; j < NCH; ++j) raw[j] = buf_load16(rx, (uint32_t)(t + j * BS) * 16u);
+  }
 #pragma unroll
   for (int i = 0; i < FW; ++i)
     if (t + i * BS < nw) s_flags[t + i * BS] = fl[i];
@@ -283,6 +299,44 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
     base += __builtin_popcount(s_flags[w]);
   }
   lds_sync();
+  // workgroup 0 writes the ascending index list and the outlier count
+  auto write_index = [&]() {
+    if (row == 0) {
+      for (int w = t; w < nw; w += BS) {
+        uint32_t f = s_flags[w];
+        int r = s_rank[w];
+        while (f) {
+          const int b = __builtin_ctz(f);
+          idx[r++] = w * 32 + b;
+          f &= f - 1u;
+        }
+      }
+      if (t == 0) *n_out = total;
+    }
+  };
+  if constexpr (FIX) {
+    const int c = argcol[row];   // uniform over the workgroup
+    const bool full = c >= 0 && ((s_flags[c >> 5] >> (c & 31)) & 1u);
+    if (!full) {
+      int8_t* qr = Xq + (size_t)row * K;
+      uint16_t* orow = X_O + (size_t)row * K;
+      const uint16_t* xr = X + (size_t)row * K;
+      for (int w = w0; w < w1; ++w) {
+        uint32_t f = s_flags[w];
+        int r = s_rank[w];
+        while (f) {
+          const int j = w * 32 + __builtin_ctz(f);
+          orow[r++] = xr[j];
+          qr[j] = 0;
+          f &= f - 1u;
+        }
+      }
+      write_index();
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) raw[j] = buf_load16(rx, (uint32_t)(t + j * BS) * 16u);
+  }
   uint32_t mx = 0;
   float lo = 0.0f, hi = 0.0f;   // zero-point mode: the range always contains 0
 #pragma unroll
@@ -379,17 +433,113 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
     if constexpr (ZP) zp[row] = zpv;
   }
 
-  if (row == 0) {
-    for (int w = t; w < nw; w += BS) {
-      uint32_t f = s_flags[w];
-      int r = s_rank[w];
-      while (f) {
-        const int b = __builtin_ctz(f);
-        idx[r++] = w * 32 + b;
-        f &= f - 1u;
+  write_index();
+}
+
+// Row pass of the prefill path (absmax codes, more than 256 rows, decomposition
+// on): one workgroup per row reads the row once.  Entries at or above the
+// threshold (a NaN never is) get code 0 and set their column's flag
+// (atomicOr; the flags were cleared before).  The other entries are coded with
+// a provisional scale, the largest magnitude among them, and a column where it
+// occurs is recorded in argcol (-1 when the scale is 0).  Every regular column
+// lies wholly below the threshold, so the maximum over the regular columns,
+// the scale the method asks for, is at most the provisional one, and equal to
+// it when the recorded column is regular: the codes, sx and all are then
+// final except in the outlier columns, which rowquant_kernel<..., FIX> zeroes
+// and gathers.  When the recorded column is an outlier column the fix-up
+// recomputes the row.  X is read once instead of twice (column scan, then row
+// quantization).
+template <int BS, int NCH>
+__global__ __launch_bounds__(BS) void rowpass_kernel(const uint16_t* __restrict__ X, int M, int K,
+                                                    float threshold, uint32_t* __restrict__ flags,
+                                                    int8_t* __restrict__ Xq,
+                                                    float* __restrict__ sx,
+                                                    int32_t* __restrict__ argcol) {
+  __shared__ uint32_t s_h[BS / 64], s_c[BS / 64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int row = blockIdx.x;
+  const buf_rsrc rx = make_rsrc(X + (size_t)row * K, (uint32_t)K * 2u);
+  const int nchunks = K >> 3;
+  v4i raw[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) raw[j] = buf_load16(rx, (uint32_t)(t + j * BS) * 16u);
+  // an entry at or above the threshold (a NaN never is)
+  auto big = [&](uint32_t h) { return h <= 0x7c00u && h2f((uint16_t)h) >= threshold; };
+  // the per-chunk masks are kept in registers up to 8 chunks per thread, and
+  // recomputed when the codes are formed beyond (register budget of 1024 threads)
+  constexpr bool kKeep = NCH <= 8;
+  uint32_t bigm[kKeep ? NCH : 1];
+  uint32_t mx = 0, mc = 0xffffffffu;   // largest magnitude bits below the threshold, its column
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int q = t + j * BS;
+    if constexpr (kKeep) bigm[j] = 0;
+    if (q < nchunks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t h = ((uint32_t)raw[j][e >> 1] >> ((e & 1) * 16)) & 0x7fffu;
+        const bool b = big(h);
+        if constexpr (kKeep) bigm[j] |= (uint32_t)b << e;
+        if (!b && h > mx) {
+          mx = h;
+          mc = (uint32_t)(q * 8 + e);
+        }
       }
     }
-    if (t == 0) *n_out = total;
+  }
+  // the workgroup's largest magnitude, and the smallest column that holds it
+  uint32_t wm = mx;
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)wm, off, 64);
+    wm = o > wm ? o : wm;
+  }
+  uint32_t wc = mx == wm ? mc : 0xffffffffu;
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)wc, off, 64);
+    wc = o < wc ? o : wc;
+  }
+  if (lane == 0) {
+    s_h[wave] = wm;
+    s_c[wave] = wc;
+  }
+  __syncthreads();
+  uint32_t bm = 0, bc = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < BS / 64; ++w) {
+    if (s_h[w] > bm) {
+      bm = s_h[w];
+      bc = s_c[w];
+    } else if (s_h[w] == bm && s_c[w] < bc) {
+      bc = s_c[w];
+    }
+  }
+  const float scale = h2f((uint16_t)bm);
+  const float inv = quant_scale(scale);
+  int8_t* qr = Xq + (size_t)row * K;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int q = t + j * BS;
+    if (q < nchunks) {
+      int code[8];
+      uint32_t bm8 = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t hb = (uint16_t)(((uint32_t)raw[j][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+        bool b;
+        if constexpr (kKeep) b = (bigm[j] >> e) & 1u;
+        else b = big(hb & 0x7fffu);
+        bm8 |= (uint32_t)b << e;
+        code[e] = b ? 0 : quant_code(h2f(hb), inv);
+      }
+      v2i packed = {(int)pack4_i8(code[0], code[1], code[2], code[3]),
+                    (int)pack4_i8(code[4], code[5], code[6], code[7])};
+      *reinterpret_cast<v2i*>(qr + q * 8) = packed;
+      if (bm8) atomicOr(flags + (q >> 2), bm8 << ((q & 3) * 8));
+    }
+  }
+  if (t == 0) {
+    sx[row] = scale;
+    argcol[row] = bm > 0 ? (int)bc : -1;
   }
 }
 
@@ -632,11 +782,25 @@ static void launch_rowquant(const uint16_t* X, int M, int K, bool zp, const Work
                             hipStream_t stream) {
   if (zp)
     hipLaunchKernelGGL((rowquant_kernel<BS, NCH, true>), dim3(M), dim3(BS), 0, stream, X, M, K,
-                       (const uint32_t*)ws.flags, ws.Xq, ws.sx, ws.zp, ws.idx, ws.n_out, ws.X_O);
+                       (const uint32_t*)ws.flags, ws.Xq, ws.sx, ws.zp, ws.idx, ws.n_out, ws.X_O,
+                       nullptr);
   else
     hipLaunchKernelGGL((rowquant_kernel<BS, NCH, false>), dim3(M), dim3(BS), 0, stream, X, M, K,
                        (const uint32_t*)ws.flags, ws.Xq, ws.sx, nullptr, ws.idx, ws.n_out,
-                       ws.X_O);
+                       ws.X_O, nullptr);
+}
+
+// Row pass, then its fix-up (absmax codes, M > 256, decomposition on; the
+// flags cleared first).  The zero-point array of the workspace, unused by
+// absmax codes, carries each row's recorded column from one to the other.
+template <int BS, int NCH>
+static void launch_rowpass(const uint16_t* X, int M, int K, float threshold, const Workspace& ws,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL((rowpass_kernel<BS, NCH>), dim3(M), dim3(BS), 0, stream, X, M, K, threshold,
+                     ws.flags, ws.Xq, ws.sx, ws.zp);
+  hipLaunchKernelGGL((rowquant_kernel<BS, NCH, false, true>), dim3(M), dim3(BS), 0, stream, X, M,
+                     K, (const uint32_t*)ws.flags, ws.Xq, ws.sx, nullptr, ws.idx, ws.n_out,
+                     ws.X_O, (const int32_t*)ws.zp);
 }
 
 hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float threshold,
@@ -680,6 +844,20 @@ hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float thr
     // one row block: every flag word is stored, so no clear launch
     hipLaunchKernelGGL(colflags_kernel<true>, dim3(bx, 1), dim3(kColThreads), 0, stream, X, M, K,
                        M, threshold, (int)enabled, ws.flags);
+  } else if (!zp) {
+    // absmax codes: one read of X (rowpass_kernel), then the fix-up
+    launch_fill_u32(ws.flags, (K + 31) / 32, 0u, stream);
+    const int nch = K / 8;
+    if (nch <= 256) launch_rowpass<256, 1>(X, M, K, threshold, ws, stream);
+    else if (nch <= 512) launch_rowpass<256, 2>(X, M, K, threshold, ws, stream);
+    else if (nch <= 1024) launch_rowpass<256, 4>(X, M, K, threshold, ws, stream);
+    else if (nch <= 2048) launch_rowpass<512, 4>(X, M, K, threshold, ws, stream);
+    else if (nch <= 4096) launch_rowpass<1024, 4>(X, M, K, threshold, ws, stream);
+    else if (nch <= 7168) launch_rowpass<1024, 7>(X, M, K, threshold, ws, stream);
+    else if (nch <= 8192) launch_rowpass<1024, 8>(X, M, K, threshold, ws, stream);
+    else if (nch <= 16384) launch_rowpass<1024, 16>(X, M, K, threshold, ws, stream);
+    else launch_rowpass<1024, 17>(X, M, K, threshold, ws, stream);
+    return hipGetLastError();
   } else {
     launch_fill_u32(ws.flags, (K + 31) / 32, 0u, stream);
     long long want = ((long long)M * bx + 2047) / 2048;

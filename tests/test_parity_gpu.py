@@ -104,6 +104,25 @@ def test_quantize_weight_bitexact(lib, K, N, seed):
 # ---------------------------------------------------------------------------------
 # activation stage (stage export)
 # ---------------------------------------------------------------------------------
+def _rowpass_x(M, K, seed):
+    """X with whole outlier columns plus rows whose largest entry below the
+    threshold lies in a column that another row makes an outlier."""
+    X, c = wl.make_x(M, K, 0.5, 3, 8, 20, seed)
+    p, p2, q = 11, 40, 41            # partial outlier columns p, p2; regular column q
+    X[:, [p, p2, q]] = np.clip(X[:, [p, p2, q]], -1, 1)
+    X[0, p] = 7.0                    # p is an outlier column because of row 0 ...
+    X[5, p] = np.float16(5.9)        # ... and holds row 5's largest entry below 6
+    X[1, p2] = -9.0
+    X[6, p2] = np.float16(5.5)       # a tie: 5.5 in outlier column p2 and regular q
+    X[6, q] = np.float16(-5.5)
+    X[7, p] = np.nan                 # a NaN in an outlier column
+    X[9, q] = np.float16(5.99609375)  # largest in a regular column: exact provisional scale
+    X[10, p] = 6.0                   # exactly the threshold, in an outlier column
+    X[M - 1, K - 1] = 6.0            # a last outlier column, set by the last row only
+    X[M - 2, K - 1] = np.float16(5.8)
+    return X, sorted(set(c) | {p, p2, K - 1})
+
+
 def _act_cases():
     yield "tiny", *wl.make_x(16, 1024, 1.0, 2, 8, 20, 1), 6.0
     yield "decode", *wl.make_x(8, 4096, 1.0, 4, 6.5, 40, 2), 6.0
@@ -144,6 +163,15 @@ def _act_cases():
         X[M - 1, 63] = -6.0
         X[M // 2, 64] = np.float16(-5.99609375)
         yield f"strip_{M}x{K}", X, sorted(set(c) | {K - 1, 63}), 6.0
+    # more than 256 rows, absmax codes: one pass over each row with a provisional
+    # scale (its largest entry below the threshold), then a fix-up that zeroes and
+    # gathers the outlier columns and recomputes a row whose provisional maximum
+    # sits in an outlier column
+    yield "rowpass_fallback", *_rowpass_x(300, 1040, 24), 6.0
+    yield "rowpass_fallback_k_mod64", *_rowpass_x(513, 2064, 25), 6.0
+    X, c = wl.make_x(260, 64, 1.0, 0, 8, 20, 26)
+    X[:, 7] = 0
+    yield "rowpass_all_outliers", X, c, 2.0 ** -24
     X, c = wl.make_x(24, 128, 0.25, 0, 8, 20, 8)
     X[3, 5] = 6.0
     X[7, 9] = np.float16(5.99609375)
@@ -339,6 +367,23 @@ def test_linear_parity(lib, case):
     r = O.int8_linear(X, Wq_o, sw_o, W, t)
     check_workspace(lib, ws, M, K, (r["Xq"], r["sx"], r["idx"], r["X_O"]), name)
     assert_y(host(Y), r["Y64"], r["Y"], name)
+
+
+@pytest.mark.parametrize("M,K,N,seed", [(300, 1040, 520, 24), (513, 2064, 300, 25)])
+def test_linear_rowpass_fallback(lib, M, K, N, seed):
+    """The whole layer on rows whose provisional scale must be recomputed
+    (their largest entry below the threshold, or a NaN, in an outlier column)."""
+    say(f"int8_linear rowpass fallback M={M} K={K} N={N}")
+    X, _ = _rowpass_x(M, K, seed)
+    W = wl.make_w(K, N, 0.02, seed)
+    Y, Wq, sw, ws = run_linear(lib, X, W, 6.0)
+    Wq_o, sw_o = O.quantize_weight(W)
+    r = O.int8_linear(X, Wq_o, sw_o, W, 6.0)
+    check_workspace(lib, ws, M, K, (r["Xq"], r["sx"], r["idx"], r["X_O"]), "rowpass")
+    # row 7 holds a NaN in an outlier column: its outputs are NaN on both sides
+    nan = np.isnan(r["Y64"])
+    assert np.array_equal(np.isnan(host(Y).astype(np.float64)), nan)
+    assert_y(np.where(nan, 0, host(Y)), np.where(nan, 0, r["Y64"]), None, "rowpass")
 
 
 def test_linear_overflow_to_inf(lib):
