@@ -8,7 +8,7 @@
 // quantization"]: absmax codes are round(x * 127 / absmax) in [-127, 127].
 //
 // For M > 16, launches on the caller's stream (absmax codes with more than
-// 256 rows: clear, rowpass, rowquant FIX instead; see below):
+// 256 rows: clear, rowpass, rowfix instead; see below):
 //   clear     zero the column bitmask (a fill kernel, safe under graph capture);
 //             only where several workgroups share a column (M > 256)
 //   colflags  one pass over X: per thread 16-byte loads, 8 running column
@@ -34,9 +34,9 @@
 // The column dependency (every row must be seen before any row scale) would
 // have X read twice.  For more than 256 rows with absmax codes it is read once:
 // rowpass_kernel codes each row with a provisional scale (its largest entry
-// below the threshold) and sets the outlier flags, and the FIX instantiation of
-// rowquant then zeroes and gathers the outlier columns, recomputing only the
-// rows whose provisional scale came from an outlier column.  Zero-point codes
+// below the threshold) and sets the outlier flags, and rowfix_kernel then
+// zeroes and gathers the outlier columns, recomputing only the rows whose
+// provisional scale came from an outlier column.  Zero-point codes
 // and 17-256 rows keep the scan + row pass (two reads; for small M the reads
 // are latency, not bytes).
 // For 1 <= M <= 16 (the small-M path with K > 4096, and the stage export) two
@@ -241,21 +241,14 @@ __device__ __forceinline__ float wave_min(float v) {
 
 // One workgroup per row of X.  NCH 16-byte chunks per thread: K <= BS * 8 * NCH.
 // ZP: zero-point codes (zp != nullptr) instead of absmax codes.
-// FIX (absmax codes only): the fix-up after rowpass_kernel.  The row's codes
-// and scale are already in Xq and sx; unless the column rowpass recorded for
-// the row (argcol) is an outlier column, the workgroup only zeroes the codes of
-// the outlier columns and copies their values to X_O, without reading the rest
-// of the row; otherwise it recomputes the row as the plain kernel does.
-template <int BS, int NCH, bool ZP, bool FIX = false>
+template <int BS, int NCH, bool ZP>
 __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                      const uint32_t* __restrict__ flags,
                                                      int8_t* __restrict__ Xq, float* __restrict__ sx,
                                                      int32_t* __restrict__ zp,
                                                      int32_t* __restrict__ idx,
                                                      int32_t* __restrict__ n_out,
-                                                     uint16_t* __restrict__ X_O,
-                                                     const int32_t* __restrict__ argcol) {
-  static_assert(!(FIX && ZP), "the row pass writes absmax codes only");
+                                                     uint16_t* __restrict__ X_O) {
   __shared__ uint32_t s_flags[kMaxFlagWords];
   __shared__ int s_rank[kMaxFlagWords];
   __shared__ int s_tmp[BS / 64 + 1];
@@ -278,10 +271,8 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
   const buf_rsrc rx = make_rsrc(X + (size_t)row * K, (uint32_t)K * 2u);
   const int nchunks = K >> 3;
   v4i raw[NCH];
-  if constexpr (!FIX) {
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) raw[j] = buf_load16(rx, (uint32_t)(t + j * BS) * 16u);
-  }
+  for (int j = 0; j < NCH; ++j) raw[j] = buf_load16(rx, (uint32_t)(t + j * BS) * 16u);
 #pragma unroll
   for (int i = 0; i < FW; ++i)
     if (t + i * BS < nw) s_flags[t + i * BS] = fl[i];
@@ -314,29 +305,6 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
       if (t == 0) *n_out = total;
     }
   };
-  if constexpr (FIX) {
-    const int c = argcol[row];   // uniform over the workgroup
-    const bool full = c >= 0 && ((s_flags[c >> 5] >> (c & 31)) & 1u);
-    if (!full) {
-      int8_t* qr = Xq + (size_t)row * K;
-      uint16_t* orow = X_O + (size_t)row * K;
-      const uint16_t* xr = X + (size_t)row * K;
-      for (int w = w0; w < w1; ++w) {
-        uint32_t f = s_flags[w];
-        int r = s_rank[w];
-        while (f) {
-          const int j = w * 32 + __builtin_ctz(f);
-          orow[r++] = xr[j];
-          qr[j] = 0;
-          f &= f - 1u;
-        }
-      }
-      write_index();
-      return;
-    }
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) raw[j] = buf_load16(rx, (uint32_t)(t + j * BS) * 16u);
-  }
   uint32_t mx = 0;
   float lo = 0.0f, hi = 0.0f;   // zero-point mode: the range always contains 0
 #pragma unroll
@@ -445,8 +413,8 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
 // lies wholly below the threshold, so the maximum over the regular columns,
 // the scale the method asks for, is at most the provisional one, and equal to
 // it when the recorded column is regular: the codes, sx and all are then
-// final except in the outlier columns, which rowquant_kernel<..., FIX> zeroes
-// and gathers.  When the recorded column is an outlier column the fix-up
+// final except in the outlier columns, which rowfix_kernel zeroes and
+// gathers.  When the recorded column is an outlier column the fix-up
 // recomputes the row.  X is read once instead of twice (column scan, then row
 // quantization).
 template <int BS, int NCH>
@@ -540,6 +508,140 @@ __global__ __launch_bounds__(BS) void rowpass_kernel(const uint16_t* __restrict_
   if (t == 0) {
     sx[row] = scale;
     argcol[row] = bm > 0 ? (int)bc : -1;
+  }
+}
+
+// Fix-up after rowpass_kernel, kFixRows rows per workgroup.  The flag words
+// and their prefix counts (the rank of each outlier column) are loaded once per
+// workgroup.  A row whose recorded column is regular only has the codes of the
+// outlier columns zeroed and their values copied to X_O at their rank (the
+// gathers of all the workgroup's rows in flight together); a row whose recorded
+// column is an outlier column is recomputed by the whole workgroup in two
+// passes over the row in 16-byte pieces (its maximum over the regular columns,
+// then the codes), with the rules of rowquant_kernel.  Workgroup 0 writes the
+// ascending index list and the outlier count.
+constexpr int kFixThreads = 256, kFixRows = 16;
+__global__ __launch_bounds__(kFixThreads) void rowfix_kernel(const uint16_t* __restrict__ X, int M,
+                                                            int K,
+                                                            const uint32_t* __restrict__ flags,
+                                                            const int32_t* __restrict__ argcol,
+                                                            int8_t* __restrict__ Xq,
+                                                            float* __restrict__ sx,
+                                                            int32_t* __restrict__ idx,
+                                                            int32_t* __restrict__ n_out,
+                                                            uint16_t* __restrict__ X_O) {
+  constexpr int BS = kFixThreads;
+  __shared__ uint32_t s_flags[kMaxFlagWords];
+  __shared__ int s_rank[kMaxFlagWords];
+  __shared__ int s_tmp[BS / 64 + 1];
+  __shared__ int s_full[kFixRows];
+  __shared__ uint32_t s_max[BS / 64];
+  const int t = threadIdx.x;
+  const int nw = (K + 31) >> 5;
+  const int r0 = blockIdx.x * kFixRows;
+  const int nr = min(kFixRows, M - r0);
+  for (int w = t; w < nw; w += BS) s_flags[w] = flags[w];
+  const int c = t < nr ? argcol[r0 + t] : -1;
+  lds_sync();
+  const int per = (nw + BS - 1) / BS;
+  const int w0 = t * per, w1 = min(nw, w0 + per);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __builtin_popcount(s_flags[w]);
+  int total;
+  int base = block_excl_scan<BS>(cnt, s_tmp, &total);
+  for (int w = w0; w < w1; ++w) {
+    s_rank[w] = base;
+    base += __builtin_popcount(s_flags[w]);
+  }
+  if (t < nr) s_full[t] = c >= 0 && ((s_flags[c >> 5] >> (c & 31)) & 1u);
+  lds_sync();
+  // regular recorded column: zero the outlier columns' codes, gather their
+  // values; the loads of all the rows go out before any store (rows past M
+  // re-read the last row and store nothing)
+  for (int w = w0; w < w1; ++w) {
+    uint32_t f = s_flags[w];
+    int r = s_rank[w];
+    while (f) {
+      const int j = w * 32 + __builtin_ctz(f);
+      uint16_t v[kFixRows];
+#pragma unroll
+      for (int i = 0; i < kFixRows; ++i) v[i] = X[(size_t)(r0 + min(i, nr - 1)) * K + j];
+#pragma unroll
+      for (int i = 0; i < kFixRows; ++i) {
+        if (i < nr && !s_full[i]) {
+          const size_t o = (size_t)(r0 + i) * K;
+          X_O[o + r] = v[i];
+          Xq[o + j] = 0;
+        }
+      }
+      ++r;
+      f &= f - 1u;
+    }
+  }
+  // outlier recorded column: the row again, with the method's scale
+  const int nchunks = K >> 3;
+  for (int i = 0; i < nr; ++i) {
+    if (!s_full[i]) continue;   // uniform
+    const int row = r0 + i;
+    const buf_rsrc rx = make_rsrc(X + (size_t)row * K, (uint32_t)K * 2u);
+    uint32_t mx = 0;
+    for (int q = t; q < nchunks; q += BS) {
+      const v4i x = buf_load16(rx, (uint32_t)q * 16u);
+      const uint32_t ob = (s_flags[q >> 2] >> ((q & 3) * 8)) & 0xffu;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t h = ((uint32_t)x[e >> 1] >> ((e & 1) * 16)) & 0x7fffu;
+        if (!((ob >> e) & 1u)) mx = h > mx ? h : mx;
+      }
+    }
+    mx = wave_max_u32(mx);
+    if ((t & 63) == 0) s_max[t >> 6] = mx;
+    __syncthreads();
+    mx = 0;
+#pragma unroll
+    for (int w = 0; w < BS / 64; ++w) mx = s_max[w] > mx ? s_max[w] : mx;
+    const float scale = h2f((uint16_t)mx);
+    const float inv = quant_scale(scale);
+    int8_t* qr = Xq + (size_t)row * K;
+    uint16_t* orow = X_O + (size_t)row * K;
+    for (int q = t; q < nchunks; q += BS) {
+      const v4i x = buf_load16(rx, (uint32_t)q * 16u);
+      const int word = q >> 2, sh = (q & 3) * 8;
+      const uint32_t ob = (s_flags[word] >> sh) & 0xffu;
+      int code[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t hb = (uint16_t)(((uint32_t)x[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+        code[e] = ((ob >> e) & 1u) ? 0 : quant_code(h2f(hb), inv);
+      }
+      v2i packed = {(int)pack4_i8(code[0], code[1], code[2], code[3]),
+                    (int)pack4_i8(code[4], code[5], code[6], code[7])};
+      *reinterpret_cast<v2i*>(qr + q * 8) = packed;
+      if (ob) {
+        const uint32_t fw = s_flags[word];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if ((ob >> e) & 1u) {
+            const int bit = sh + e;
+            orow[s_rank[word] + __builtin_popcount(fw & ((1u << bit) - 1u))] =
+                (uint16_t)(((uint32_t)x[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+          }
+        }
+      }
+    }
+    if (t == 0) sx[row] = scale;
+    __syncthreads();   // s_max is reused by the next recomputed row
+  }
+  if (blockIdx.x == 0) {
+    for (int w = t; w < nw; w += BS) {
+      uint32_t f = s_flags[w];
+      int r = s_rank[w];
+      while (f) {
+        idx[r++] = w * 32 + __builtin_ctz(f);
+        f &= f - 1u;
+      }
+    }
+    if (t == 0) *n_out = total;
   }
 }
 
@@ -782,12 +884,11 @@ static void launch_rowquant(const uint16_t* X, int M, int K, bool zp, const Work
                             hipStream_t stream) {
   if (zp)
     hipLaunchKernelGGL((rowquant_kernel<BS, NCH, true>), dim3(M), dim3(BS), 0, stream, X, M, K,
-                       (const uint32_t*)ws.flags, ws.Xq, ws.sx, ws.zp, ws.idx, ws.n_out, ws.X_O,
-                       nullptr);
+                       (const uint32_t*)ws.flags, ws.Xq, ws.sx, ws.zp, ws.idx, ws.n_out, ws.X_O);
   else
     hipLaunchKernelGGL((rowquant_kernel<BS, NCH, false>), dim3(M), dim3(BS), 0, stream, X, M, K,
                        (const uint32_t*)ws.flags, ws.Xq, ws.sx, nullptr, ws.idx, ws.n_out,
-                       ws.X_O, nullptr);
+                       ws.X_O);
 }
 
 // Row pass, then its fix-up (absmax codes, M > 256, decomposition on; the
@@ -798,9 +899,9 @@ static void launch_rowpass(const uint16_t* X, int M, int K, float threshold, con
                            hipStream_t stream) {
   hipLaunchKernelGGL((rowpass_kernel<BS, NCH>), dim3(M), dim3(BS), 0, stream, X, M, K, threshold,
                      ws.flags, ws.Xq, ws.sx, ws.zp);
-  hipLaunchKernelGGL((rowquant_kernel<BS, NCH, false, true>), dim3(M), dim3(BS), 0, stream, X, M,
-                     K, (const uint32_t*)ws.flags, ws.Xq, ws.sx, nullptr, ws.idx, ws.n_out,
-                     ws.X_O, (const int32_t*)ws.zp);
+  hipLaunchKernelGGL(rowfix_kernel, dim3((M + kFixRows - 1) / kFixRows), dim3(kFixThreads), 0,
+                     stream, X, M, K, (const uint32_t*)ws.flags, (const int32_t*)ws.zp, ws.Xq,
+                     ws.sx, ws.idx, ws.n_out, ws.X_O);
 }
 
 hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float threshold,
