@@ -7,8 +7,8 @@
 // states are quantized row by row.  [blog, "Introduction to model
 // quantization"]: absmax codes are round(x * 127 / absmax) in [-127, 127].
 //
-// For M > 16, launches on the caller's stream (absmax codes with more than
-// 256 rows: clear, rowpass, rowfix instead; see below):
+// For M > 16, launches on the caller's stream (more than 256 rows with the
+// decomposition on: clear, rowpass, rowfix instead; see below):
 //   clear     zero the column bitmask (a fill kernel, safe under graph capture);
 //             only where several workgroups share a column (M > 256)
 //   colflags  one pass over X: per thread 16-byte loads, 8 running column
@@ -32,12 +32,13 @@
 // outlier columns store zp - 128 (the code of 0).  The row writes
 // fl32(range / 255) to sx and zp to the zero-point array.
 // The column dependency (every row must be seen before any row scale) would
-// have X read twice.  For more than 256 rows with absmax codes it is read once:
-// rowpass_kernel codes each row with a provisional scale (its largest entry
-// below the threshold) and sets the outlier flags, and rowfix_kernel then
-// zeroes and gathers the outlier columns, recomputing only the rows whose
-// provisional scale came from an outlier column.  Zero-point codes
-// and 17-256 rows keep the scan + row pass (two reads; for small M the reads
+// have X read twice.  For more than 256 rows it is read once: rowpass_kernel
+// codes each row with a provisional scale (its largest entry below the
+// threshold; zero-point codes: its smallest and largest) and sets the outlier
+// flags, and rowfix_kernel then zeroes (zero-point codes: sets to the code of
+// 0) and gathers the outlier columns, recomputing only the rows whose
+// provisional scale came from an outlier column.  17-256 rows, and the
+// threshold off, keep the scan + row pass (two reads; for small M the reads
 // are latency, not bytes).
 // For 1 <= M <= 16 (the small-M path with K > 4096, and the stage export) two
 // launches over 512-column slices do the same work with many workgroups
@@ -234,6 +235,14 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
 
 constexpr int kMaxFlagWords = (I8L_MAX_K_DEV + 31) / 32;
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off, 64);
+    v = o < v ? o : v;
+  }
+  return v;
+}
+
 __device__ __forceinline__ float wave_min(float v) {
   for (int off = 32; off > 0; off >>= 1) v = __builtin_fminf(v, __shfl_xor(v, off, 64));
   return v;
@@ -409,7 +418,8 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
 // threshold (a NaN never is) get code 0 and set their column's flag
 // (atomicOr; the flags were cleared before).  The other entries are coded with
 // a provisional scale, the largest magnitude among them, and a column where it
-// occurs is recorded in argcol (-1 when the scale is 0).  Every regular column
+// occurs is recorded in rowval (-1 when the scale is 0; rowval is the
+// workspace's zero-point array, unused by absmax codes).  Every regular column
 // lies wholly below the threshold, so the maximum over the regular columns,
 // the scale the method asks for, is at most the provisional one, and equal to
 // it when the recorded column is regular: the codes, sx and all are then
@@ -417,13 +427,22 @@ __global__ __launch_bounds__(BS) void rowquant_kernel(const uint16_t* __restrict
 // gathers.  When the recorded column is an outlier column the fix-up
 // recomputes the row.  X is read once instead of twice (column scan, then row
 // quantization).
-template <int BS, int NCH>
+// ZP (zero-point codes): the provisional range is the smallest and largest
+// entry below the threshold, widened to contain 0 (a NaN counts for neither),
+// recorded with a column of each; the codes, xscale and zero point follow the
+// rules of rowquant_kernel.  The two columns go to the last 8 bytes of the
+// row's X_O capacity (the zero-point array is an output here); the fix-up
+// reads them before it writes any X_O value of the row.
+template <int BS, int NCH, bool ZP>
 __global__ __launch_bounds__(BS) void rowpass_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                     float threshold, uint32_t* __restrict__ flags,
                                                     int8_t* __restrict__ Xq,
                                                     float* __restrict__ sx,
-                                                    int32_t* __restrict__ argcol) {
+                                                    int32_t* __restrict__ rowval,
+                                                    uint16_t* __restrict__ X_O) {
   __shared__ uint32_t s_h[BS / 64], s_c[BS / 64];
+  __shared__ float s_lo[ZP ? BS / 64 : 1], s_hi[ZP ? BS / 64 : 1];
+  __shared__ uint32_t s_cl[ZP ? BS / 64 : 1], s_ch[ZP ? BS / 64 : 1];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int row = blockIdx.x;
   const buf_rsrc rx = make_rsrc(X + (size_t)row * K, (uint32_t)K * 2u);
@@ -438,6 +457,8 @@ __global__ __launch_bounds__(BS) void rowpass_kernel(const uint16_t* __restrict_
   constexpr bool kKeep = NCH <= 8;
   uint32_t bigm[kKeep ? NCH : 1];
   uint32_t mx = 0, mc = 0xffffffffu;   // largest magnitude bits below the threshold, its column
+  float lo = 0.0f, hi = 0.0f;          // zero-point codes: the range, with its columns
+  uint32_t cl = 0xffffffffu, ch = 0xffffffffu;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int q = t + j * BS;
@@ -445,15 +466,91 @@ __global__ __launch_bounds__(BS) void rowpass_kernel(const uint16_t* __restrict_
     if (q < nchunks) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t h = ((uint32_t)raw[j][e >> 1] >> ((e & 1) * 16)) & 0x7fffu;
+        const uint32_t hb = ((uint32_t)raw[j][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        const uint32_t h = hb & 0x7fffu;
         const bool b = big(h);
         if constexpr (kKeep) bigm[j] |= (uint32_t)b << e;
-        if (!b && h > mx) {
+        if constexpr (ZP) {
+          const float x = h2f((uint16_t)hb);
+          if (!b && x < lo) {
+            lo = x;
+            cl = (uint32_t)(q * 8 + e);
+          }
+          if (!b && x > hi) {
+            hi = x;
+            ch = (uint32_t)(q * 8 + e);
+          }
+        } else if (!b && h > mx) {
           mx = h;
           mc = (uint32_t)(q * 8 + e);
         }
       }
     }
+  }
+  if constexpr (ZP) {
+    // the workgroup's range, and the smallest column holding each end
+    const float wl = wave_min(lo), wh = wave_max(hi);
+    const uint32_t wcl = wave_min_u32(lo == wl ? cl : 0xffffffffu);
+    const uint32_t wch = wave_min_u32(hi == wh ? ch : 0xffffffffu);
+    if (lane == 0) {
+      s_lo[wave] = wl;
+      s_hi[wave] = wh;
+      s_cl[wave] = wcl;
+      s_ch[wave] = wch;
+    }
+    __syncthreads();
+    float bl = 0.0f, bh = 0.0f;
+    uint32_t bcl = 0xffffffffu, bch = 0xffffffffu;
+#pragma unroll
+    for (int w = 0; w < BS / 64; ++w) {
+      if (s_lo[w] < bl) {
+        bl = s_lo[w];
+        bcl = s_cl[w];
+      } else if (s_lo[w] == bl && s_cl[w] < bcl) {
+        bcl = s_cl[w];
+      }
+      if (s_hi[w] > bh) {
+        bh = s_hi[w];
+        bch = s_ch[w];
+      } else if (s_hi[w] == bh && s_ch[w] < bch) {
+        bch = s_ch[w];
+      }
+    }
+    const float range = bh - bl;
+    const float inv = range > 0.0f ? 255.0f / range : 0.0f;
+    const int zpv = (int)__builtin_roundf(-bl * inv);
+    int8_t* qr = Xq + (size_t)row * K;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int q = t + j * BS;
+      if (q < nchunks) {
+        int code[8];
+        uint32_t bm8 = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t hb = (uint16_t)(((uint32_t)raw[j][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+          bool b;
+          if constexpr (kKeep) b = (bigm[j] >> e) & 1u;
+          else b = big(hb & 0x7fffu);
+          bm8 |= (uint32_t)b << e;
+          int c = b ? zpv : (int)__builtin_roundf(h2f(hb) * inv) + zpv;
+          c = c < 0 ? 0 : (c > 255 ? 255 : c);
+          code[e] = c - 128;
+        }
+        v2i packed = {(int)pack4_i8(code[0], code[1], code[2], code[3]),
+                      (int)pack4_i8(code[4], code[5], code[6], code[7])};
+        *reinterpret_cast<v2i*>(qr + q * 8) = packed;
+        if (bm8) atomicOr(flags + (q >> 2), bm8 << ((q & 3) * 8));
+      }
+    }
+    if (t == 0) {
+      sx[row] = range / 255.0f;
+      rowval[row] = zpv;   // the zero-point array
+      int32_t* cols = reinterpret_cast<int32_t*>(X_O + (size_t)row * K + K - 4);
+      cols[0] = bl < 0.0f ? (int)bcl : -1;
+      cols[1] = bh > 0.0f ? (int)bch : -1;
+    }
+    return;
   }
   // the workgroup's largest magnitude, and the smallest column that holds it
   uint32_t wm = mx;
@@ -507,7 +604,7 @@ __global__ __launch_bounds__(BS) void rowpass_kernel(const uint16_t* __restrict_
   }
   if (t == 0) {
     sx[row] = scale;
-    argcol[row] = bm > 0 ? (int)bc : -1;
+    rowval[row] = bm > 0 ? (int)bc : -1;
   }
 }
 
@@ -520,11 +617,15 @@ __global__ __launch_bounds__(BS) void rowpass_kernel(const uint16_t* __restrict_
 // passes over the row in 16-byte pieces (its maximum over the regular columns,
 // then the codes), with the rules of rowquant_kernel.  Workgroup 0 writes the
 // ascending index list and the outlier count.
+// ZP: the row's two recorded columns (its range's ends) come from the end of
+// its X_O capacity and its zero point from rowval; outlier columns get the
+// zero point's code; the recompute follows rowquant_kernel's zero-point rules.
 constexpr int kFixThreads = 256, kFixRows = 16;
+template <bool ZP>
 __global__ __launch_bounds__(kFixThreads) void rowfix_kernel(const uint16_t* __restrict__ X, int M,
                                                             int K,
                                                             const uint32_t* __restrict__ flags,
-                                                            const int32_t* __restrict__ argcol,
+                                                            int32_t* __restrict__ rowval,
                                                             int8_t* __restrict__ Xq,
                                                             float* __restrict__ sx,
                                                             int32_t* __restrict__ idx,
@@ -535,13 +636,28 @@ __global__ __launch_bounds__(kFixThreads) void rowfix_kernel(const uint16_t* __r
   __shared__ int s_rank[kMaxFlagWords];
   __shared__ int s_tmp[BS / 64 + 1];
   __shared__ int s_full[kFixRows];
+  __shared__ int s_c0[kFixRows], s_c1[kFixRows], s_zq[kFixRows];
   __shared__ uint32_t s_max[BS / 64];
+  __shared__ float s_lo[ZP ? BS / 64 : 1], s_hi[ZP ? BS / 64 : 1];
   const int t = threadIdx.x;
   const int nw = (K + 31) >> 5;
   const int r0 = blockIdx.x * kFixRows;
   const int nr = min(kFixRows, M - r0);
   for (int w = t; w < nw; w += BS) s_flags[w] = flags[w];
-  const int c = t < nr ? argcol[r0 + t] : -1;
+  // the rows' recorded columns (and zero points) into LDS before the barrier,
+  // so that these loads are complete before any X_O store of the workgroup
+  if (t < nr) {
+    if constexpr (ZP) {
+      const int32_t* cols = reinterpret_cast<const int32_t*>(X_O + (size_t)(r0 + t) * K + K - 4);
+      s_c0[t] = cols[0];
+      s_c1[t] = cols[1];
+      s_zq[t] = rowval[r0 + t] - 128;   // the code of 0
+    } else {
+      s_c0[t] = rowval[r0 + t];
+      s_c1[t] = -1;
+      s_zq[t] = 0;
+    }
+  }
   lds_sync();
   const int per = (nw + BS - 1) / BS;
   const int w0 = t * per, w1 = min(nw, w0 + per);
@@ -553,11 +669,19 @@ __global__ __launch_bounds__(kFixThreads) void rowfix_kernel(const uint16_t* __r
     s_rank[w] = base;
     base += __builtin_popcount(s_flags[w]);
   }
-  if (t < nr) s_full[t] = c >= 0 && ((s_flags[c >> 5] >> (c & 31)) & 1u);
+  if (t < nr) {
+    const int c0 = s_c0[t], c1 = s_c1[t];
+    s_full[t] = (c0 >= 0 && ((s_flags[c0 >> 5] >> (c0 & 31)) & 1u)) ||
+                (c1 >= 0 && ((s_flags[c1 >> 5] >> (c1 & 31)) & 1u));
+  }
   lds_sync();
   // regular recorded column: zero the outlier columns' codes, gather their
   // values; the loads of all the rows go out before any store (rows past M
-  // re-read the last row and store nothing)
+  // re-read the last row and store nothing).  Offsets inside the workgroup's
+  // kFixRows rows fit in 32 bits (16 * K).
+  const uint16_t* xw = X + (size_t)r0 * K;
+  uint16_t* ow = X_O + (size_t)r0 * K;
+  int8_t* qw = Xq + (size_t)r0 * K;
   for (int w = w0; w < w1; ++w) {
     uint32_t f = s_flags[w];
     int r = s_rank[w];
@@ -565,13 +689,12 @@ __global__ __launch_bounds__(kFixThreads) void rowfix_kernel(const uint16_t* __r
       const int j = w * 32 + __builtin_ctz(f);
       uint16_t v[kFixRows];
 #pragma unroll
-      for (int i = 0; i < kFixRows; ++i) v[i] = X[(size_t)(r0 + min(i, nr - 1)) * K + j];
+      for (int i = 0; i < kFixRows; ++i) v[i] = xw[min(i, nr - 1) * K + j];
 #pragma unroll
       for (int i = 0; i < kFixRows; ++i) {
         if (i < nr && !s_full[i]) {
-          const size_t o = (size_t)(r0 + i) * K;
-          X_O[o + r] = v[i];
-          Xq[o + j] = 0;
+          ow[i * K + r] = v[i];
+          qw[i * K + j] = (int8_t)s_zq[i];
         }
       }
       ++r;
@@ -585,23 +708,54 @@ __global__ __launch_bounds__(kFixThreads) void rowfix_kernel(const uint16_t* __r
     const int row = r0 + i;
     const buf_rsrc rx = make_rsrc(X + (size_t)row * K, (uint32_t)K * 2u);
     uint32_t mx = 0;
+    float lo = 0.0f, hi = 0.0f;   // zero-point codes: the range always contains 0
     for (int q = t; q < nchunks; q += BS) {
       const v4i x = buf_load16(rx, (uint32_t)q * 16u);
       const uint32_t ob = (s_flags[q >> 2] >> ((q & 3) * 8)) & 0xffu;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t h = ((uint32_t)x[e >> 1] >> ((e & 1) * 16)) & 0x7fffu;
-        if (!((ob >> e) & 1u)) mx = h > mx ? h : mx;
+        const uint32_t hb = ((uint32_t)x[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        if (!((ob >> e) & 1u)) {
+          if constexpr (ZP) {
+            const float v = h2f((uint16_t)hb);
+            lo = __builtin_fminf(lo, v);
+            hi = __builtin_fmaxf(hi, v);
+          } else {
+            const uint32_t h = hb & 0x7fffu;
+            mx = h > mx ? h : mx;
+          }
+        }
       }
     }
-    mx = wave_max_u32(mx);
-    if ((t & 63) == 0) s_max[t >> 6] = mx;
-    __syncthreads();
-    mx = 0;
+    float scale, inv;
+    int zpv = 0;
+    if constexpr (ZP) {
+      lo = wave_min(lo);
+      hi = wave_max(hi);
+      if ((t & 63) == 0) {
+        s_lo[t >> 6] = lo;
+        s_hi[t >> 6] = hi;
+      }
+      __syncthreads();
 #pragma unroll
-    for (int w = 0; w < BS / 64; ++w) mx = s_max[w] > mx ? s_max[w] : mx;
-    const float scale = h2f((uint16_t)mx);
-    const float inv = quant_scale(scale);
+      for (int w = 0; w < BS / 64; ++w) {
+        lo = __builtin_fminf(lo, s_lo[w]);
+        hi = __builtin_fmaxf(hi, s_hi[w]);
+      }
+      const float range = hi - lo;
+      inv = range > 0.0f ? 255.0f / range : 0.0f;
+      zpv = (int)__builtin_roundf(-lo * inv);
+      scale = range / 255.0f;
+    } else {
+      mx = wave_max_u32(mx);
+      if ((t & 63) == 0) s_max[t >> 6] = mx;
+      __syncthreads();
+      mx = 0;
+#pragma unroll
+      for (int w = 0; w < BS / 64; ++w) mx = s_max[w] > mx ? s_max[w] : mx;
+      scale = h2f((uint16_t)mx);
+      inv = quant_scale(scale);
+    }
     int8_t* qr = Xq + (size_t)row * K;
     uint16_t* orow = X_O + (size_t)row * K;
     for (int q = t; q < nchunks; q += BS) {
@@ -612,7 +766,13 @@ __global__ __launch_bounds__(kFixThreads) void rowfix_kernel(const uint16_t* __r
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint16_t hb = (uint16_t)(((uint32_t)x[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-        code[e] = ((ob >> e) & 1u) ? 0 : quant_code(h2f(hb), inv);
+        if constexpr (ZP) {
+          int cz = ((ob >> e) & 1u) ? zpv : (int)__builtin_roundf(h2f(hb) * inv) + zpv;
+          cz = cz < 0 ? 0 : (cz > 255 ? 255 : cz);
+          code[e] = cz - 128;
+        } else {
+          code[e] = ((ob >> e) & 1u) ? 0 : quant_code(h2f(hb), inv);
+        }
       }
       v2i packed = {(int)pack4_i8(code[0], code[1], code[2], code[3]),
                     (int)pack4_i8(code[4], code[5], code[6], code[7])};
@@ -629,8 +789,11 @@ __global__ __launch_bounds__(kFixThreads) void rowfix_kernel(const uint16_t* __r
         }
       }
     }
-    if (t == 0) sx[row] = scale;
-    __syncthreads();   // s_max is reused by the next recomputed row
+    if (t == 0) {
+      sx[row] = scale;
+      if constexpr (ZP) rowval[row] = zpv;
+    }
+    __syncthreads();   // s_max, s_lo, s_hi are reused by the next recomputed row
   }
   if (blockIdx.x == 0) {
     for (int w = t; w < nw; w += BS) {
@@ -657,13 +820,6 @@ __global__ __launch_bounds__(kFixThreads) void rowfix_kernel(const uint16_t* __r
 // slice; slice 0 writes the row scales, zero points and the outlier count.
 constexpr int kSmallThreads = 256;   // wave w holds rows w, w + 4, w + 8, w + 12
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t o = __shfl_xor(v, off, 64);
-    v = o < v ? o : v;
-  }
-  return v;
-}
 
 // X[r][c .. c+8) of the lane's rows as fp16 (zero past M or K).
 __device__ __forceinline__ void small_load_rows(const uint16_t* X, int M, int K, int c,
@@ -895,13 +1051,20 @@ static void launch_rowquant(const uint16_t* X, int M, int K, bool zp, const Work
 // flags cleared first).  The zero-point array of the workspace, unused by
 // absmax codes, carries each row's recorded column from one to the other.
 template <int BS, int NCH>
-static void launch_rowpass(const uint16_t* X, int M, int K, float threshold, const Workspace& ws,
-                           hipStream_t stream) {
-  hipLaunchKernelGGL((rowpass_kernel<BS, NCH>), dim3(M), dim3(BS), 0, stream, X, M, K, threshold,
-                     ws.flags, ws.Xq, ws.sx, ws.zp);
-  hipLaunchKernelGGL(rowfix_kernel, dim3((M + kFixRows - 1) / kFixRows), dim3(kFixThreads), 0,
-                     stream, X, M, K, (const uint32_t*)ws.flags, (const int32_t*)ws.zp, ws.Xq,
-                     ws.sx, ws.idx, ws.n_out, ws.X_O);
+static void launch_rowpass(const uint16_t* X, int M, int K, float threshold, bool zp,
+                           const Workspace& ws, hipStream_t stream) {
+  const dim3 fgrid((M + kFixRows - 1) / kFixRows), fblock(kFixThreads);
+  if (zp) {
+    hipLaunchKernelGGL((rowpass_kernel<BS, NCH, true>), dim3(M), dim3(BS), 0, stream, X, M, K,
+                       threshold, ws.flags, ws.Xq, ws.sx, ws.zp, ws.X_O);
+    hipLaunchKernelGGL(rowfix_kernel<true>, fgrid, fblock, 0, stream, X, M, K,
+                       (const uint32_t*)ws.flags, ws.zp, ws.Xq, ws.sx, ws.idx, ws.n_out, ws.X_O);
+  } else {
+    hipLaunchKernelGGL((rowpass_kernel<BS, NCH, false>), dim3(M), dim3(BS), 0, stream, X, M, K,
+                       threshold, ws.flags, ws.Xq, ws.sx, ws.zp, ws.X_O);
+    hipLaunchKernelGGL(rowfix_kernel<false>, fgrid, fblock, 0, stream, X, M, K,
+                       (const uint32_t*)ws.flags, ws.zp, ws.Xq, ws.sx, ws.idx, ws.n_out, ws.X_O);
+  }
 }
 
 hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float threshold,
@@ -945,28 +1108,21 @@ hipError_t launch_quantize_activation(const uint16_t* X, int M, int K, float thr
     // one row block: every flag word is stored, so no clear launch
     hipLaunchKernelGGL(colflags_kernel<true>, dim3(bx, 1), dim3(kColThreads), 0, stream, X, M, K,
                        M, threshold, (int)enabled, ws.flags);
-  } else if (!zp) {
-    // absmax codes: one read of X (rowpass_kernel), then the fix-up
-    launch_fill_u32(ws.flags, (K + 31) / 32, 0u, stream);
-    const int nch = K / 8;
-    if (nch <= 256) launch_rowpass<256, 1>(X, M, K, threshold, ws, stream);
-    else if (nch <= 512) launch_rowpass<256, 2>(X, M, K, threshold, ws, stream);
-    else if (nch <= 1024) launch_rowpass<256, 4>(X, M, K, threshold, ws, stream);
-    else if (nch <= 2048) launch_rowpass<512, 4>(X, M, K, threshold, ws, stream);
-    else if (nch <= 4096) launch_rowpass<1024, 4>(X, M, K, threshold, ws, stream);
-    else if (nch <= 7168) launch_rowpass<1024, 7>(X, M, K, threshold, ws, stream);
-    else if (nch <= 8192) launch_rowpass<1024, 8>(X, M, K, threshold, ws, stream);
-    else if (nch <= 16384) launch_rowpass<1024, 16>(X, M, K, threshold, ws, stream);
-    else launch_rowpass<1024, 17>(X, M, K, threshold, ws, stream);
-    return hipGetLastError();
   } else {
-    launch_fill_u32(ws.flags, (K + 31) / 32, 0u, stream);
-    long long want = ((long long)M * bx + 2047) / 2048;
-    int rows = (int)((want + 15) / 16 * 16);
-    if (rows < 16) rows = 16;
-    const int by = (M + rows - 1) / rows;
-    hipLaunchKernelGGL(colflags_kernel<false>, dim3(bx, by), dim3(kColThreads), 0, stream, X, M,
-                       K, rows, threshold, 1, ws.flags);
+    // one read of X (rowpass_kernel), then the fix-up
+    const hipError_t e = launch_fill_u32(ws.flags, (K + 31) / 32, 0u, stream);
+    if (e != hipSuccess) return e;
+    const int nch = K / 8;
+    if (nch <= 256) launch_rowpass<256, 1>(X, M, K, threshold, zp, ws, stream);
+    else if (nch <= 512) launch_rowpass<256, 2>(X, M, K, threshold, zp, ws, stream);
+    else if (nch <= 1024) launch_rowpass<256, 4>(X, M, K, threshold, zp, ws, stream);
+    else if (nch <= 2048) launch_rowpass<512, 4>(X, M, K, threshold, zp, ws, stream);
+    else if (nch <= 4096) launch_rowpass<1024, 4>(X, M, K, threshold, zp, ws, stream);
+    else if (nch <= 7168) launch_rowpass<1024, 7>(X, M, K, threshold, zp, ws, stream);
+    else if (nch <= 8192) launch_rowpass<1024, 8>(X, M, K, threshold, zp, ws, stream);
+    else if (nch <= 16384) launch_rowpass<1024, 16>(X, M, K, threshold, zp, ws, stream);
+    else launch_rowpass<1024, 17>(X, M, K, threshold, zp, ws, stream);
+    return hipGetLastError();
   }
   if (M > 0) {
     // Few 16-byte chunks per thread and wide workgroups: the row's loads are

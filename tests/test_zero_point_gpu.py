@@ -92,6 +92,25 @@ def shaped_x(kind, M, K, n_out, seed):
     return X, cols
 
 
+def _rowpass_zp_x(M, K, seed):
+    """Rows whose largest or smallest entry below the threshold lies in a column
+    that another row makes an outlier (and one tie), on off-centre rows."""
+    X, c = shaped_x("offset", M, K, 3, seed)
+    p, p2, q = 11, 40, 41            # partial outlier columns p, p2; regular column q
+    X[:, [p, p2, q]] = np.clip(X[:, [p, p2, q]], -1, 1)
+    X[0, p] = 7.0                    # p is an outlier column because of row 0 ...
+    X[5, p] = np.float16(5.9)        # ... and holds row 5's largest entry below 6
+    X[1, p2] = -9.0
+    X[6, p2] = np.float16(-5.75)     # row 6's smallest entry, in outlier column p2
+    X[8, p] = np.float16(-5.25)      # a tie for row 8's smallest: outlier p, regular q
+    X[8, q] = np.float16(-5.25)
+    X[7, p] = np.nan                 # a NaN in an outlier column
+    X[9, q] = np.float16(5.99609375)  # largest in a regular column
+    X[M - 1, K - 1] = -6.0           # a last outlier column, set by the last row only
+    X[M - 2, K - 1] = np.float16(-5.8)
+    return X, sorted(set(c) | {p, p2, K - 1})
+
+
 # ---------------------------------------------------------------------------------
 # weight code sums
 # ---------------------------------------------------------------------------------
@@ -128,6 +147,15 @@ def _act_cases():
     yield "small_all_outliers", X, c, 2.0 ** -24
     yield "small_disabled", *shaped_x("offset", 10, 1040, 3, 13), math.inf
     yield "rows64_wide_k", *shaped_x("offset", 64, 24592, 7, 14), 6.0
+    # more than 256 rows: one pass per row with a provisional range (its
+    # smallest and largest entry below the threshold), then the fix-up, which
+    # recomputes a row whose range end sits in an outlier column
+    yield "rowpass_offset", *shaped_x("offset", 300, 1040, 3, 15), 6.0
+    yield "rowpass_fallback", *_rowpass_zp_x(300, 1040, 16), 6.0
+    yield "rowpass_fallback_k_mod64", *_rowpass_zp_x(513, 2064, 17), 6.0
+    X, c = shaped_x("negative", 260, 64, 0, 18)
+    X[:, 7] = 0
+    yield "rowpass_all_outliers", X, c, 2.0 ** -24
     X, c = shaped_x("offset", 33, 256, 0, 9)
     yield "all_outliers", X, c, 2.0 ** -24
     yield "disabled_inf", X, c, math.inf
