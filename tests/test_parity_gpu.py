@@ -180,6 +180,47 @@ def _act_cases():
     yield "boundary", X, c, 6.0
 
 
+def _rowpass_random(n=12, seed=77):
+    """More than 256 rows with partial outlier columns: entries at or above
+    the threshold in some rows only, so that other rows hold entries below it
+    in those columns (zeroed by the fix-up, or, when one is a row's largest,
+    recomputed), plus values exactly at the threshold and NaNs in outlier
+    columns (a row with a NaN in a regular column has no defined scale)."""
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        M = int(rng.integers(257, 700))
+        K = int(16 * rng.integers(2, 400))
+        X, _ = wl.make_x(M, K, float(rng.choice([0.25, 1.0, 2.0])), 0, 8, 20, 100 + i)
+        partial = []
+        for _ in range(int(rng.integers(0, 12))):          # partial outlier columns
+            col = int(rng.integers(0, K))
+            rows = rng.choice(M, size=int(rng.integers(1, 4)), replace=False)
+            X[rows, col] = np.float16(rng.choice([6.0, -6.0, 7.5, -40.0]))
+            near = rng.choice(M, size=int(rng.integers(0, 6)), replace=False)
+            X[near, col] = np.float16(rng.choice([5.99609375, -5.9, 5.5]))
+            partial.append((col, set(rows.tolist())))
+        for col, rows in partial[:int(rng.integers(0, 3))]:   # NaNs in outlier columns
+            r = int(rng.integers(0, M))
+            if r not in rows:
+                X[r, col] = np.nan
+        yield f"rp{i}_{M}x{K}", X
+
+
+@pytest.mark.parametrize("case", list(_rowpass_random()), ids=lambda c: c[0])
+def test_rowpass_random_bitexact(lib, case):
+    name, X = case
+    say(f"quantize_activation (row pass) {name}")
+    r = lib.quantize_activation(dev(X), 6.0)
+    Xq_o, sx_o, idx_o, XO_o = O.quantize_activation(X, 6.0)
+    n = int(host(r["n_out"])[0])
+    assert n == len(idx_o), name
+    np.testing.assert_array_equal(host(r["idx"])[:n], idx_o, err_msg=name)
+    np.testing.assert_array_equal(host(r["sx"]).view(np.uint32), sx_o.view(np.uint32), err_msg=name)
+    np.testing.assert_array_equal(host(r["Xq"]), Xq_o, err_msg=name)
+    np.testing.assert_array_equal(host(r["X_O"])[:, :n].view(np.uint16), XO_o.view(np.uint16),
+                                  err_msg=name)
+
+
 @pytest.mark.parametrize("case", list(_act_cases()), ids=lambda c: c[0])
 def test_quantize_activation_bitexact(lib, case):
     name, X, _, t = case

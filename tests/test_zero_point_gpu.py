@@ -162,6 +162,33 @@ def _act_cases():
     yield "disabled_zero", X, c, 0.0
 
 
+def _rowpass_random(n=8, seed=78):
+    """More than 256 rows, zero-point codes, with partial outlier columns (see
+    the absmax sweep in test_parity_gpu.py) on off-centre rows."""
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        M = int(rng.integers(257, 600))
+        K = int(16 * rng.integers(2, 300))
+        X, _ = shaped_x(str(rng.choice(["offset", "positive", "negative", "normal"])), M, K, 0,
+                        200 + i)
+        for _ in range(int(rng.integers(0, 10))):
+            col = int(rng.integers(0, K))
+            rows = rng.choice(M, size=int(rng.integers(1, 4)), replace=False)
+            X[rows, col] = np.float16(rng.choice([6.0, -6.0, 9.0]))
+            near = rng.choice(M, size=int(rng.integers(0, 6)), replace=False)
+            X[near, col] = np.float16(rng.choice([5.99609375, -5.9, 5.5, -5.75]))
+        yield f"rpzp{i}_{M}x{K}", X
+
+
+@pytest.mark.parametrize("case", list(_rowpass_random()), ids=lambda c: c[0])
+def test_rowpass_random_zp_bitexact(lib, case):
+    name, X = case
+    say(f"quantize_activation_zp (row pass) {name}")
+    r = lib.quantize_activation_zp(dev(X), 6.0)
+    r["sx"] = r["xscale"]
+    check_act(r, O.quantize_activation_zp(X, 6.0), name)
+
+
 @pytest.mark.parametrize("case", list(_act_cases()), ids=lambda c: c[0])
 def test_quantize_activation_zp_bitexact(lib, case):
     name, X, _, t = case
