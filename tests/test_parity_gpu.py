@@ -180,29 +180,42 @@ def _act_cases():
     yield "boundary", X, c, 6.0
 
 
+def _partial_outliers(X, rng, ncols, nan=True):
+    """Entries at or above the threshold in a few rows of `ncols` random
+    columns, entries just below it in a few other rows of the same columns,
+    and (with `nan`) a NaN in some of those columns."""
+    M, K = X.shape
+    partial = []
+    for _ in range(ncols):
+        col = int(rng.integers(0, K))
+        rows = rng.choice(M, size=int(rng.integers(1, 4)), replace=False)
+        X[rows, col] = np.float16(rng.choice([6.0, -6.0, 7.5, -40.0]))
+        near = rng.choice(M, size=int(rng.integers(0, 6)), replace=False)
+        X[near, col] = np.float16(rng.choice([5.99609375, -5.9, 5.5]))
+        partial.append((col, set(rows.tolist())))
+    if nan:
+        for col, rows in partial[:int(rng.integers(0, 3))]:
+            r = int(rng.integers(0, M))
+            if r not in rows:
+                X[r, col] = np.nan
+    return X
+
+
 def _rowpass_random(n=12, seed=77):
     """More than 256 rows with partial outlier columns: entries at or above
     the threshold in some rows only, so that other rows hold entries below it
     in those columns (zeroed by the fix-up, or, when one is a row's largest,
     recomputed), plus values exactly at the threshold and NaNs in outlier
-    columns (a row with a NaN in a regular column has no defined scale)."""
+    columns (a row with a NaN in a regular column has no defined scale).
+    The last cases take the wide launch shapes of the row pass (K up to
+    32768, 65536, 131072 and the largest K, the last two recomputing the
+    per-chunk threshold masks instead of keeping them)."""
     rng = np.random.default_rng(seed)
-    for i in range(n):
-        M = int(rng.integers(257, 700))
-        K = int(16 * rng.integers(2, 400))
+    shapes = [(int(rng.integers(257, 700)), int(16 * rng.integers(2, 400))) for _ in range(n)]
+    shapes += [(257, 24592), (300, 61456), (261, 99984), (258, 133136)]
+    for i, (M, K) in enumerate(shapes):
         X, _ = wl.make_x(M, K, float(rng.choice([0.25, 1.0, 2.0])), 0, 8, 20, 100 + i)
-        partial = []
-        for _ in range(int(rng.integers(0, 12))):          # partial outlier columns
-            col = int(rng.integers(0, K))
-            rows = rng.choice(M, size=int(rng.integers(1, 4)), replace=False)
-            X[rows, col] = np.float16(rng.choice([6.0, -6.0, 7.5, -40.0]))
-            near = rng.choice(M, size=int(rng.integers(0, 6)), replace=False)
-            X[near, col] = np.float16(rng.choice([5.99609375, -5.9, 5.5]))
-            partial.append((col, set(rows.tolist())))
-        for col, rows in partial[:int(rng.integers(0, 3))]:   # NaNs in outlier columns
-            r = int(rng.integers(0, M))
-            if r not in rows:
-                X[r, col] = np.nan
+        _partial_outliers(X, rng, int(rng.integers(0, 12)))
         yield f"rp{i}_{M}x{K}", X
 
 

@@ -14,6 +14,7 @@ import pytest
 
 from mixed_precision_quantized_int8_amd import workloads as wl
 from oracle import int8_oracle as O
+from test_parity_gpu import _partial_outliers
 
 pytestmark = pytest.mark.gpu
 
@@ -164,19 +165,16 @@ def _act_cases():
 
 def _rowpass_random(n=8, seed=78):
     """More than 256 rows, zero-point codes, with partial outlier columns (see
-    the absmax sweep in test_parity_gpu.py) on off-centre rows."""
+    the absmax sweep in test_parity_gpu.py) on off-centre rows; the last cases
+    take the wide launch shapes of the row pass up to the largest K of
+    zero-point codes (where the per-chunk masks are recomputed)."""
     rng = np.random.default_rng(seed)
-    for i in range(n):
-        M = int(rng.integers(257, 600))
-        K = int(16 * rng.integers(2, 300))
+    shapes = [(int(rng.integers(257, 600)), int(16 * rng.integers(2, 300))) for _ in range(n)]
+    shapes += [(259, 24592), (300, 61456), (257, O.ZP_MAX_K)]
+    for i, (M, K) in enumerate(shapes):
         X, _ = shaped_x(str(rng.choice(["offset", "positive", "negative", "normal"])), M, K, 0,
                         200 + i)
-        for _ in range(int(rng.integers(0, 10))):
-            col = int(rng.integers(0, K))
-            rows = rng.choice(M, size=int(rng.integers(1, 4)), replace=False)
-            X[rows, col] = np.float16(rng.choice([6.0, -6.0, 9.0]))
-            near = rng.choice(M, size=int(rng.integers(0, 6)), replace=False)
-            X[near, col] = np.float16(rng.choice([5.99609375, -5.9, 5.5, -5.75]))
+        _partial_outliers(X, rng, int(rng.integers(0, 10)), nan=False)
         yield f"rpzp{i}_{M}x{K}", X
 
 
