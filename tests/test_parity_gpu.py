@@ -130,10 +130,21 @@ def _act_cases():
     yield "one_row", *wl.make_x(1, 16, 1.0, 0, 8, 20, 4), 6.0
     yield "k_mod32_16", *wl.make_x(17, 1040, 1.0, 3, 8, 20, 5), 6.0
     yield "many_outliers", *wl.make_x(40, 512, 1.0, 45, 8, 20, 6), 6.0
-    # one case per row-quantizer launch shape (chunks of 8 columns per thread)
+    # wide rows at M <= 16 (512-column slices)
     yield "k_24576", *wl.make_x(5, 24576, 1.0, 3, 8, 20, 11), 6.0
     yield "k_60000", *wl.make_x(3, 60000, 1.0, 4, 8, 20, 12), 6.0
     yield "k_max", *wl.make_x(2, 133136, 1.0, 5, 8, 20, 13), 6.0
+    # 17-256 rows (strip scan, then one row-quantizer workgroup per row): one
+    # case per wide launch shape of the row quantizer (16-byte chunks per
+    # thread up to 4, 7, 8, 16 and 17), then the same quantizer after the
+    # full-column flag pass (more than 256 rows, decomposition off)
+    for M, K, seed in ((40, 24576, 31), (100, 57344, 32), (65, 61456, 33), (200, 99984, 34),
+                       (33, 133136, 35)):
+        X, c = wl.make_x(M, K, 1.0, 5, 8, 20, seed)
+        X[M - 1, K - 1] = 6.0
+        X[M // 2, K // 2] = np.float16(5.99609375)
+        yield f"rowquant_{M}x{K}", X, sorted(set(c) | {K - 1}), 6.0
+    yield "rowquant_disabled_300x99984", *wl.make_x(300, 99984, 1.0, 3, 8, 20, 36), math.inf
     X, c = wl.make_x(33, 256, 1.0, 0, 8, 20, 7)
     yield "all_outliers", X, c, 2.0 ** -24
     yield "disabled_inf", X, c, math.inf
@@ -151,7 +162,7 @@ def _act_cases():
     X, c = wl.make_x(6, 256, 1.0, 0, 8, 20, 16)
     yield "small_all_outliers", X, c, 2.0 ** -24
     yield "small_disabled", *wl.make_x(10, 1040, 1.0, 3, 8, 20, 17), math.inf
-    yield "rows64_wide_k", *wl.make_x(64, 24592, 1.0, 7, 8, 20, 18), 6.0   # 64-row slices
+    yield "rows64_wide_k", *wl.make_x(64, 24592, 1.0, 7, 8, 20, 18), 6.0   # strip scan, 2 rows/thread
     # 64-column strip scan, one launch shape per rows-per-thread count (up to 32,
     # 64, 128, 256 rows): threshold edges in the last row block, a K that ends
     # inside a strip (K % 64 == 16) and one on a strip edge

@@ -148,6 +148,12 @@ def _act_cases():
     yield "small_all_outliers", X, c, 2.0 ** -24
     yield "small_disabled", *shaped_x("offset", 10, 1040, 3, 13), math.inf
     yield "rows64_wide_k", *shaped_x("offset", 64, 24592, 7, 14), 6.0
+    # 17-256 rows: the wide launch shapes of the row quantizer up to the
+    # largest K of zero-point codes, and the same quantizer after the
+    # full-column flag pass (more than 256 rows, decomposition off)
+    for M, K, seed in ((100, 57344, 31), (65, 61456, 32), (200, O.ZP_MAX_K, 33)):
+        yield f"rowquant_{M}x{K}", *shaped_x("offset", M, K, 5, seed), 6.0
+    yield "rowquant_disabled_300x66304", *shaped_x("offset", 300, O.ZP_MAX_K, 3, 34), math.inf
     # more than 256 rows: one pass per row with a provisional range (its
     # smallest and largest entry below the threshold), then the fix-up, which
     # recomputes a row whose range end sits in an outlier column
