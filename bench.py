@@ -318,8 +318,9 @@ def measure(torch, pkg, workloads, w, args, steps, warmup, with_fp16_context):
                       "activation stage timed alone")
         else:
             launch = ("gemm_i8_kernel whole tiles, split-K tail and fix-up: the call's time "
-                      "less its activation stage (flag clear, rowpass_kernel, rowquant_kernel "
-                      "fix-up; zero-point codes: colflags_kernel, rowquant_kernel) timed alone")
+                      "less its activation stage (flag clear, rowpass_kernel, rowfix_kernel, "
+                      "for both code types; decomposition off: colflags_kernel, "
+                      "rowquant_kernel) timed alone")
     # counter figures were taken on the default layer (fp16 outlier rows, absmax codes)
     tr = None if (args.zero_point or args.rebuilt_rows or args.bias) else TRAFFIC.get((kname, w.name))
     roof["traffic"] = tr["bytes"] if tr and tr["src"] == src_hash else None
